@@ -1,0 +1,223 @@
+"""Reference oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow fp64 CPU implementation of the attention hot path, used by the
+test suite, the smoke check and the benchmark's CPU-baseline leg to check the
+HIP library.  The product path never imports it.  It shares no code with the
+HIP library: the arithmetic lives in ``oracle.c`` (fp64, materialised score and
+probability rows) and the fp8 encoder in ``fp8.py``; this module only slices
+tensors into heads and sequences and calls them.
+
+Sources (pages on IO-aware exact attention):
+  * "Dao and colleagues: IO-aware exact attention with FlashAttention",
+    research record, fields "summary" and "boundary": the method is exact
+    attention computed with tiling and recomputation, without the full
+    attention matrix; the result is the plain definition.
+  * "Flash Attention and Efficient Transformer Mechanisms": exact, "without
+    approximation".
+  * "Dao-AILab" repository overview: the public surface has dense, packed
+    variable-length (varlen) and KV-cache entry points -- the varlen oracle
+    below is the dense oracle run on every packed sequence separately.
+
+Layouts (readings; the pages give none): dense tensors are [B, S, H, d];
+packed varlen tensors are [T, H, d] with cumulative sequence offsets; LSE is
+[B, Hq, Sq] (dense) or [Hq, T] (varlen).  Query head h uses kv head
+h // (Hq // Hkv) (grouped-query attention with contiguous groups).
+
+All array arguments are numpy arrays (any float dtype; converted exactly to
+float64) or torch CPU tensors.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        i64, dbl, ip = ctypes.c_int64, ctypes.c_double, ctypes.c_int
+        pd = ctypes.POINTER(ctypes.c_double)
+        pi64 = ctypes.POINTER(ctypes.c_int64)
+        lib.oracle_head_fwd.argtypes = [i64, i64, i64, pd, pi64, i64, ip, dbl,
+                                        pd, pd, pd, pd, pd]
+        lib.oracle_head_fwd.restype = None
+        lib.oracle_group_bwd.argtypes = [i64, i64, i64, i64, pd, pd, pd, pd,
+                                         ip, dbl, pd, pd, pd, pd, pd]
+        lib.oracle_group_bwd.restype = None
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads():
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _f64(x):
+    if hasattr(x, "detach"):  # torch tensor: bf16/fp16/fp8 -> fp32 is exact
+        import torch
+        x = x.detach().cpu()
+        if x.dtype != torch.float64:
+            x = x.to(torch.float32)
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _default_scale(d, scale):
+    return 1.0 / np.sqrt(d) if scale is None else float(scale)
+
+
+def head_fwd(q_rows, pos, k, v, diag, causal, scale, want_probs=False):
+    """Exact attention for some query rows of one head.
+
+    q_rows [n, d]; pos [n] integer position of each row in its sequence;
+    k, v [sk, d]; diag = Sk - Sq of the sequence (bottom-right causal mask).
+    Returns (o [n, d], lse [n]) and, if want_probs, P [n, sk].
+    """
+    lib = _load()
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    n, d = q_rows.shape
+    sk = k.shape[0]
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    assert pos.shape == (n,) and k.shape == (sk, d) and v.shape == (sk, d)
+    o = np.zeros((n, d))
+    lse = np.zeros(n)
+    p = np.zeros((n, sk)) if want_probs else None
+    lib.oracle_head_fwd(n, sk, d, _ptr(q_rows),
+                        pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                        int(diag), int(bool(causal)), float(scale), _ptr(k),
+                        _ptr(v), _ptr(o), _ptr(lse),
+                        _ptr(p) if want_probs else None)
+    return (o, lse, p) if want_probs else (o, lse)
+
+
+def attention_fwd(q, k, v, causal=False, scale=None, want_probs=False):
+    """Dense forward.  q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] -> o [B,Sq,Hq,d],
+    lse [B,Hq,Sq] (and P [B,Hq,Sq,Sk] if want_probs)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    assert Hq % Hkv == 0
+    scale = _default_scale(d, scale)
+    grp = Hq // Hkv
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    probs = np.zeros((B, Hq, Sq, Sk)) if want_probs else None
+    pos = np.arange(Sq)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            res = head_fwd(q[b, :, h, :], pos, k[b, :, g, :], v[b, :, g, :],
+                           Sk - Sq, causal, scale, want_probs)
+            o[b, :, h, :], lse[b, h, :] = res[0], res[1]
+            if want_probs:
+                probs[b, h] = res[2]
+    return (o, lse, probs) if want_probs else (o, lse)
+
+
+def attention_fwd_rows(q, k, v, b_idx, h_idx, i_idx, causal=False, scale=None):
+    """Dense forward evaluated only at the query rows (b_idx[n], h_idx[n],
+    i_idx[n]).  Returns o [n, d], lse [n].  q/k/v may be torch tensors on any
+    device; only the needed heads are copied to the host."""
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    scale = _default_scale(d, scale)
+    grp = Hq // Hkv
+    b_idx, h_idx, i_idx = (np.asarray(x, dtype=np.int64) for x in (b_idx, h_idx, i_idx))
+    n = len(b_idx)
+    o = np.zeros((n, d))
+    lse = np.zeros(n)
+    keys = {}
+    for r in range(n):
+        keys.setdefault((int(b_idx[r]), int(h_idx[r])), []).append(r)
+    for (b, h), rows in keys.items():
+        g = h // grp
+        rows = np.asarray(rows)
+        qr = _f64(q[b, :, h, :][i_idx[rows]] if not hasattr(q, "detach")
+                  else q[b, i_idx[rows], h, :])
+        o[rows], lse[rows] = head_fwd(qr, i_idx[rows], k[b, :, g, :],
+                                      v[b, :, g, :], Sk - Sq, causal, scale)
+    return o, lse
+
+
+def attention_bwd(q, k, v, dout, causal=False, scale=None, bh=None):
+    """Dense forward + backward.  Returns (o, lse, dq, dk, dv) in the dense
+    layouts; dk/dv [B,Sk,Hkv,d] are summed over each kv head's query heads.
+    With bh = [(b, g), ...] only those (batch, kv-head) slices are computed
+    and the other entries are left at zero."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    assert Hq % Hkv == 0
+    scale = _default_scale(d, scale)
+    grp = Hq // Hkv
+    lib = _load()
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    dq = np.zeros((B, Sq, Hq, d))
+    dk = np.zeros((B, Sk, Hkv, d))
+    dv = np.zeros((B, Sk, Hkv, d))
+    if bh is None:
+        bh = [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in bh:
+        hs = slice(g * grp, (g + 1) * grp)
+        qg = np.ascontiguousarray(q[b, :, hs, :].transpose(1, 0, 2))
+        dog = np.ascontiguousarray(dout[b, :, hs, :].transpose(1, 0, 2))
+        kg = np.ascontiguousarray(k[b, :, g, :])
+        vg = np.ascontiguousarray(v[b, :, g, :])
+        og = np.zeros((grp, Sq, d))
+        lg = np.zeros((grp, Sq))
+        dqg = np.zeros((grp, Sq, d))
+        dkg = np.zeros((Sk, d))
+        dvg = np.zeros((Sk, d))
+        lib.oracle_group_bwd(grp, Sq, Sk, d, _ptr(qg), _ptr(kg), _ptr(vg),
+                             _ptr(dog), int(bool(causal)), scale, _ptr(og),
+                             _ptr(lg), _ptr(dqg), _ptr(dkg), _ptr(dvg))
+        o[b, :, hs, :] = og.transpose(1, 0, 2)
+        lse[b, hs, :] = lg
+        dq[b, :, hs, :] = dqg.transpose(1, 0, 2)
+        dk[b, :, g, :] = dkg
+        dv[b, :, g, :] = dvg
+    return o, lse, dq, dk, dv
+
+
+def attention_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal=False,
+                         scale=None, seqs=None, rows_per_seq=None):
+    """Packed variable-length forward: each sequence z attends only to its own
+    keys.  q [Tq,Hq,d], k/v [Tk,Hkv,d], cu_seqlens_* [nseq+1] -> o [Tq,Hq,d],
+    lse [Hq,Tq].  `seqs` restricts the work to some sequences and
+    `rows_per_seq` (dict z -> positions) to some rows; rows not computed are
+    left at zero (o) and nan (lse)."""
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = _default_scale(d, scale)
+    grp = Hq // Hkv
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    o = np.zeros((Tq, Hq, d))
+    lse = np.full((Hq, Tq), np.nan)
+    nseq = len(cq) - 1
+    for z in (range(nseq) if seqs is None else seqs):
+        q0, q1, k0, k1 = cq[z], cq[z + 1], ck[z], ck[z + 1]
+        lq, lk = q1 - q0, k1 - k0
+        pos = np.arange(lq) if rows_per_seq is None else np.asarray(rows_per_seq[z], dtype=np.int64)
+        for h in range(Hq):
+            g = h // grp
+            qr = q[q0 + pos, h, :] if len(pos) else q[q0:q0, h, :]
+            res = head_fwd(qr, pos, k[k0:k1, g, :], v[k0:k1, g, :], lk - lq,
+                           causal, scale)
+            o[q0 + pos, h, :] = res[0]
+            lse[h, q0 + pos] = res[1]
+    return o, lse

@@ -1,0 +1,103 @@
+"""FP8 (OCP E4M3) encoder for the oracle -- TEST INFRASTRUCTURE ONLY.
+
+Source: "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+Low-precision" (summary, third contribution and the error comparison): the
+forward runs its GEMMs in FP8, and block-wise scaling is compared with
+per-tensor quantisation.  The pages fix neither the FP8 format nor the block
+size; readings used here:
+  * format OCP E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); codes 0x7F and
+    0xFF are NaN; no infinities; largest finite value 1.75 * 2^8 = 448;
+  * encoding rounds to the nearest representable value, ties to the even
+    code, and saturates to +-448;
+  * one scale per (batch, head, 128-token block): scale = amax / 448 computed
+    in fp32, a block of zeros gets scale 1; the encoder's input is the fp32
+    quotient x / scale (the decision is taken in fp32, the precision of the
+    GPU quantiser);
+  * per-tensor quantisation is the same with one block covering the tensor.
+The value table is built from the format definition, not from any library.
+"""
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Real value of an 8-bit E4M3 code (NaN for 0x7F / 0xFF)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# non-negative finite codes 0..126 in increasing value order
+_POS_VALUES = np.array([e4m3_value(c) for c in range(127)], dtype=np.float64)
+
+
+def encode_e4m3(y):
+    """Round fp32 values y to E4M3 codes (uint8): nearest, ties to even code,
+    saturating at +-448.  NaN inputs map to 0x7F."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y).astype(np.float64), E4M3_MAX)
+    hi = np.searchsorted(_POS_VALUES, a, side="left")  # first value >= a
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dhi = _POS_VALUES[hi] - a
+    dlo = a - _POS_VALUES[lo]
+    pick_lo = (dlo < dhi) | ((dlo == dhi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    code = np.where(np.signbit(y), code | 0x80, code).astype(np.uint8)
+    code = np.where(np.isnan(y), np.uint8(0x7F), code)
+    return code
+
+
+def decode_e4m3(code):
+    """E4M3 codes -> float64 values."""
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(code, dtype=np.uint8)]
+
+
+def block_scales(x, block=128):
+    """x [B,S,H,d] fp32 -> fp32 scales [B,H,ceil(S/block)], amax/448 per
+    (batch, head, block of `block` tokens); zero blocks get 1."""
+    x = np.asarray(x, dtype=np.float32)
+    B, S, H, d = x.shape
+    nb = (S + block - 1) // block
+    sc = np.ones((B, H, nb), dtype=np.float32)
+    for t in range(nb):
+        blk = np.abs(x[:, t * block:(t + 1) * block, :, :])
+        amax = blk.max(axis=(1, 3)).astype(np.float32)  # [B,H]
+        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        sc[:, :, t] = np.where(amax > 0, s, np.float32(1.0))
+    return sc
+
+
+def quantize_blocks(x, block=128):
+    """Per-block quantisation of x [B,S,H,d]: returns (codes uint8 [B,S,H,d],
+    scales fp32 [B,H,nb])."""
+    x = np.asarray(x, dtype=np.float32)
+    sc = block_scales(x, block)
+    B, S, H, d = x.shape
+    tok_scale = np.repeat(sc, block, axis=2)[:, :, :S]          # [B,H,S]
+    y = x / tok_scale.transpose(0, 2, 1)[..., None].astype(np.float32)
+    return encode_e4m3(y.astype(np.float32)), sc
+
+
+def quantize_tensor(x):
+    """Per-tensor quantisation: one scale amax/448 for the whole tensor."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.abs(x).max())
+    s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    return encode_e4m3((x / s).astype(np.float32)), s
+
+
+def dequantize_blocks(codes, scales, block=128):
+    """codes [B,S,H,d] + scales [B,H,nb] -> float64 values."""
+    B, S, H, d = codes.shape
+    tok_scale = np.repeat(np.asarray(scales, np.float64), block, axis=2)[:, :, :S]
+    return decode_e4m3(codes) * tok_scale.transpose(0, 2, 1)[..., None]

@@ -1,0 +1,184 @@
+/*
+ * fa.h -- C ABI of libfa.so: IO-aware exact attention on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the calls compute.  Exact softmax attention, O = softmax(scale * Q K^T
+ * [+ causal mask]) V, evaluated tile by tile with a running row maximum and
+ * row sum so that the Sq x Sk score matrix never reaches device memory, and
+ * its backward, which rebuilds the probabilities from the saved row
+ * log-sum-exp instead of storing them.  Sources (pages on IO-aware exact
+ * attention):
+ *   - "Dao and colleagues: IO-aware exact attention with FlashAttention",
+ *     research record, fields "summary" and "boundary": exact attention by
+ *     tiling plus recomputation, the full attention matrix is never
+ *     materialised, arithmetic stays quadratic;
+ *   - "Flash Attention and Efficient Transformer Mechanisms": blocks of Q, K
+ *     and V are read from high-bandwidth memory into on-chip memory and
+ *     partial outputs are computed there, "without approximation";
+ *   - Dao-AILab repository overview: online softmax with rescaling, tiled
+ *     attention staged through on-chip memory, a dense entry point, a packed
+ *     variable-length entry point and a KV-cache (decode) entry point,
+ *     deterministic backward passes;
+ *   - "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+ *     Low-precision" (summary, third contribution): an FP8 forward with
+ *     block-wise scaling.
+ *
+ * Conventions (readings; the pages fix none of them):
+ *   - dense tensors are [B, S, H, d] with element strides for B, S and H and
+ *     a contiguous last dimension; packed (varlen) tensors are [T, H, d];
+ *   - query head h uses kv head h / (Hq / Hkv) (grouped-query attention);
+ *   - causal masking is bottom-right aligned: query row i sees key j iff
+ *     j <= i + (Sk - Sq); a row that sees no key gets O = 0, LSE = -inf;
+ *   - LSE is the natural-log log-sum-exp of the scaled, masked scores, fp32,
+ *     laid out [B, Hq, Sq] (dense) or [Hq, T_q] (varlen), contiguous;
+ *   - inputs are bf16 (or OCP e4m3 for the FP8 forward); accumulation is fp32;
+ *     outputs O, dQ, dK, dV are bf16, rounded to nearest even.
+ *
+ * Ownership.  Every pointer is a DEVICE pointer owned by the caller.  The
+ * library never allocates, frees or keeps a pointer past the enqueued work,
+ * and never synchronises the stream: all work is enqueued on `stream`.
+ * Outputs are fully overwritten.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued; a
+ * failed check returns a nonzero fa_status and has no side effect.  A failed
+ * kernel launch returns FA_ERR_HIP.  Faults inside kernels are asynchronous
+ * and surface at the caller's next synchronisation.  The contents of
+ * cu_seqlens arrays live on the device and are trusted (they must be
+ * non-decreasing, start at 0 and stay within the packed tensors).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* a size is <= 0 or out of the supported range */
+  FA_ERR_HEADDIM = 3,     /* d is not 64 or 128 */
+  FA_ERR_DTYPE = 4,       /* unsupported dtype for this call */
+  FA_ERR_GQA = 5,         /* Hq is not a multiple of Hkv */
+  FA_ERR_ALIGN = 6,       /* a pointer or stride is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
+  FA_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
+  FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
+  FA_ERR_SCALE = 10       /* softmax scale is not a finite positive number */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_FP8_E4M3 = 2 } fa_dtype;
+
+/* A dense [B, S, H, d] tensor: base pointer and element strides of the B, S
+ * and H dimensions (the d dimension has stride 1).  Strides must be
+ * multiples of 8 elements for bf16 and of 16 for fp8 (16-byte rows). */
+typedef struct {
+  void* ptr;
+  int64_t stride_b, stride_s, stride_h;
+} fa_tensor;
+
+/* Dense forward.  q [B,Sq,Hq,d], k and v [B,Sk,Hkv,d] in `dtype`; o
+ * [B,Sq,Hq,d] bf16; lse [B,Hq,Sq] fp32 contiguous (required).
+ * FP8 only: q_descale [B,Hq,ceil(Sq/128)], k_descale and v_descale
+ * [B,Hkv,ceil(Sk/128)], fp32 contiguous: the real value of an element is its
+ * e4m3 value times the scale of its (batch, head, 128-token block).
+ * workspace: used only by the split-KV decode path (see fa_fwd_workspace_size);
+ * pass NULL / 0 when the size query returns 0. */
+typedef struct {
+  fa_dtype dtype;
+  int32_t B, Sq, Sk, Hq, Hkv, d;
+  int32_t causal;
+  float softmax_scale;
+  fa_tensor q, k, v, o;
+  float* lse;
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  void* workspace;
+  size_t workspace_bytes;
+} fa_fwd_args;
+
+/* Packed variable-length forward (bf16).  Sequence z owns query rows
+ * cu_seqlens_q[z] .. cu_seqlens_q[z+1]-1 of q [Tq,Hq,d] and key rows
+ * cu_seqlens_k[z] .. cu_seqlens_k[z+1]-1 of k, v [Tk,Hkv,d]; it attends only
+ * to its own keys (causal alignment per sequence).  cu_seqlens_* are int32
+ * device arrays of nseq+1 entries; max_seqlen_q bounds every query length.
+ * o [Tq,Hq,d] bf16; lse [Hq,Tq] fp32 contiguous; total_q = Tq. */
+typedef struct {
+  fa_dtype dtype;
+  int32_t nseq, Hq, Hkv, d, max_seqlen_q, max_seqlen_k, total_q, total_k;
+  int32_t causal;
+  float softmax_scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_stride_t, q_stride_h, k_stride_t, k_stride_h;
+  int64_t v_stride_t, v_stride_h, o_stride_t, o_stride_h;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  float* lse;
+} fa_fwd_varlen_args;
+
+/* Dense backward (bf16).  Inputs: q, k, v, the forward output o, its
+ * gradient dout [B,Sq,Hq,d], and the forward's lse [B,Hq,Sq].  Outputs dq
+ * [B,Sq,Hq,d], dk and dv [B,Sk,Hkv,d] (bf16; for GQA, dk/dv sum over the query
+ * heads of each kv head).  workspace: at least fa_bwd_workspace_size bytes,
+ * 256-byte aligned.  The result is bitwise reproducible run to run. */
+typedef struct {
+  fa_dtype dtype;
+  int32_t B, Sq, Sk, Hq, Hkv, d;
+  int32_t causal;
+  float softmax_scale;
+  fa_tensor q, k, v, o, dout, dq, dk, dv;
+  const float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} fa_bwd_args;
+
+/* Returns FA_ABI_VERSION. */
+int32_t fa_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* fa_status_string(fa_status status);
+
+/* Workspace bytes fa_fwd needs for these arguments (0 when none). */
+size_t fa_fwd_workspace_size(const fa_fwd_args* args);
+
+/* Workspace bytes fa_bwd needs for these arguments. */
+size_t fa_bwd_workspace_size(const fa_bwd_args* args);
+
+/* Dense forward; see fa_fwd_args. */
+fa_status fa_fwd(const fa_fwd_args* args, hipStream_t stream);
+
+/* Packed variable-length forward; see fa_fwd_varlen_args. */
+fa_status fa_fwd_varlen(const fa_fwd_varlen_args* args, hipStream_t stream);
+
+/* Dense backward; see fa_bwd_args. */
+fa_status fa_bwd(const fa_bwd_args* args, hipStream_t stream);
+
+/* FP8 quantiser (input preparation for the FP8 forward).
+ * x [B,S,H,d] fp32 with element strides (d contiguous) -> codes [B,S,H,d]
+ * e4m3 contiguous and scales [B,H,ceil(S/128)] fp32 contiguous.
+ * per_tensor = 0: one scale per (batch, head, 128-token block),
+ *   scale = amax/448 over the block (1 for an all-zero block);
+ * per_tensor = 1: one scale amax/448 over the whole tensor, written to every
+ *   entry of `scales` so the FP8 forward reads the same layout.
+ * code = nearest e4m3 value of the fp32 quotient x/scale, ties to the even
+ * code, saturating to +-448.  Deterministic. */
+fa_status fa_quantize_fp8(const float* x, int64_t stride_b, int64_t stride_s,
+                          int64_t stride_h, int32_t B, int32_t S, int32_t H,
+                          int32_t d, int32_t per_tensor, void* codes,
+                          float* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

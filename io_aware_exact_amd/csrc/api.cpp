@@ -1,0 +1,206 @@
+// Host entry points of libfa.so: argument checks, then kernel launches on the
+// caller's stream.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kBM = 128;   // query rows per forward workgroup
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte span of a [B,S,H,d] tensor with non-negative element strides.
+Span span4(const void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb, int64_t ss,
+           int64_t sh, int64_t esize) {
+  if (B <= 0 || S <= 0 || H <= 0 || d <= 0) return {(uintptr_t)ptr, (uintptr_t)ptr};
+  const int64_t last = (B - 1) * sb + (S - 1) * ss + (H - 1) * sh + (d - 1);
+  return {(uintptr_t)ptr, (uintptr_t)ptr + (uintptr_t)((last + 1) * esize)};
+}
+
+bool overlap(Span a, Span b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Kernels address one (batch, head) slice with 32-bit byte offsets, padded
+// by one tile of rows.
+bool fits32(int64_t rows, int64_t row_stride_elems, int64_t esize) {
+  return (rows + 128) * row_stride_elems * esize < (int64_t)0xffffffffLL;
+}
+
+bool strides_ok(const fa_tensor& t, int64_t mult) {
+  return t.stride_b >= 0 && t.stride_s >= 0 && t.stride_h >= 0 && t.stride_b % mult == 0 &&
+         t.stride_s % mult == 0 && t.stride_h % mult == 0;
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+fa_status check_fwd(const fa_fwd_args* a) {
+  if (!a) return FA_ERR_NULL;
+  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
+  if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
+  if (!isfinite(a->softmax_scale)) return FA_ERR_SCALE;
+  if (!a->q.ptr || !a->k.ptr || !a->v.ptr || !a->o.ptr || !a->lse) return FA_ERR_NULL;
+  if (!aligned16(a->q.ptr) || !aligned16(a->k.ptr) || !aligned16(a->v.ptr) || !aligned16(a->o.ptr) ||
+      ((uintptr_t)a->lse & 3u))
+    return FA_ERR_ALIGN;
+  if (!strides_ok(a->q, 8) || !strides_ok(a->k, 8) || !strides_ok(a->v, 8) || !strides_ok(a->o, 8))
+    return FA_ERR_ALIGN;
+  const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
+  if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!fits32(a->Sq, a->q.stride_s, 2) || !fits32(a->Sq, a->o.stride_s, 2) ||
+      !fits32(a->Sk, a->k.stride_s, 2) || !fits32(a->Sk, a->v.stride_s, 2))
+    return FA_ERR_SHAPE;
+  const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
+  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
+  const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2);
+  const Span sk = span4(a->k.ptr, a->B, a->Sk, a->Hkv, a->d, a->k.stride_b, a->k.stride_s, a->k.stride_h, 2);
+  const Span sv = span4(a->v.ptr, a->B, a->Sk, a->Hkv, a->d, a->v.stride_b, a->v.stride_s, a->v.stride_h, 2);
+  if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sl) || overlap(sl, sq) ||
+      overlap(sl, sk) || overlap(sl, sv))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+fa_status check_varlen(const fa_fwd_varlen_args* a) {
+  if (!a) return FA_ERR_NULL;
+  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->nseq < 0 || a->Hq < 1 || a->Hkv < 1 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0 ||
+      a->total_q < 0 || a->total_k < 0)
+    return FA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
+  if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
+  if (!isfinite(a->softmax_scale)) return FA_ERR_SCALE;
+  if (!a->q || !a->k || !a->v || !a->o || !a->lse || !a->cu_seqlens_q || !a->cu_seqlens_k)
+    return FA_ERR_NULL;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
+      ((uintptr_t)a->lse & 3u) || ((uintptr_t)a->cu_seqlens_q & 3u) || ((uintptr_t)a->cu_seqlens_k & 3u))
+    return FA_ERR_ALIGN;
+  const int64_t st[8] = {a->q_stride_t, a->q_stride_h, a->k_stride_t, a->k_stride_h,
+                         a->v_stride_t, a->v_stride_h, a->o_stride_t, a->o_stride_h};
+  for (int i = 0; i < 8; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_ALIGN;
+  const int64_t tiles = ((int64_t)a->max_seqlen_q + kBM - 1) / kBM;
+  if (tiles * a->Hq * (int64_t)a->nseq > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!fits32(a->max_seqlen_q, a->q_stride_t, 2) || !fits32(a->max_seqlen_q, a->o_stride_t, 2) ||
+      !fits32(a->max_seqlen_k, a->k_stride_t, 2) || !fits32(a->max_seqlen_k, a->v_stride_t, 2))
+    return FA_ERR_SHAPE;
+  const Span so = span4(a->o, 1, a->total_q, a->Hq, a->d, 0, a->o_stride_t, a->o_stride_h, 2);
+  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->Hq * a->total_q * 4};
+  const Span sq = span4(a->q, 1, a->total_q, a->Hq, a->d, 0, a->q_stride_t, a->q_stride_h, 2);
+  const Span sk = span4(a->k, 1, a->total_k, a->Hkv, a->d, 0, a->k_stride_t, a->k_stride_h, 2);
+  const Span sv = span4(a->v, 1, a->total_k, a->Hkv, a->d, 0, a->v_stride_t, a->v_stride_h, 2);
+  if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sl) || overlap(sl, sq) ||
+      overlap(sl, sk) || overlap(sl, sv))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid or unsupported size";
+    case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "unsupported dtype for this call";
+    case FA_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case FA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_ALIAS: return "an output overlaps another tensor";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_SCALE: return "softmax scale must be finite";
+  }
+  return "unknown status";
+}
+
+size_t fa_fwd_workspace_size(const fa_fwd_args* a) {
+  (void)a;
+  return 0;
+}
+
+fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
+  const fa_status s = check_fwd(a);
+  if (s != FA_OK) return s;
+  if (a->B == 0 || a->Sq == 0) return FA_OK;
+  FwdParams p = {};
+  p.q = a->q.ptr;
+  p.k = a->k.ptr;
+  p.v = a->v.ptr;
+  p.o = a->o.ptr;
+  p.lse = a->lse;
+  p.q_sb = a->q.stride_b; p.q_ss = a->q.stride_s; p.q_sh = a->q.stride_h;
+  p.k_sb = a->k.stride_b; p.k_ss = a->k.stride_s; p.k_sh = a->k.stride_h;
+  p.v_sb = a->v.stride_b; p.v_ss = a->v.stride_s; p.v_sh = a->v.stride_h;
+  p.o_sb = a->o.stride_b; p.o_ss = a->o.stride_s; p.o_sh = a->o.stride_h;
+  p.lse_sb = (int64_t)a->Hq * a->Sq;
+  p.lse_sh = a->Sq;
+  p.B = a->B; p.Sq = a->Sq; p.Sk = a->Sk; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.num_m_tiles = (a->Sq + kBM - 1) / kBM;
+  p.scale = a->softmax_scale;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  return hip_status(launch_fwd_bf16(p, a->d, a->causal != 0, false, stream));
+}
+
+fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, hipStream_t stream) {
+  const fa_status s = check_varlen(a);
+  if (s != FA_OK) return s;
+  if (a->nseq == 0 || a->max_seqlen_q == 0 || a->total_q == 0) return FA_OK;
+  FwdParams p = {};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.q_ss = a->q_stride_t; p.q_sh = a->q_stride_h;
+  p.k_ss = a->k_stride_t; p.k_sh = a->k_stride_h;
+  p.v_ss = a->v_stride_t; p.v_sh = a->v_stride_h;
+  p.o_ss = a->o_stride_t; p.o_sh = a->o_stride_h;
+  p.lse_sb = 0;
+  p.lse_sh = a->total_q;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.B = a->nseq; p.Sq = a->max_seqlen_q; p.Sk = a->max_seqlen_k; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.num_m_tiles = (a->max_seqlen_q + kBM - 1) / kBM;
+  p.scale = a->softmax_scale;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  return hip_status(launch_fwd_bf16(p, a->d, a->causal != 0, true, stream));
+}
+
+size_t fa_bwd_workspace_size(const fa_bwd_args* a) {
+  (void)a;
+  return 0;
+}
+
+fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
+  (void)stream;
+  if (!a) return FA_ERR_NULL;
+  return FA_ERR_DTYPE;
+}
+
+fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int32_t B, int32_t S,
+                          int32_t H, int32_t d, int32_t per_tensor, void* codes, float* scales,
+                          hipStream_t stream) {
+  (void)x; (void)sb; (void)ss; (void)sh; (void)B; (void)S; (void)H; (void)d; (void)per_tensor;
+  (void)codes; (void)scales; (void)stream;
+  return FA_ERR_DTYPE;
+}
+
+}  // extern "C"

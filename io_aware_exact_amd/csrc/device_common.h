@@ -1,0 +1,62 @@
+// Device-side vector types and small helpers shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand layout (lane l, element e):
+//   A[m][k]: m = l % 32, k = 8 * (l / 32) + e
+//   B[k][n]: n = l % 32, k = 8 * (l / 32) + e
+//   C[m][n]: n = l % 32, m = 8 * (i / 4) + 4 * (l / 32) + (i % 4) for reg i
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transposing read of 4 x 16-bit values.  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte rows addressed by lanes
+// 16 * (l / 16) + i / 4 + 4 * e, for e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat_bf16(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Raw buffer resource over [base, base + bytes).  Loads past the end return
+// zero and stores past the end are dropped (the bounds check covers the
+// per-lane offset), which is how tile tails are handled without clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): all outstanding vector-memory loads have returned.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -1,0 +1,55 @@
+// Internal launch descriptors shared by the host entry points and kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;   // element strides; for varlen q_sb is unused
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh;     // dense: [B,Hq,Sq]; varlen: lse_sh = total_q
+  const int32_t* cu_q;        // varlen only
+  const int32_t* cu_k;
+  const float* q_descale;     // fp8 only
+  const float* k_descale;
+  const float* v_descale;
+  int B, Sq, Sk, Hq, Hkv, group;   // varlen: B = nseq, Sq/Sk = max lengths
+  int num_m_tiles;
+  float scale;                // softmax scale
+  float scale_log2;           // scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* lse;
+  float* delta;               // workspace [B,Hq,Sq]: rowsum(dO * O)
+  float* dq_acc;              // workspace [B,Hq,Sq,d] fp32
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  int B, Sq, Sk, Hq, Hkv, group;
+  int causal;
+  float scale;
+  float scale_log2;
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen,
+                           hipStream_t stream);

@@ -1,0 +1,286 @@
+// Forward kernel of IO-aware exact attention for gfx950 (bf16 in, fp32
+// accumulate, bf16 out, fp32 LSE).
+//
+// Method (pages on IO-aware exact attention): blocks of Q, K and V are moved
+// from HBM into on-chip memory and partial outputs are computed there
+// ("Flash Attention and Efficient Transformer Mechanisms", block
+// computation); the softmax is evaluated online with a running row maximum
+// and rescaling of earlier partial results (Dao-AILab repository overview,
+// core contributions), so the Sq x Sk score matrix is never written out
+// ("Dao and colleagues: IO-aware exact attention with FlashAttention",
+// summary).  The result is exact attention up to floating-point rounding.
+//
+// gfx950 mapping.
+//   * A workgroup of 4 waves owns BM = 128 query rows of one (batch, head);
+//     each wave owns 32 rows for the whole KV sweep, so the forward needs no
+//     cross-wave reduction.
+//   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
+//     MFMA: K rows are the A operand (read from LDS), Q^T is the B operand
+//     held in VGPRs for the whole sweep.  In the accumulator layout every lane
+//     then owns ONE query row (column n = lane % 32) and 16 of the 32 keys of a
+//     block, so row max and row sum are in-lane, plus one exchange with lane
+//     l ^ 32 for the max.
+//   * K rows are loaded into the A operand in a permuted order chosen so that
+//     accumulator registers 0..7 / 8..15 of a lane hold 8 consecutive keys:
+//     after the exponentials they are directly the B operand (P^T) of
+//     O^T += V^T P^T, with no register shuffle and no LDS round trip.
+//   * V^T, the A operand of that product, is read from the row-major V tile
+//     with the LDS transposing load (ds_read_b64_tr_b16).
+//   * K/V tiles of BN = 64 keys are double-buffered in LDS; the next tile's
+//     global loads (16 bytes per lane, whole 256-byte rows per 16 lanes) are
+//     issued before the current tile's MFMAs and written to the other buffer
+//     after them.  One barrier per tile.
+//   * exp2 with the softmax scale and log2(e) folded into one FMA.
+//   * Causal: tiles entirely above the diagonal are skipped (the loop stops at
+//     the last visible key), waves skip tiles none of their rows can see, and
+//     element masks are applied only on tiles that cross the diagonal or the
+//     sequence end.  Heavy (late) query tiles are dispatched first.
+//   * Workgroup ids are remapped so that consecutive tiles of one kv head land
+//     on the same XCD (dispatch is round-robin over the 8 XCDs, each with its
+//     own L2), letting the head's K/V tiles be served from that L2.
+#include "device_common.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int BM = 128;
+constexpr int BN = 64;
+constexpr int NTHREADS = 256;
+
+template <int D>
+struct FwdTile {
+  static constexpr int KSTR = D + 8;    // K row stride in LDS (elements)
+  static constexpr int VSTR = D + 16;   // V row stride in LDS (elements)
+  static constexpr int NC = D / 16;     // 16-wide chunks of d (QK^T)
+  static constexpr int ND = D / 32;     // 32-row blocks of d (O^T)
+  static constexpr int CH = D / 8;      // 16-byte chunks per row
+  static constexpr int RPP = NTHREADS / CH;  // rows per load pass
+  static constexpr int NP = BN / RPP;        // load passes per tile
+  static constexpr int STAGE = BN * (KSTR + VSTR);
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+};
+
+// Map a dispatch index to a logical tile index so that logical neighbours
+// share an XCD: dispatch index w runs on XCD w % 8.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = w & 7, s = w >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
+  using T = FwdTile<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
+
+  // ---- which (batch, head, query tile)
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int mt = L % p.num_m_tiles;
+  const int rest = L / p.num_m_tiles;
+  const int h = rest % p.Hq;
+  const int b = rest / p.Hq;
+  if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  const int g = h / p.group;
+
+  int Lq = p.Sq, Lk = p.Sk;
+  int64_t qtok = 0, ktok = 0;
+  if (VARLEN) {
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    Lq = p.cu_q[b + 1] - qs;
+    Lk = p.cu_k[b + 1] - ks;
+    qtok = qs;
+    ktok = ks;
+  }
+  const int q0 = mt * BM;
+  if (q0 >= Lq) return;
+  const int diag = Lk - Lq;
+
+  const __bf16* qb = (const __bf16*)p.q + (VARLEN ? qtok * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+  const __bf16* kb = (const __bf16*)p.k + (VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
+  __bf16* ob = (__bf16*)p.o + (VARLEN ? qtok * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
+  float* lseb = p.lse + (VARLEN ? qtok : (int64_t)b * p.lse_sb) + (int64_t)h * p.lse_sh;
+
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, q0 + BM + diag);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- Q^T fragments (B operand of S^T = K Q^T), resident for the sweep.
+  // Rows past the sequence end read as zero (buffer bounds check).
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
+  const int qrow = q0 + wave * 32 + l32;
+  bf16x8 qf[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * p.q_ss + 16 * c + 8 * hh) * 2));
+
+  // K row read by this lane for A-operand row m = l32 (see file comment)
+  const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  // transposing-read coordinates for V^T
+  const int trG = lane >> 4;
+  const int tr_r = lane & 3;
+  const int tr_e = (lane >> 2) & 3;
+  const int tr_row = 8 * (trG >> 1) + tr_e;
+  const int tr_col = 16 * (trG & 1) + 4 * tr_r;
+
+  // global -> register staging of one K/V tile; rows past the sequence end
+  // read as zero (their scores are masked, their P entries are zero)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  const int lrow = tid / T::CH;
+  const int lcol = (tid % T::CH) * 8;
+  const uint32_t koff = (uint32_t)(lrow * p.k_ss + lcol) * 2;
+  const uint32_t voff = (uint32_t)(lrow * p.v_ss + lcol) * 2;
+  u32x4 kreg[T::NP], vreg[T::NP];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      const uint32_t r = (uint32_t)(j0 + u * T::RPP);
+      kreg[u] = buf_load16(rk, koff + r * (uint32_t)p.k_ss * 2);
+      vreg[u] = buf_load16(rv, voff + r * (uint32_t)p.v_ss * 2);
+    }
+  };
+  auto lstore = [&](int st) {
+    __bf16* Ks = smem + st * T::STAGE;
+    __bf16* Vs = Ks + BN * T::KSTR;
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      *(u32x4*)(Ks + (lrow + u * T::RPP) * T::KSTR + lcol) = kreg[u];
+      *(u32x4*)(Vs + (lrow + u * T::RPP) * T::VSTR + lcol) = vreg[u];
+    }
+  };
+
+  f32x16 oacc[T::ND];
+#pragma unroll
+  for (int i = 0; i < T::ND; ++i) oacc[i] = (f32x16){};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c2 = p.scale_log2;
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  wait_vmem();  // Q fragments have landed on every path into the loop
+  __syncthreads();
+
+  const int wave_last_row = q0 + wave * 32 + 31;
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    const int j0 = t * BN;
+    const bool more = t + 1 < ntiles;
+    if (more) gload(j0 + BN);
+
+    const bool wave_active = !CAUSAL || j0 <= wave_last_row + diag;
+    if (wave_active) {
+      const __bf16* Ks = smem + st * T::STAGE;
+      const __bf16* Vs = Ks + BN * T::KSTR;
+      // ---- S^T = K Q^T for two 32-key blocks
+      f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const bf16x8 kf = *(const bf16x8*)(Ks + (32 * kb2 + kperm) * T::KSTR + 16 * c + 8 * hh);
+          sacc[kb2] = mfma32(kf, qf[c], sacc[kb2]);
+        }
+      }
+      // ---- mask (only on tiles crossing the diagonal or the sequence end)
+      const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > q0 + wave * 32 + diag);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(Lk - 1, qrow + diag) : Lk - 1;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kj = j0 + 32 * kb2 + 16 * (i >> 3) + 8 * hh + (i & 7);
+            if (kj > lim) sacc[kb2][i] = -INFINITY;
+          }
+      }
+      // ---- online softmax: running max, rescale, exponentials, row sum
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_base) * c2);
+      const float nb = -m_base * c2;
+      float rs = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = fast_exp2(__builtin_fmaf(sacc[kb2][8 * half + e], c2, nb));
+            rs += pv;
+            pf[2 * kb2 + half][e] = (__bf16)pv;
+          }
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int db = 0; db < T::ND; ++db) {
+          const __bf16* vp = Vs + (16 * c + tr_row) * T::VSTR + 32 * db + tr_col;
+          const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
+          oacc[db] = mfma32(vf, pf[c], oacc[db]);
+        }
+      }
+    }
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
+  const float l_tot = l_run + wave_xor32(l_run);
+  if (qrow < Lq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)((int64_t)Lq * p.o_ss * 2));
+    const uint32_t orow = (uint32_t)(qrow * p.o_ss) * 2;
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(oacc[db][4 * gi + r] * inv);
+        buf_store8(__builtin_bit_cast(u32x2, w), ro, orow + (uint32_t)(32 * db + 8 * gi + 4 * hh) * 2);
+      }
+    if (hh == 0) lseb[qrow] = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  const long nblk = (long)p.num_m_tiles * p.Hq * p.B;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
+  if (d == 128) {
+    if (causal) return varlen ? launch<128, true, true>(p, stream) : launch<128, true, false>(p, stream);
+    return varlen ? launch<128, false, true>(p, stream) : launch<128, false, false>(p, stream);
+  }
+  if (causal) return varlen ? launch<64, true, true>(p, stream) : launch<64, true, false>(p, stream);
+  return varlen ? launch<64, false, true>(p, stream) : launch<64, false, false>(p, stream);
+}

@@ -1,0 +1,217 @@
+"""ctypes binding of libfa.so (the C ABI in include/fa.h).
+
+Argument marshalling only: every step of the attention computation runs in the
+library's HIP kernels.  Tensors are PyTorch-allocated device tensors; work is
+enqueued on the current torch stream.  The library is required: if it has not
+been built, or a call fails, an exception is raised -- there is no fallback.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_BF16 = 0
+FA_FP8_E4M3 = 2
+
+
+class FaError(RuntimeError):
+    """A libfa entry point returned a nonzero fa_status."""
+
+    def __init__(self, call, status, message):
+        super().__init__(f"{call} failed: status {status} ({message})")
+        self.status = status
+
+
+class FaTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Sq", ctypes.c_int32),
+                ("Sk", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float),
+                ("q", FaTensor), ("k", FaTensor), ("v", FaTensor), ("o", FaTensor),
+                ("lse", ctypes.c_void_p), ("q_descale", ctypes.c_void_p),
+                ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class FwdVarlenArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("nseq", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p),
+                ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+                ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
+                ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
+                ("o_stride_t", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Sq", ctypes.c_int32),
+                ("Sk", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float),
+                ("q", FaTensor), ("k", FaTensor), ("v", FaTensor), ("o", FaTensor),
+                ("dout", FaTensor), ("dq", FaTensor), ("dk", FaTensor), ("dv", FaTensor),
+                ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+# Every symbol include/fa.h declares.
+EXPORTS = ["fa_abi_version", "fa_status_string", "fa_fwd_workspace_size",
+           "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
+           "fa_quantize_fp8"]
+
+_lib = None
+
+
+def lib():
+    """Open libfa.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m io_aware_exact_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.fa_abi_version.restype = ctypes.c_int32
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_status_string.argtypes = [ctypes.c_int]
+        L.fa_fwd_workspace_size.restype = ctypes.c_size_t
+        L.fa_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
+        L.fa_bwd_workspace_size.restype = ctypes.c_size_t
+        L.fa_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp]
+        L.fa_fwd_varlen.restype = ctypes.c_int
+        L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), vp]
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd.argtypes = [ctypes.POINTER(BwdArgs), vp]
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.fa_quantize_fp8.restype = ctypes.c_int
+        L.fa_quantize_fp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _check(call, status):
+    if status != 0:
+        raise FaError(call, status, lib().fa_status_string(status).decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _t4(x):
+    """fa_tensor of a [B,S,H,d] tensor (d contiguous)."""
+    assert x.dim() == 4 and x.stride(3) == 1, "last dimension must be contiguous"
+    return FaTensor(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
+
+
+def _scale(d, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Dense forward.  q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16 on the GPU.
+    Returns (o [B,Sq,Hq,d] bf16, lse [B,Hq,Sq] fp32)."""
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    a = FwdArgs(dt, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
+                _t4(q), _t4(k), _t4(v), _t4(out), lse.data_ptr(), None, None, None, None, 0)
+    _check("fa_fwd", lib().fa_fwd(ctypes.byref(a), _stream()))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+               causal=False, scale=None, out=None, lse=None):
+    """Packed forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16; cu_seqlens_* int32
+    [nseq+1] on the GPU.  Returns (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32)."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    for x in (q, k, v):
+        assert x.stride(2) == 1
+    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32
+    nseq = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((Tq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    a = FwdVarlenArgs(dt, nseq, Hq, Hkv, d, int(max_seqlen_q), int(max_seqlen_k), Tq, Tk,
+                      int(bool(causal)), _scale(d, scale),
+                      q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      q.stride(0), q.stride(1), k.stride(0), k.stride(1),
+                      v.stride(0), v.stride(1), out.stride(0), out.stride(1),
+                      cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), lse.data_ptr())
+    _check("fa_fwd_varlen", lib().fa_fwd_varlen(ctypes.byref(a), _stream()))
+    return out, lse
+
+
+def bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace=None):
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return BwdArgs(dt, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
+                   _t4(q), _t4(k), _t4(v), _t4(o), _t4(dout), _t4(dq), _t4(dk), _t4(dv),
+                   lse.data_ptr(), ws_ptr, ws_bytes)
+
+
+def bwd(q, k, v, o, dout, lse, causal=False, scale=None):
+    """Dense backward.  Returns (dq, dk, dv) bf16."""
+    dq = torch.empty_like(q, dtype=torch.bfloat16)
+    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
+    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale)
+    nbytes = lib().fa_bwd_workspace_size(ctypes.byref(a))
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q.device)
+    a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, ws)
+    _check("fa_bwd", lib().fa_bwd(ctypes.byref(a), _stream()))
+    return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = fwd(q, k, v, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, do.contiguous(), lse, ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal=False, scale=None):
+    """Exact attention with autograd: q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16."""
+    return _Attention.apply(q, k, v, causal, scale)
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                     causal=False, scale=None):
+    """Packed variable-length forward; returns o [Tq,Hq,d]."""
+    return fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                      causal, scale)[0]

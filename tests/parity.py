@@ -1,0 +1,67 @@
+"""Helpers shared by the GPU parity tests: tolerances, comparisons and
+guarded output buffers."""
+import numpy as np
+import torch
+
+# Parity bars for bf16 inputs with fp32 accumulation, against the fp64 oracle
+# evaluated on the same (bf16-rounded) inputs.
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_MAX_ABS = 1e-3
+GRAD_MAX_ABS = 5e-2
+REL_L2 = 1e-2
+
+
+def stats(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    fin = np.isfinite(ref)
+    assert (np.isfinite(got) == fin).all(), "finite/infinite pattern differs"
+    assert (got[~fin] == ref[~fin]).all(), "infinite entries differ"
+    d = np.abs(got[fin] - ref[fin])
+    if d.size == 0:
+        return 0.0, 0.0, 0.0
+    nref = np.linalg.norm(ref[fin])
+    rel = float(np.linalg.norm(got[fin] - ref[fin]) / nref) if nref > 0 else float(np.linalg.norm(got[fin]))
+    return float(d.max()), float(d.mean()), rel
+
+
+def check_o(name, got, ref, max_abs=O_MAX_ABS, mean_abs=O_MEAN_ABS, rel=REL_L2):
+    mx, mn, rl = stats(got, ref)
+    print(f"  {name}: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rl:.3e}", flush=True)
+    assert mx <= max_abs and mn <= mean_abs and rl <= rel, (name, mx, mn, rl)
+    return mx, mn, rl
+
+
+def check_lse(name, got, ref, max_abs=LSE_MAX_ABS):
+    mx, mn, _ = stats(got, ref)
+    print(f"  {name}: max_abs={mx:.3e} mean_abs={mn:.3e}", flush=True)
+    assert mx <= max_abs, (name, mx)
+    return mx
+
+
+def check_grad(name, got, ref, max_abs=GRAD_MAX_ABS, rel=REL_L2):
+    mx, mn, rl = stats(got, ref)
+    print(f"  {name}: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rl:.3e}", flush=True)
+    assert mx <= max_abs and rl <= rel, (name, mx, rl)
+    return mx, mn, rl
+
+
+class Guarded:
+    """An output tensor embedded in a larger buffer whose guard regions hold
+    a sentinel bit pattern; the tensor itself is pre-filled with NaN so that
+    unwritten elements show up."""
+
+    GUARD = 4096
+
+    def __init__(self, shape, dtype, device="cuda"):
+        n = int(np.prod(shape))
+        self.buf = torch.empty(n + 2 * self.GUARD, dtype=dtype, device=device)
+        self.buf.fill_(-12345.0)
+        self.t = self.buf[self.GUARD:self.GUARD + n].view(shape)
+        self.t.fill_(float("nan"))
+
+    def check_guards(self):
+        lo = self.buf[:self.GUARD]
+        hi = self.buf[-self.GUARD:]
+        assert (lo == -12345.0).all() and (hi == -12345.0).all(), "write outside the output"

@@ -1,0 +1,75 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_exact_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(fa.EXPORTS)
+    L = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_strings():
+    L = fa.lib()
+    assert L.fa_abi_version() == 1
+    assert L.fa_status_string(0) == b"ok"
+    assert b"head dimension" in L.fa_status_string(3)
+
+
+FAKE = 0x7F0000000000  # never dereferenced: validation fails first
+
+
+def fwd_args(**kw):
+    B, Sq, Sk, Hq, Hkv, d = 1, 16, 16, 2, 2, 64
+    base = dict(dtype=0, B=B, Sq=Sq, Sk=Sk, Hq=Hq, Hkv=Hkv, d=d, causal=0, softmax_scale=0.125)
+    base.update({k: v for k, v in kw.items() if k in base})
+
+    def t(ptr, H):
+        return fa.FaTensor(ptr, base["Sq"] * H * base["d"], H * base["d"], base["d"])
+
+    a = fa.FwdArgs(base["dtype"], base["B"], base["Sq"], base["Sk"], base["Hq"], base["Hkv"],
+                   base["d"], base["causal"], base["softmax_scale"],
+                   kw.get("q", t(FAKE, 2)), kw.get("k", t(FAKE + (1 << 24), 2)),
+                   kw.get("v", t(FAKE + (2 << 24), 2)), kw.get("o", t(FAKE + (3 << 24), 2)),
+                   kw.get("lse", FAKE + (4 << 24)), None, None, None, None, 0)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=3, Hkv=2), 5), (dict(Sq=-1), 2),
+    (dict(dtype=7), 4), (dict(softmax_scale=float("nan")), 10),
+    (dict(q=fa.FaTensor(0, 2048, 128, 64)), 1), (dict(lse=0), 1),
+    (dict(q=fa.FaTensor(FAKE + 2, 2048, 128, 64)), 6),
+    (dict(q=fa.FaTensor(FAKE, 2048, 130, 64)), 6),
+    (dict(o=fa.FaTensor(FAKE + 64, 2048, 128, 64)), 8),
+])
+def test_fwd_rejects(kw, status):
+    a = fwd_args(**kw)
+    assert fa.lib().fa_fwd(ctypes.byref(a), None) == status
+
+
+def test_fwd_null_args():
+    assert fa.lib().fa_fwd(None, None) == 1
+    assert fa.lib().fa_fwd_varlen(None, None) == 1
+    assert fa.lib().fa_bwd(None, None) == 1
+
+
+def test_fwd_empty_is_noop():
+    a = fwd_args(Sq=0)
+    assert fa.lib().fa_fwd(ctypes.byref(a), None) == 0

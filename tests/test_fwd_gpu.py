@@ -1,0 +1,105 @@
+"""GPU parity of the dense and packed forward against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_exact_amd import fa, inputs
+from parity import Guarded, check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+
+
+def run_dense(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
+    print(f"dense B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}", flush=True)
+    q, k, v = inputs.qkv(B, Sq, Sk, Hq, Hkv, d, seed, device="cuda")
+    go = Guarded((B, Sq, Hq, d), torch.bfloat16)
+    gl = Guarded((B, Hq, Sq), torch.float32)
+    fa.fwd(q, k, v, causal, scale, out=go.t, lse=gl.t)
+    torch.cuda.synchronize()
+    go.check_guards()
+    gl.check_guards()
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, causal, scale)
+    check_o("O", go.t.float().cpu().numpy(), o_ref)
+    check_lse("LSE", gl.t.cpu().numpy(), lse_ref)
+    return go.t, gl.t
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_config(causal):
+    # B=1, H=2, Sq=Sk=256, d=64, iid N(0,1), scale 1/sqrt(d)
+    run_dense(1, 256, 256, 2, 2, 64, causal, seed=0)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 1, 1, 1, 64), (1, 2, 2, 2, 2, 128), (2, 127, 127, 3, 3, 64),
+    (1, 129, 129, 2, 2, 128), (1, 1000, 1000, 2, 1, 128), (2, 200, 333, 4, 2, 64),
+    (1, 333, 200, 2, 2, 128), (1, 64, 1, 2, 1, 128), (1, 300, 257, 8, 1, 128),
+    (1, 512, 512, 8, 2, 64),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes(shape, causal):
+    B, Sq, Sk, Hq, Hkv, d = shape
+    run_dense(B, Sq, Sk, Hq, Hkv, d, causal, seed=sum(shape))
+
+
+def test_scale_and_strided_views():
+    # q/k/v as views into a packed [B,S,3,H,d] buffer (non-trivial strides)
+    B, S, H, d = 2, 190, 4, 128
+    qkv = inputs.normal((B, S, 3, H, d), 11, device="cuda")
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    o, lse = fa.fwd(q, k, v, False, 0.05)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, False, 0.05)
+    check_o("O", o.float().cpu().numpy(), o_ref)
+    check_lse("LSE", lse.cpu().numpy(), lse_ref)
+
+
+def test_deterministic():
+    q, k, v = inputs.qkv(2, 700, 700, 4, 2, 128, 5, device="cuda")
+    outs = [fa.fwd(q, k, v, True) for _ in range(3)]
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_gqa_equals_repeated_heads():
+    q, k, v = inputs.qkv(1, 300, 300, 8, 2, 128, 6, device="cuda")
+    o1, l1 = fa.fwd(q, k, v, True)
+    o2, l2 = fa.fwd(q, k.repeat_interleave(4, dim=2).contiguous(),
+                    v.repeat_interleave(4, dim=2).contiguous(), True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen(d, causal):
+    lens = [1, 0, 17, 128, 129, 300, 64, 255]
+    Hq, Hkv = 4, 2
+    print(f"varlen lens={lens} d={d} causal={causal}", flush=True)
+    q, k, v = inputs.packed_qkv(lens, lens, Hq, Hkv, d, 21, device="cuda")
+    cu = inputs.cu_seqlens(lens, device="cuda")
+    T = sum(lens)
+    go = Guarded((T, Hq, d), torch.bfloat16)
+    gl = Guarded((Hq, T), torch.float32)
+    fa.fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), causal, None, out=go.t, lse=gl.t)
+    torch.cuda.synchronize()
+    go.check_guards()
+    gl.check_guards()
+    o_ref, lse_ref = oracle.attention_fwd_varlen(q, k, v, cu.cpu(), cu.cpu(), causal)
+    check_o("O", go.t.float().cpu().numpy(), o_ref)
+    check_lse("LSE", gl.t.cpu().numpy(), lse_ref)
+
+
+def test_varlen_equals_dense_per_sequence():
+    lens_q = [100, 37, 256]
+    lens_k = [150, 37, 300]
+    q, k, v = inputs.packed_qkv(lens_q, lens_k, 4, 1, 128, 22, device="cuda")
+    cq = inputs.cu_seqlens(lens_q, device="cuda")
+    ck = inputs.cu_seqlens(lens_k, device="cuda")
+    o, lse = fa.fwd_varlen(q, k, v, cq, ck, max(lens_q), max(lens_k), True)
+    for z in range(3):
+        qs, qe = int(cq[z]), int(cq[z + 1])
+        ks, ke = int(ck[z]), int(ck[z + 1])
+        od, ld = fa.fwd(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], True)
+        assert torch.equal(od[0], o[qs:qe]) and torch.equal(ld[0], lse[:, qs:qe])

@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of IO-aware exact attention on one AMD Instinct MI355X.
+
+A step is one pass of the attention hot path over one batch: the forward
+(fa_fwd: O and LSE) followed by the recomputation-based backward (fa_bwd: dQ,
+dK, dV) at B=2, H=16, Sq=Sk=8192, d=128, bf16, non-causal, iid N(0,1) inputs
+(seed 2000), all resident in HBM before timing starts.  Throughput counts the
+method's algorithmic flops: 4*B*H*Sq*Sk*d for the forward and 2.5 times that
+for the backward (five GEMM-shaped products: the recomputed scores, dP, dV,
+dK, dQ), so fwd+bwd = 14*B*H*Sq*Sk*d.  Any extra recomputation the kernels do
+is not counted.
+
+Printed: one JSON line with the whole-step TFLOP/s, the forward alone, the
+forward kernel's roofline fraction against the dense bf16 MFMA peak
+(256 CU x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6
+WORKLOAD = dict(B=2, S=8192, H=16, d=128, causal=False, seed=2000)
+
+
+def fwd_flops(B, Sq, Sk, H, d, causal):
+    return 4.0 * B * H * Sq * Sk * d / (2 if causal else 1)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("fwd.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "io_aware_exact_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per forward launch from the committed counter summary, or
+    None if it was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "fwd_bf16_b2_h16_s8192_d128_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, do, causal, with_bwd):
+    """The fp64 oracle on one full (batch 0, head 0) slice of the step,
+    converted to a TFLOP/s rate with the same algorithmic flop count."""
+    import oracle
+    B, S, H, d = q.shape
+    t0 = time.perf_counter()
+    if with_bwd:
+        oracle.attention_bwd(q[:1, :, :1], k[:1, :, :1], v[:1, :, :1], do[:1, :, :1],
+                             causal, None)
+    else:
+        oracle.attention_fwd(q[:1, :, :1], k[:1, :, :1], v[:1, :, :1], causal, None)
+    dt = time.perf_counter() - t0
+    flops = (3.5 if with_bwd else 1.0) * fwd_flops(1, S, S, 1, d, causal)
+    what = "forward+backward" if with_bwd else "forward"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 {what} of one full (b,h) slice of the step (S={S}, d={d}) "
+                      f"took {dt:.1f} s; rate uses the step's algorithmic flops"}
+
+
+def sampled_check(q, k, v, o, lse, causal):
+    """Oracle rows {0, 1, S-1} plus 13 seeded rows of (b, h) = (0, 0) and (B-1, H-1)."""
+    import numpy as np
+    import oracle
+    from io_aware_exact_amd import inputs
+    B, S, H, d = q.shape
+    rows = inputs.sample_indices(S, 13, 77, always=(0, 1, S - 1))
+    bi, hi, ii = [], [], []
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        for i in rows:
+            bi.append(b), hi.append(h), ii.append(i)
+    o_ref, lse_ref = oracle.attention_fwd_rows(q, k, v, bi, hi, ii, causal)
+    o_got = o[bi, ii, hi].float().cpu().numpy()
+    l_got = lse[bi, hi, ii].cpu().numpy()
+    return float(np.abs(o_got - o_ref).max()), float(np.abs(l_got - lse_ref).max())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 launches), the reference "
+                         "for scaling HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(batch and heads shard with no exchange, so N GPUs run N copies of this step)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": x.numel() * 4,
+                          "copy_calibration_bytes_written": y.numel() * 4, "launches": 3}))
+        return
+    from io_aware_exact_amd import fa, inputs
+    fa.lib()
+
+    W = WORKLOAD
+    B, S, H, d, causal = W["B"], W["S"], W["H"], W["d"], W["causal"]
+    q, k, v, do = inputs.qkv(B, S, S, H, H, d, W["seed"], device="cuda", with_dout=True)
+    o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    have_bwd = True
+    try:
+        fa.fwd(q, k, v, causal, out=o, lse=lse)
+        fa.bwd(q, k, v, o, do, lse, causal)
+    except fa.FaError:
+        have_bwd = False
+
+    def step():
+        fa.fwd(q, k, v, causal, out=o, lse=lse)
+        if have_bwd:
+            fa.bwd(q, k, v, o, do, lse, causal)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # forward kernel alone (one launch per fa_fwd call) on the same stream
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        fa.fwd(q, k, v, causal, out=o, lse=lse)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ms_fwd = f0.elapsed_time(f1) / args.steps
+
+    ff = fwd_flops(B, S, S, H, d, causal)
+    step_flops = ff * (3.5 if have_bwd else 1.0)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = ff / (ms_fwd * 1e-3) / 1e12
+    err_o, err_lse = sampled_check(q, k, v, o, lse, causal)
+
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s (bf16, d=128)" if have_bwd
+                  else "attention fwd TFLOP/s (bf16, d=128)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "wall_s": round(wall, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic iid N(0,1), seed 2000",
+        "config": {"workload": f"exact attention {'fwd+bwd' if have_bwd else 'fwd'}, "
+                               f"B={B} H={H} Sq=Sk={S} d={d} non-causal",
+                   "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "causal": causal},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"tflops": round(fwd_tflops, 2), "ms": round(ms_fwd, 4),
+                "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "fwd_bf16_kernel<128,false,false>", "bound": "mfma",
+                     "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile()},
+        "check": {"o_max_abs": err_o, "lse_max_abs": err_lse},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(q, k, v, do, causal, have_bwd)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

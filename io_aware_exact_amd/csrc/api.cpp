@@ -106,6 +106,58 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
   return FA_OK;
 }
 
+size_t bwd_delta_bytes(const fa_bwd_args* a) {
+  const size_t n = (size_t)(a->B > 0 ? a->B : 0) * (size_t)(a->Hq > 0 ? a->Hq : 0) *
+                   (size_t)(a->Sq > 0 ? a->Sq : 0) * 4;
+  return (n + 255) & ~(size_t)255;
+}
+
+fa_status check_bwd(const fa_bwd_args* a) {
+  if (!a) return FA_ERR_NULL;
+  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
+  if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
+  if (!isfinite(a->softmax_scale)) return FA_ERR_SCALE;
+  const fa_tensor* ts[8] = {&a->q, &a->k, &a->v, &a->o, &a->dout, &a->dq, &a->dk, &a->dv};
+  for (int i = 0; i < 8; ++i)
+    if (!ts[i]->ptr) return FA_ERR_NULL;
+  if (!a->lse) return FA_ERR_NULL;
+  for (int i = 0; i < 8; ++i)
+    if (!aligned16(ts[i]->ptr) || !strides_ok(*ts[i], 8)) return FA_ERR_ALIGN;
+  if ((uintptr_t)a->lse & 3u) return FA_ERR_ALIGN;
+  const int64_t B = a->B, Sq = a->Sq, Sk = a->Sk, Hq = a->Hq, Hkv = a->Hkv, d = a->d;
+  if (((Sq + 127) / 128) * Hq * B > 0x7fffffffLL || ((Sk + 127) / 128) * Hkv * B > 0x7fffffffLL)
+    return FA_ERR_SHAPE;
+  if (B * Sq * Hq > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
+  if (!fits32(Sq, a->q.stride_s, 2) || !fits32(Sq, a->dout.stride_s, 2) ||
+      !fits32(Sk, a->k.stride_s, 2) || !fits32(Sk, a->v.stride_s, 2))
+    return FA_ERR_SHAPE;
+  const size_t need = bwd_delta_bytes(a);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
+  // outputs must not overlap each other, the inputs or the workspace
+  const Span in[6] = {
+      span4(a->q.ptr, B, Sq, Hq, d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2),
+      span4(a->k.ptr, B, Sk, Hkv, d, a->k.stride_b, a->k.stride_s, a->k.stride_h, 2),
+      span4(a->v.ptr, B, Sk, Hkv, d, a->v.stride_b, a->v.stride_s, a->v.stride_h, 2),
+      span4(a->o.ptr, B, Sq, Hq, d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2),
+      span4(a->dout.ptr, B, Sq, Hq, d, a->dout.stride_b, a->dout.stride_s, a->dout.stride_h, 2),
+      {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)(B * Hq * Sq * 4)}};
+  const Span out[4] = {
+      span4(a->dq.ptr, B, Sq, Hq, d, a->dq.stride_b, a->dq.stride_s, a->dq.stride_h, 2),
+      span4(a->dk.ptr, B, Sk, Hkv, d, a->dk.stride_b, a->dk.stride_s, a->dk.stride_h, 2),
+      span4(a->dv.ptr, B, Sk, Hkv, d, a->dv.stride_b, a->dv.stride_s, a->dv.stride_h, 2),
+      {(uintptr_t)a->workspace, (uintptr_t)a->workspace + need}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(out[i], in[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,14 +237,48 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, hipStream_t stream) {
 }
 
 size_t fa_bwd_workspace_size(const fa_bwd_args* a) {
-  (void)a;
-  return 0;
+  if (!a) return 0;
+  return bwd_delta_bytes(a);
 }
 
 fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
-  (void)stream;
-  if (!a) return FA_ERR_NULL;
-  return FA_ERR_DTYPE;
+  const fa_status s = check_bwd(a);
+  if (s != FA_OK) return s;
+  if (a->B == 0 || a->Sq == 0 || a->Sk == 0) {
+    // no query rows or no keys: dQ, dK, dV are all zero
+    const fa_tensor* outs[3] = {&a->dq, &a->dk, &a->dv};
+    const int64_t S[3] = {a->Sq, a->Sk, a->Sk};
+    const int64_t H[3] = {a->Hq, a->Hkv, a->Hkv};
+    for (int i = 0; i < 3; ++i) {
+      const fa_tensor& t = *outs[i];
+      if (a->B == 0 || S[i] == 0) continue;
+      const bool dense = t.stride_h == a->d && t.stride_s == H[i] * a->d && t.stride_b == S[i] * t.stride_s;
+      if (!dense) return FA_ERR_SHAPE;
+      if (hipMemsetAsync(t.ptr, 0, (size_t)(a->B * S[i] * H[i] * a->d * 2), stream) != hipSuccess)
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+  }
+  BwdParams p = {};
+  p.q = a->q.ptr; p.k = a->k.ptr; p.v = a->v.ptr; p.o = a->o.ptr; p.dout = a->dout.ptr;
+  p.dq = a->dq.ptr; p.dk = a->dk.ptr; p.dv = a->dv.ptr;
+  p.lse = a->lse;
+  p.delta = (float*)a->workspace;
+  p.dq_acc = nullptr;
+  p.q_sb = a->q.stride_b; p.q_ss = a->q.stride_s; p.q_sh = a->q.stride_h;
+  p.k_sb = a->k.stride_b; p.k_ss = a->k.stride_s; p.k_sh = a->k.stride_h;
+  p.v_sb = a->v.stride_b; p.v_ss = a->v.stride_s; p.v_sh = a->v.stride_h;
+  p.o_sb = a->o.stride_b; p.o_ss = a->o.stride_s; p.o_sh = a->o.stride_h;
+  p.do_sb = a->dout.stride_b; p.do_ss = a->dout.stride_s; p.do_sh = a->dout.stride_h;
+  p.dq_sb = a->dq.stride_b; p.dq_ss = a->dq.stride_s; p.dq_sh = a->dq.stride_h;
+  p.dk_sb = a->dk.stride_b; p.dk_ss = a->dk.stride_s; p.dk_sh = a->dk.stride_h;
+  p.dv_sb = a->dv.stride_b; p.dv_ss = a->dv.stride_s; p.dv_sh = a->dv.stride_h;
+  p.B = a->B; p.Sq = a->Sq; p.Sk = a->Sk; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.causal = a->causal != 0;
+  p.scale = a->softmax_scale;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, stream));
 }
 
 fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int32_t B, int32_t S,

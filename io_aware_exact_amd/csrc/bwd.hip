@@ -1,0 +1,500 @@
+// Backward kernels of IO-aware exact attention for gfx950 (bf16 in, fp32
+// accumulate, bf16 gradients).
+//
+// Method.  The backward recomputes the attention probabilities from the
+// saved row log-sum-exp instead of reading a stored probability matrix
+// ("Dao and colleagues: IO-aware exact attention with FlashAttention",
+// summary: tiling plus recomputation), and its reductions are deterministic
+// (Dao-AILab repository overview: deterministic backward passes).  With
+// P = exp(scale Q K^T - LSE) and D_i = sum_c dO_ic O_ic, the calculus
+// derivative of exact attention is
+//     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),
+//     dK = scale dS^T Q,   dQ = scale dS K.
+//
+// gfx950 mapping (32x32x16 bf16 MFMA, operand layouts in device_common.h).
+//   * bwd_preprocess: D = rowsum(dO o O) in fp32, one 16-lane group per row.
+//   * bwd_dkdv: a workgroup of 4 waves owns 128 keys of one (batch, kv head);
+//     each wave keeps its 32 K and V rows in VGPRs as the B operands of
+//     S = Q K^T and dP = dO V^T, and its dK^T, dV^T accumulators for the
+//     whole sweep.  Query tiles of 64 rows (Q, dO, LSE, D) of every query
+//     head of the group stream through a double-buffered LDS ring.  Query
+//     rows are fed to the A operand in a permuted order so that accumulator
+//     registers 0..7 / 8..15 of a lane hold 8 consecutive queries: P and dS
+//     are then directly the B operands of dV^T += dO^T P and dK^T += Q^T dS
+//     (dO^T and Q^T come from the LDS transposing read).  Each key's gradient
+//     is a sum in a fixed order over (query head, query tile): no atomics.
+//   * bwd_dq: a workgroup of 4 waves owns 128 query rows; each wave keeps
+//     Q^T, dO^T, LSE and D of its 32 rows in registers and sweeps the K/V
+//     tiles (double-buffered in LDS) in order, computing S^T = K Q^T,
+//     dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.  dQ is therefore a
+//     fixed-order sum as well; the price is recomputing S and dP a second
+//     time (7 products instead of the method's 5).
+//   * Causal: key tiles above the diagonal are skipped on both sides, element
+//     masks only on tiles crossing it.  Rows past the sequence end read as
+//     zero (buffer bounds checks) and their LSE is taken as +inf, so their
+//     probabilities are exactly zero.
+#include "device_common.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int NTHREADS = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// A-operand row order that makes accumulator registers 0..7 / 8..15 of a
+// lane cover 8 consecutive rows (see the forward kernel).
+__device__ __forceinline__ int row_perm(int l32) {
+  return 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+}
+
+// Row (within a 32-row block) held by accumulator register i of a lane in
+// half hh, when the A operand rows were fed in row_perm order.
+__device__ __forceinline__ int perm_row_of_reg(int i, int hh) {
+  return (i < 8) ? 8 * hh + i : 16 + 8 * hh + (i - 8);
+}
+
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = w & 7, s = w >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO_ic O_ic (fp32), written to delta[b][h][i].
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void bwd_preprocess_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;                 // lanes per row (16 B each)
+  constexpr int RPB = NTHREADS / LPR;        // rows per block
+  const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const long nrows = (long)p.B * p.Sq * p.Hq;
+  const int c = (threadIdx.x % LPR) * 8;
+  float acc = 0.f;
+  long b = 0, i = 0, h = 0;
+  if (row < nrows) {
+    h = row % p.Hq;
+    const long t = row / p.Hq;
+    i = t % p.Sq;
+    b = t / p.Sq;
+    const bf16x8 o = *(const bf16x8*)((const __bf16*)p.o + b * p.o_sb + i * p.o_ss + h * p.o_sh + c);
+    const bf16x8 g = *(const bf16x8*)((const __bf16*)p.dout + b * p.do_sb + i * p.do_ss + h * p.do_sh + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 64);
+  if (row < nrows && (threadIdx.x % LPR) == 0) p.delta[(b * p.Hq + h) * p.Sq + i] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV for 128 keys of one (batch, kv head).
+template <int D>
+struct DkdvTile {
+  static constexpr int BKV = 128;             // keys per workgroup (32 per wave)
+  static constexpr int BQ = 64;               // query rows per streamed tile
+  static constexpr int STR = D + 8;           // LDS row stride (elements)
+  static constexpr int NC = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int CH = D / 8;
+  static constexpr int RPP = NTHREADS / CH;
+  static constexpr int NP = BQ / RPP;
+  static constexpr int TILE = BQ * STR;       // elements of one Q or dO tile
+  static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using T = DkdvTile<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE_BYTES];
+
+  const int nkt = (p.Sk + T::BKV - 1) / T::BKV;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = L % nkt;
+  const int rest = L / nkt;
+  const int g = rest % p.Hkv;
+  const int b = rest / p.Hkv;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int Lq = p.Sq, Lk = p.Sk;
+  const int diag = Lk - Lq;
+  const int k0 = kt * T::BKV;
+  const int kw0 = k0 + 32 * wave;           // first key of this wave
+  const int key = kw0 + l32;                // key owned by this lane (C column)
+
+  // ---- resident K and V rows: B operands of S = Q K^T and dP = dO V^T
+  const __bf16* kb = (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  bf16x8 kf[T::NC], vf[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+    kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)(key * p.k_ss + 16 * c + 8 * hh) * 2));
+    vf[c] = __builtin_bit_cast(bf16x8, buf_load16(rv, (uint32_t)(key * p.v_ss + 16 * c + 8 * hh) * 2));
+  }
+
+  // ---- query tiles to visit: every head of the group, tiles from the first
+  // one that can see this workgroup's keys
+  const int nqt = (Lq + T::BQ - 1) / T::BQ;
+  int qt0 = 0;
+  if (CAUSAL) qt0 = max(0, k0 - diag) / T::BQ;
+  const int per_head = max(0, nqt - qt0);
+  const int niter = per_head * p.group;
+
+  const int lrow = tid / T::CH;
+  const int lcol = (tid % T::CH) * 8;
+  u32x4 qreg[T::NP], oreg[T::NP];
+  float sval = 0.f;
+  __amdgpu_buffer_rsrc_t rq, rdo;
+  const float* lse_h = nullptr;
+  const float* del_h = nullptr;
+  auto head_setup = [&](int h) {
+    const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    const __bf16* db = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
+    rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
+    rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
+    lse_h = p.lse + ((int64_t)b * p.Hq + h) * Lq;
+    del_h = p.delta + ((int64_t)b * p.Hq + h) * Lq;
+  };
+  auto gload = [&](int it) {
+    const int h = p.group * g + it / per_head;
+    const int q0 = (qt0 + it % per_head) * T::BQ;
+    head_setup(h);
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      const uint32_t r = (uint32_t)(q0 + lrow + u * T::RPP);
+      qreg[u] = buf_load16(rq, (r * (uint32_t)p.q_ss + lcol) * 2);
+      oreg[u] = buf_load16(rdo, (r * (uint32_t)p.do_ss + lcol) * 2);
+    }
+    // threads 0..63 fetch LSE (as log2 values), threads 64..127 fetch D
+    if (tid < 2 * T::BQ) {
+      const int r = q0 + (tid & (T::BQ - 1));
+      if (tid < T::BQ) {
+        float v = r < Lq ? lse_h[r] : INFINITY;
+        // no visible key (LSE = -inf) or padding: probabilities are zero
+        sval = (v == -INFINITY) ? INFINITY : v * LOG2E;
+      } else {
+        sval = r < Lq ? del_h[r] : 0.f;
+      }
+    }
+  };
+  auto lstore = [&](int st) {
+    __bf16* Qs = (__bf16*)(smem + st * T::STAGE_BYTES);
+    __bf16* Os = Qs + T::TILE;
+    float* stats = (float*)(Os + T::TILE);
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      *(u32x4*)(Qs + (lrow + u * T::RPP) * T::STR + lcol) = qreg[u];
+      *(u32x4*)(Os + (lrow + u * T::RPP) * T::STR + lcol) = oreg[u];
+    }
+    if (tid < 2 * T::BQ) stats[tid] = sval;
+  };
+
+  f32x16 dk[T::ND], dv[T::ND];
+#pragma unroll
+  for (int i = 0; i < T::ND; ++i) {
+    dk[i] = (f32x16){};
+    dv[i] = (f32x16){};
+  }
+  const float c2 = p.scale_log2;
+  const int prow = row_perm(l32);
+  const int trG = lane >> 4;
+  const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
+  const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
+  const bool wave_has_keys = kw0 < Lk;
+
+  if (niter > 0) {
+    gload(0);
+    wait_vmem();
+    lstore(0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  for (int it = 0; it < niter; ++it) {
+    const int st = it & 1;
+    const int q0 = (qt0 + it % per_head) * T::BQ;
+    const bool more = it + 1 < niter;
+    if (more) gload(it + 1);
+
+    const __bf16* Qs = (const __bf16*)(smem + st * T::STAGE_BYTES);
+    const __bf16* Os = Qs + T::TILE;
+    const float* lse2s = (const float*)(Os + T::TILE);
+    const float* dels = lse2s + T::BQ;
+#pragma unroll
+    for (int qb = 0; qb < T::BQ / 32; ++qb) {
+      const int qr0 = q0 + 32 * qb;
+      // skip query blocks that see none of this wave's keys
+      bool active = wave_has_keys && qr0 < Lq;
+      if (CAUSAL) active = active && (qr0 + 31 + diag >= kw0);
+      if (!active) continue;
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c) {
+        const int off = (32 * qb + prow) * T::STR + 16 * c + 8 * hh;
+        s = mfma32(*(const bf16x8*)(Qs + off), kf[c], s);
+        dp = mfma32(*(const bf16x8*)(Os + off), vf[c], dp);
+      }
+      const f32x4* l4 = (const f32x4*)(lse2s + 32 * qb + 8 * hh);
+      const f32x4* d4 = (const f32x4*)(dels + 32 * qb + 8 * hh);
+      const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+      const f32x4 da = d4[0], db = d4[1], dc = d4[4], dd = d4[5];
+      const float lrow_v[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
+                                lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
+      const float drow_v[16] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3],
+                                dc[0], dc[1], dc[2], dc[3], dd[0], dd[1], dd[2], dd[3]};
+      const bool need_mask = (kw0 + 31 >= Lk) || (CAUSAL && qr0 + diag < kw0 + 31);
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(__builtin_fmaf(s[i], c2, -lrow_v[i]));
+        if (need_mask) {
+          const int iq = qr0 + perm_row_of_reg(i, hh);
+          if (key >= Lk || (CAUSAL && key > iq + diag)) pv = 0.f;
+        }
+        const float dsv = pv * (dp[i] - drow_v[i]);
+        pb[i >> 3][i & 7] = (__bf16)pv;
+        dsb[i >> 3][i & 7] = (__bf16)dsv;
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (A operands by transposing reads)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int dbk = 0; dbk < T::ND; ++dbk) {
+          const int toff = (32 * qb + 16 * kc + tr_row) * T::STR + 32 * dbk + tr_col;
+          const bf16x8 oa = cat_bf16(lds_read_tr16(Os + toff), lds_read_tr16(Os + toff + 4 * T::STR));
+          dv[dbk] = mfma32(oa, pb[kc], dv[dbk]);
+          const bf16x8 qa = cat_bf16(lds_read_tr16(Qs + toff), lds_read_tr16(Qs + toff + 4 * T::STR));
+          dk[dbk] = mfma32(qa, dsb[kc], dk[dbk]);
+        }
+      }
+    }
+    // the other stage was last read before the previous barrier
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale * dK^T^T, dV = dV^T^T, bf16, one key row per lane
+  if (key < Lk) {
+    __bf16* dkb = (__bf16*)p.dk + (int64_t)b * p.dk_sb + (int64_t)g * p.dk_sh + (int64_t)key * p.dk_ss;
+    __bf16* dvb = (__bf16*)p.dv + (int64_t)b * p.dv_sb + (int64_t)g * p.dv_sh + (int64_t)key * p.dv_ss;
+#pragma unroll
+    for (int dbk = 0; dbk < T::ND; ++dbk)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          wk[r] = (__bf16)(dk[dbk][4 * gi + r] * p.scale);
+          wv[r] = (__bf16)(dv[dbk][4 * gi + r]);
+        }
+        const int col = 32 * dbk + 8 * gi + 4 * hh;
+        *(bf16x4*)(dkb + col) = wk;
+        *(bf16x4*)(dvb + col) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ for 128 query rows of one (batch, query head).
+template <int D>
+struct DqTile {
+  static constexpr int BM = 128;
+  static constexpr int BN = 64;
+  static constexpr int STR = D + 8;
+  static constexpr int NC = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int CH = D / 8;
+  static constexpr int RPP = NTHREADS / CH;
+  static constexpr int NP = BN / RPP;
+  static constexpr int TILE = BN * STR;
+  static constexpr int STAGE = 2 * TILE;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdParams p) {
+  using T = DqTile<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::STAGE];
+
+  const int nmt = (p.Sq + T::BM - 1) / T::BM;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int mt = L % nmt;
+  const int rest = L / nmt;
+  const int h = rest % p.Hq;
+  const int b = rest / p.Hq;
+  if (CAUSAL) mt = nmt - 1 - mt;
+  const int g = h / p.group;
+  const int Lq = p.Sq, Lk = p.Sk;
+  const int diag = Lk - Lq;
+  const int q0 = mt * T::BM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int qrow = q0 + 32 * wave + l32;
+
+  const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+  const __bf16* dob = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
+  const __bf16* kb = (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+
+  // ---- resident Q^T, dO^T fragments (B operands), LSE and D of this row
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dob, (uint32_t)((int64_t)Lq * p.do_ss * 2));
+  bf16x8 qf[T::NC], of[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+    qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * p.q_ss + 16 * c + 8 * hh) * 2));
+    of[c] = __builtin_bit_cast(bf16x8, buf_load16(rdo, (uint32_t)(qrow * p.do_ss + 16 * c + 8 * hh) * 2));
+  }
+  float lse2 = INFINITY, dlt = 0.f;
+  if (qrow < Lq) {
+    const float v = p.lse[((int64_t)b * p.Hq + h) * Lq + qrow];
+    lse2 = (v == -INFINITY) ? INFINITY : v * LOG2E;
+    dlt = p.delta[((int64_t)b * p.Hq + h) * Lq + qrow];
+  }
+
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, q0 + T::BM + diag);
+  const int ntiles = kend > 0 ? (kend + T::BN - 1) / T::BN : 0;
+
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  const int lrow = tid / T::CH;
+  const int lcol = (tid % T::CH) * 8;
+  u32x4 kreg[T::NP], vreg[T::NP];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      const uint32_t r = (uint32_t)(j0 + lrow + u * T::RPP);
+      kreg[u] = buf_load16(rk, (r * (uint32_t)p.k_ss + lcol) * 2);
+      vreg[u] = buf_load16(rv, (r * (uint32_t)p.v_ss + lcol) * 2);
+    }
+  };
+  auto lstore = [&](int st) {
+    __bf16* Ks = smem + st * T::STAGE;
+    __bf16* Vs = Ks + T::TILE;
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      *(u32x4*)(Ks + (lrow + u * T::RPP) * T::STR + lcol) = kreg[u];
+      *(u32x4*)(Vs + (lrow + u * T::RPP) * T::STR + lcol) = vreg[u];
+    }
+  };
+
+  f32x16 dq[T::ND];
+#pragma unroll
+  for (int i = 0; i < T::ND; ++i) dq[i] = (f32x16){};
+  const float c2 = p.scale_log2;
+  const int prow = row_perm(l32);
+  const int trG = lane >> 4;
+  const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
+  const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
+  const int wave_last_row = q0 + 32 * wave + 31;
+
+  if (ntiles > 0) {
+    gload(0);
+    wait_vmem();
+    lstore(0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    const int j0 = t * T::BN;
+    const bool more = t + 1 < ntiles;
+    if (more) gload(j0 + T::BN);
+
+    const bool wave_active = (q0 + 32 * wave < Lq) && (!CAUSAL || j0 <= wave_last_row + diag);
+    if (wave_active) {
+      const __bf16* Ks = smem + st * T::STAGE;
+      const __bf16* Vs = Ks + T::TILE;
+      const bool need_mask = (j0 + T::BN > Lk) || (CAUSAL && j0 + T::BN - 1 > q0 + 32 * wave + diag);
+      const int lim = CAUSAL ? min(Lk - 1, qrow + diag) : Lk - 1;
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+        for (int c = 0; c < T::NC; ++c) {
+          const int off = (32 * kb2 + prow) * T::STR + 16 * c + 8 * hh;
+          s = mfma32(*(const bf16x8*)(Ks + off), qf[c], s);
+          dp = mfma32(*(const bf16x8*)(Vs + off), of[c], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = fast_exp2(__builtin_fmaf(s[i], c2, -lse2));
+          if (need_mask) {
+            const int kj = j0 + 32 * kb2 + perm_row_of_reg(i, hh);
+            if (kj > lim) pv = 0.f;
+          }
+          dsb[2 * kb2 + (i >> 3)][i & 7] = (__bf16)(pv * (dp[i] - dlt));
+        }
+      }
+      // dQ^T += K^T dS^T  (K^T by transposing reads)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int dbk = 0; dbk < T::ND; ++dbk) {
+          const __bf16* kp = Ks + (16 * c + tr_row) * T::STR + 32 * dbk + tr_col;
+          const bf16x8 ka = cat_bf16(lds_read_tr16(kp), lds_read_tr16(kp + 4 * T::STR));
+          dq[dbk] = mfma32(ka, dsb[c], dq[dbk]);
+        }
+      }
+    }
+    // the other stage was last read before the previous barrier
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < Lq) {
+    __bf16* dqb = (__bf16*)p.dq + (int64_t)b * p.dq_sb + (int64_t)h * p.dq_sh + (int64_t)qrow * p.dq_ss;
+#pragma unroll
+    for (int dbk = 0; dbk < T::ND; ++dbk)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(dq[dbk][4 * gi + r] * p.scale);
+        *(bf16x4*)(dqb + 32 * dbk + 8 * gi + 4 * hh) = w;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  {
+    constexpr int RPB = NTHREADS / (D / 8);
+    const long rows = (long)p.B * p.Sq * p.Hq;
+    const long nblk = (rows + RPB - 1) / RPB;
+    if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.Sk > 0) {
+    const long nblk = (long)((p.Sk + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV) * p.Hkv * p.B;
+    if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const long nblk = (long)((p.Sq + DqTile<D>::BM - 1) / DqTile<D>::BM) * p.Hq * p.B;
+    if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_bwd<128, true>(p, stream) : launch_bwd<128, false>(p, stream);
+  return causal ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
+}

@@ -53,3 +53,4 @@ struct BwdParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen,
                            hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);

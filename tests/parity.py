@@ -10,6 +10,12 @@ O_MEAN_ABS = 2e-3
 LSE_MAX_ABS = 1e-3
 GRAD_MAX_ABS = 5e-2
 REL_L2 = 1e-2
+# Gradients are stored in bf16, whose rounding alone moves a value by up to
+# 2^-9 of its magnitude.  At the benchmark shapes gradient entries are ~1e-2
+# and this term is negligible; on degenerate shapes (one key shared by a
+# hundred query rows) entries reach ~20, where half an ulp is 0.06.  The
+# gradient bar is therefore GRAD_MAX_ABS plus one bf16 ulp of the exact value.
+BF16_ULP_REL = 2.0 ** -8
 
 
 def stats(got, ref):
@@ -42,8 +48,12 @@ def check_lse(name, got, ref, max_abs=LSE_MAX_ABS):
 
 def check_grad(name, got, ref, max_abs=GRAD_MAX_ABS, rel=REL_L2):
     mx, mn, rl = stats(got, ref)
-    print(f"  {name}: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rl:.3e}", flush=True)
-    assert mx <= max_abs and rl <= rel, (name, mx, rl)
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    excess = float((np.abs(got - ref) - (max_abs + BF16_ULP_REL * np.abs(ref))).max(initial=-1.0))
+    print(f"  {name}: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rl:.3e} "
+          f"bar_excess={excess:.3e}", flush=True)
+    assert excess <= 0.0 and rl <= rel, (name, mx, excess, rl)
     return mx, mn, rl
 
 

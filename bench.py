@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 import torch  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBPS = 8000.0
 WORKLOAD = dict(B=2, S=8192, H=16, d=128, causal=False, seed=2000)
 
 
@@ -94,12 +95,98 @@ def sampled_check(q, k, v, o, lse, causal):
     return float(np.abs(o_got - o_ref).max()), float(np.abs(l_got - lse_ref).max())
 
 
+def time_calls(fn, reps, warmup=2):
+    """Average ms of fn() over reps back-to-back calls on the current stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def leg_causal(reps):
+    """fwd and fwd+bwd at B=2, H=16, S=8192, d=128, causal (flops halved)."""
+    from io_aware_exact_amd import fa, inputs
+    B, S, H, d = 2, 8192, 16, 128
+    q, k, v, do = inputs.qkv(B, S, S, H, H, d, 2000, device="cuda", with_dout=True)
+    o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    ms_f = time_calls(lambda: fa.fwd(q, k, v, True, out=o, lse=lse), reps)
+    ms_b = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, True), reps)
+    ff = fwd_flops(B, S, S, H, d, True)
+    return {"workload": "B=2 H=16 Sq=Sk=8192 d=128 causal",
+            "fwd_tflops": round(ff / ms_f / 1e9, 2), "fwd_ms": round(ms_f, 4),
+            "fwd_bwd_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2),
+            "bwd_ms": round(ms_b, 4)}
+
+
+def leg_decode(reps):
+    """Split-KV decode: B=64, Sq=1, Sk=32768, Hq=32, Hkv=8, d=128, causal.
+    HBM-bound: reports K+V bytes / time against 8 TB/s."""
+    from io_aware_exact_amd import fa, inputs
+    B, Sq, Sk, Hq, Hkv, d = 64, 1, 32768, 32, 8, 128
+    q, k, v = inputs.qkv(B, Sq, Sk, Hq, Hkv, d, 3100, device="cuda")
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fwd_workspace_bytes(q, k, v, True), dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda: fa.fwd(q, k, v, True, out=o, lse=lse, workspace=ws), reps)
+    kv_bytes = 2 * B * Sk * Hkv * d * 2
+    io_bytes = kv_bytes + 2 * (B * Sq * Hq * d * 2) + B * Hq * Sq * 4
+    return {"workload": "decode B=64 Sq=1 Sk=32768 Hq=32 Hkv=8 d=128",
+            "ms": round(ms, 4), "gbps": round(io_bytes / ms / 1e6, 1),
+            "frac_of_hbm": round(io_bytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
+            "tflops": round(4.0 * B * Hq * Sq * Sk * d / ms / 1e9, 2)}
+
+
+def leg_varlen(reps):
+    """Packed varlen + GQA forward: 16 sequences, lengths uniform on
+    [128, 32768] (seed 3000), Hq=32, Hkv=8, d=128, causal."""
+    from io_aware_exact_amd import fa, inputs
+    lens = inputs.varlen_lengths(16, 128, 32768, 3000)
+    Hq, Hkv, d = 32, 8, 128
+    q, k, v = inputs.packed_qkv(lens, lens, Hq, Hkv, d, 3001, device="cuda")
+    cu = inputs.cu_seqlens(lens, device="cuda")
+    T = sum(lens)
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    ms = time_calls(lambda: fa.fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), True,
+                                          out=o, lse=lse), reps)
+    pairs = sum(L * (L + 1) // 2 for L in lens)
+    flops_half = sum(2.0 * Hq * d * L * L for L in lens)
+    return {"workload": "varlen 16 seqs U[128,32768] Hq=32 Hkv=8 d=128 causal",
+            "total_tokens": T, "ms": round(ms, 3),
+            "tflops": round(flops_half / ms / 1e9, 2),
+            "tflops_exact_pairs": round(4.0 * Hq * d * pairs / ms / 1e9, 2)}
+
+
+def extra_legs(args):
+    out = {}
+    for name, fn, reps in (("causal", leg_causal, 10), ("decode", leg_decode, 20),
+                           ("varlen", leg_varlen, 5)):
+        if args.only and args.only != name:
+            continue
+        out[name] = fn(reps)
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary workloads (causal, decode, varlen)")
+    ap.add_argument("--only", choices=["decode", "varlen", "causal"],
+                    help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "
                          "for scaling HBM byte counters")
@@ -123,6 +210,9 @@ def main():
         return
     from io_aware_exact_amd import fa, inputs
     fa.lib()
+    if args.only:
+        print(json.dumps(extra_legs(args)), flush=True)
+        return
 
     W = WORKLOAD
     B, S, H, d, causal = W["B"], W["S"], W["H"], W["d"], W["causal"]
@@ -199,6 +289,8 @@ def main():
                      "traffic": traffic_from_profile()},
         "check": {"o_max_abs": err_o, "lse_max_abs": err_lse},
     }
+    if not args.no_extra:
+        line["extra"] = extra_legs(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(q, k, v, do, causal, have_bwd)
     print(json.dumps(line), flush=True)

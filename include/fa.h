@@ -70,7 +70,7 @@ typedef enum {
   FA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
   FA_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
-  FA_ERR_SCALE = 10       /* softmax scale is not a finite positive number */
+  FA_ERR_SCALE = 10       /* softmax scale is not a finite number > 0 */
 } fa_status;
 
 typedef enum { FA_BF16 = 0, FA_FP8_E4M3 = 2 } fa_dtype;
@@ -88,8 +88,19 @@ typedef struct {
  * FP8 only: q_descale [B,Hq,ceil(Sq/128)], k_descale and v_descale
  * [B,Hkv,ceil(Sk/128)], fp32 contiguous: the real value of an element is its
  * e4m3 value times the scale of its (batch, head, 128-token block).
- * workspace: used only by the split-KV decode path (see fa_fwd_workspace_size);
- * pass NULL / 0 when the size query returns 0. */
+ * softmax_scale must be finite and > 0 (1/sqrt(d) is the usual choice).
+ *
+ * Split-KV decode path (KV-cache inference: the repository overview's
+ * flash_attn_with_kvcache entry point, here over a dense cache).  When all
+ * query rows of one kv head fit one 32-wide tile, Sq * (Hq / Hkv) <= 32
+ * (e.g. one new token per sequence), fa_fwd_workspace_size returns a nonzero
+ * size; given a workspace of at least that many bytes (256-byte aligned, not
+ * overlapping any tensor), fa_fwd cuts the keys into chunks that run in
+ * parallel, each producing a partial (O_p, LSE_p), and merges them exactly:
+ * LSE = ln sum_p exp(LSE_p), O = sum_p exp(LSE_p - LSE) O_p.  Without a
+ * workspace the same call runs the tiled kernel (same result up to rounding
+ * order, much slower for these shapes).  The workspace holds no state between
+ * calls. */
 typedef struct {
   fa_dtype dtype;
   int32_t B, Sq, Sk, Hq, Hkv, d;
@@ -148,7 +159,8 @@ int32_t fa_abi_version(void);
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(fa_status status);
 
-/* Workspace bytes fa_fwd needs for these arguments (0 when none). */
+/* Workspace bytes the split-KV decode path of fa_fwd uses for these
+ * arguments; 0 when the decode path does not apply (then pass none). */
 size_t fa_fwd_workspace_size(const fa_fwd_args* args);
 
 /* Workspace bytes fa_bwd needs for these arguments. */

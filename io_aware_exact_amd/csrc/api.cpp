@@ -43,13 +43,58 @@ bool strides_ok(const fa_tensor& t, int64_t mult) {
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// The kernels evaluate exp2(scale * log2(e) * s - m); masked scores are -inf,
+// which needs a strictly positive scale.
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---- split-KV decode plan: taken when all query rows of one kv head fit in
+// the 32 columns of one MFMA tile.
+constexpr int kDecodeMaxRows = 32;
+constexpr int64_t kDecodeTargetWaves = 4096;  // one wave per (batch, kv head, split)
+constexpr int64_t kDecodeMinKeysPerSplit = 256;
+constexpr int64_t kDecodeMaxSplits = 64;
+
+struct DecodePlan {
+  bool eligible;
+  int nsplit, chunk;
+  size_t o_part_bytes, lse_part_bytes;
+};
+
+DecodePlan decode_plan(const fa_fwd_args* a) {
+  DecodePlan pl = {false, 1, 32, 0, 0};
+  if (a->dtype != FA_BF16 || a->B <= 0 || a->Sq <= 0 || a->Sk < 0 || a->Hkv <= 0 || a->Hq <= 0 ||
+      a->Hq % a->Hkv != 0 || (a->d != 64 && a->d != 128))
+    return pl;
+  const int64_t group = a->Hq / a->Hkv;
+  if ((int64_t)a->Sq * group > kDecodeMaxRows) return pl;
+  pl.eligible = true;
+  const int64_t Sk = a->Sk;
+  if (Sk > 0) {
+    const int64_t pairs = (int64_t)a->B * a->Hkv;
+    int64_t ns = (kDecodeTargetWaves + pairs - 1) / pairs;
+    const int64_t by_len = (Sk + kDecodeMinKeysPerSplit - 1) / kDecodeMinKeysPerSplit;
+    if (ns > by_len) ns = by_len;
+    if (ns > kDecodeMaxSplits) ns = kDecodeMaxSplits;
+    if (ns < 1) ns = 1;
+    const int64_t chunk = ((Sk + ns - 1) / ns + 31) / 32 * 32;
+    pl.chunk = (int)chunk;
+    pl.nsplit = (int)((Sk + chunk - 1) / chunk);
+  }
+  const size_t rows = (size_t)a->B * a->Hq * a->Sq * pl.nsplit;
+  pl.o_part_bytes = align256(rows * a->d * 4);
+  pl.lse_part_bytes = align256(rows * 4);
+  return pl;
+}
+
 fa_status check_fwd(const fa_fwd_args* a) {
   if (!a) return FA_ERR_NULL;
   if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
   if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
-  if (!isfinite(a->softmax_scale)) return FA_ERR_SCALE;
+  if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
   if (!a->q.ptr || !a->k.ptr || !a->v.ptr || !a->o.ptr || !a->lse) return FA_ERR_NULL;
   if (!aligned16(a->q.ptr) || !aligned16(a->k.ptr) || !aligned16(a->v.ptr) || !aligned16(a->o.ptr) ||
       ((uintptr_t)a->lse & 3u))
@@ -69,6 +114,12 @@ fa_status check_fwd(const fa_fwd_args* a) {
   if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sl) || overlap(sl, sq) ||
       overlap(sl, sk) || overlap(sl, sv))
     return FA_ERR_ALIAS;
+  if (a->workspace && a->workspace_bytes > 0) {
+    if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
+    const Span sw = {(uintptr_t)a->workspace, (uintptr_t)a->workspace + a->workspace_bytes};
+    if (overlap(sw, sq) || overlap(sw, sk) || overlap(sw, sv) || overlap(sw, so) || overlap(sw, sl))
+      return FA_ERR_ALIAS;
+  }
   return FA_OK;
 }
 
@@ -80,7 +131,7 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
     return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
-  if (!isfinite(a->softmax_scale)) return FA_ERR_SCALE;
+  if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
   if (!a->q || !a->k || !a->v || !a->o || !a->lse || !a->cu_seqlens_q || !a->cu_seqlens_k)
     return FA_ERR_NULL;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
@@ -118,7 +169,7 @@ fa_status check_bwd(const fa_bwd_args* a) {
   if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
-  if (!isfinite(a->softmax_scale)) return FA_ERR_SCALE;
+  if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
   const fa_tensor* ts[8] = {&a->q, &a->k, &a->v, &a->o, &a->dout, &a->dq, &a->dk, &a->dv};
   for (int i = 0; i < 8; ++i)
     if (!ts[i]->ptr) return FA_ERR_NULL;
@@ -176,14 +227,15 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_ALIAS: return "an output overlaps another tensor";
     case FA_ERR_HIP: return "HIP runtime error at launch";
-    case FA_ERR_SCALE: return "softmax scale must be finite";
+    case FA_ERR_SCALE: return "softmax scale must be finite and positive";
   }
   return "unknown status";
 }
 
 size_t fa_fwd_workspace_size(const fa_fwd_args* a) {
-  (void)a;
-  return 0;
+  if (!a) return 0;
+  const DecodePlan pl = decode_plan(a);
+  return pl.eligible ? pl.o_part_bytes + pl.lse_part_bytes : 0;
 }
 
 fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
@@ -207,6 +259,25 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
   p.num_m_tiles = (a->Sq + kBM - 1) / kBM;
   p.scale = a->softmax_scale;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  const DecodePlan pl = decode_plan(a);
+  if (pl.eligible && a->workspace && a->workspace_bytes >= pl.o_part_bytes + pl.lse_part_bytes) {
+    DecodeParams d = {};
+    d.q = p.q; d.k = p.k; d.v = p.v; d.o = p.o; d.lse = p.lse;
+    d.o_part = (float*)a->workspace;
+    d.lse_part = (float*)((char*)a->workspace + pl.o_part_bytes);
+    d.q_sb = p.q_sb; d.q_ss = p.q_ss; d.q_sh = p.q_sh;
+    d.k_sb = p.k_sb; d.k_ss = p.k_ss; d.k_sh = p.k_sh;
+    d.v_sb = p.v_sb; d.v_ss = p.v_ss; d.v_sh = p.v_sh;
+    d.o_sb = p.o_sb; d.o_ss = p.o_ss; d.o_sh = p.o_sh;
+    d.lse_sb = p.lse_sb; d.lse_sh = p.lse_sh;
+    d.B = p.B; d.Sq = p.Sq; d.Sk = p.Sk; d.Hq = p.Hq; d.Hkv = p.Hkv; d.group = p.group;
+    d.causal = a->causal != 0;
+    d.nsplit = pl.nsplit;
+    d.chunk = pl.chunk;
+    d.scale = p.scale;
+    d.scale_log2 = p.scale_log2;
+    return hip_status(launch_decode_bf16(d, a->d, stream));
+  }
   return hip_status(launch_fwd_bf16(p, a->d, a->causal != 0, false, stream));
 }
 

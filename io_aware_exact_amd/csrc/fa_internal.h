@@ -51,6 +51,28 @@ struct BwdParams {
   float scale_log2;
 };
 
+// Split-KV decode: partial results per (row, split) in the caller's workspace.
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* o_part;              // [B,Hq,Sq,nsplit,d] fp32, each normalised by its own row sum
+  float* lse_part;            // [B,Hq,Sq,nsplit] fp32
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh;
+  int B, Sq, Sk, Hq, Hkv, group;
+  int causal;
+  int nsplit, chunk;          // keys [s*chunk, (s+1)*chunk) form split s
+  float scale;
+  float scale_log2;
+};
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen,
                            hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);

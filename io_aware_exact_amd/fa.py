@@ -125,20 +125,48 @@ def _scale(d, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """Dense forward.  q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16 on the GPU.
-    Returns (o [B,Sq,Hq,d] bf16, lse [B,Hq,Sq] fp32)."""
+def fwd_args(q, k, v, out, lse, causal, scale, workspace=None):
     B, Sq, Hq, d = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return FwdArgs(dt, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
+                   _t4(q), _t4(k), _t4(v), _t4(out), lse.data_ptr(), None, None, None,
+                   ws_ptr, ws_bytes)
+
+
+def fwd_workspace_bytes(q, k, v, causal=False, scale=None):
+    """Bytes of workspace the split-KV decode path wants (0: not applicable)."""
+    B, Sq, Hq, d = q.shape
+    dummy = torch.empty(0)
+    a = FwdArgs(FA_BF16, B, Sq, k.shape[1], Hq, k.shape[2], d, int(bool(causal)),
+                _scale(d, scale), _t4(q), _t4(k), _t4(v), _t4(q), dummy.data_ptr(),
+                None, None, None, None, 0)
+    return int(lib().fa_fwd_workspace_size(ctypes.byref(a)))
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None):
+    """Dense forward.  q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16 on the GPU.
+    Returns (o [B,Sq,Hq,d] bf16, lse [B,Hq,Sq] fp32).  With a `workspace`
+    (uint8 device tensor of fwd_workspace_bytes) decode-shaped calls take the
+    split-KV path."""
+    B, Sq, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
-    a = FwdArgs(dt, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
-                _t4(q), _t4(k), _t4(v), _t4(out), lse.data_ptr(), None, None, None, None, 0)
+    a = fwd_args(q, k, v, out, lse, causal, scale, workspace)
     _check("fa_fwd", lib().fa_fwd(ctypes.byref(a), _stream()))
     return out, lse
+
+
+def fwd_decode(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Forward that allocates the split-KV workspace when the decode path
+    applies (Sq * Hq / Hkv <= 32), else the plain dense forward."""
+    n = fwd_workspace_bytes(q, k, v, causal, scale)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+    return fwd(q, k, v, causal, scale, out, lse, ws)
 
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
@@ -208,6 +236,12 @@ class _Attention(torch.autograd.Function):
 def attention(q, k, v, causal=False, scale=None):
     """Exact attention with autograd: q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16."""
     return _Attention.apply(q, k, v, causal, scale)
+
+
+def attention_decode(q, k, v, causal=False, scale=None):
+    """Forward for KV-cache decoding (few query rows against a long cache);
+    returns o [B,Sq,Hq,d]."""
+    return fwd_decode(q, k, v, causal, scale)[0]
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,

@@ -29,6 +29,7 @@ import torch  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2
 WORKLOAD = dict(B=2, S=8192, H=16, d=128, causal=False, seed=2000)
 
 
@@ -166,10 +167,29 @@ def leg_varlen(reps):
             "tflops_exact_pairs": round(4.0 * Hq * d * pairs / ms / 1e9, 2)}
 
 
+def leg_fp8(reps):
+    """FP8 (E4M3, per-block scales) forward: B=1, H=16, S=16384, d=128,
+    non-causal, inputs N(0,1) + Bernoulli(0.001) N(0,100) (seed 4000).
+    Quantisation is input preparation and is not timed."""
+    from io_aware_exact_amd import fa, inputs
+    B, S, H, d = 1, 16384, 16, 128
+    qkv = [fa.quantize_fp8(inputs.outlier_normal((B, S, H, d), 4000 + i, device="cuda"))
+           for i in range(3)]
+    codes = [c for c, _ in qkv]
+    scales = [s for _, s in qkv]
+    o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    ms = time_calls(lambda: fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse), reps)
+    ff = fwd_flops(B, S, S, H, d, False)
+    return {"workload": "fp8 e4m3 fwd B=1 H=16 S=16384 d=128 non-causal, per-block scales",
+            "ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2),
+            "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
+
+
 def extra_legs(args):
     out = {}
     for name, fn, reps in (("causal", leg_causal, 10), ("decode", leg_decode, 20),
-                           ("varlen", leg_varlen, 5)):
+                           ("varlen", leg_varlen, 5), ("fp8", leg_fp8, 10)):
         if args.only and args.only != name:
             continue
         out[name] = fn(reps)
@@ -185,7 +205,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
-    ap.add_argument("--only", choices=["decode", "varlen", "causal"],
+    ap.add_argument("--only", choices=["decode", "varlen", "causal", "fp8"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

@@ -166,7 +166,11 @@ size_t fa_fwd_workspace_size(const fa_fwd_args* args);
 /* Workspace bytes fa_bwd needs for these arguments. */
 size_t fa_bwd_workspace_size(const fa_bwd_args* args);
 
-/* Dense forward; see fa_fwd_args. */
+/* Dense forward; see fa_fwd_args.  dtype FA_BF16, or FA_FP8_E4M3 (FP8
+ * forward, "FlashAttention-3 ..." third contribution: both products run on
+ * FP8 MFMA with fp32 accumulation; q/k/v are OCP E4M3 codes with strides in
+ * bytes, the three descale arrays are required, the probabilities are
+ * rounded to E4M3 after a 2^8 prescale; no decode path and no backward). */
 fa_status fa_fwd(const fa_fwd_args* args, hipStream_t stream);
 
 /* Packed variable-length forward; see fa_fwd_varlen_args. */
@@ -175,7 +179,11 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args* args, hipStream_t stream);
 /* Dense backward; see fa_bwd_args. */
 fa_status fa_bwd(const fa_bwd_args* args, hipStream_t stream);
 
-/* FP8 quantiser (input preparation for the FP8 forward).
+/* FP8 quantiser (input preparation for the FP8 forward; "FlashAttention-3:
+ * Fast and Accurate Attention with Asynchrony and Low-precision", third
+ * contribution and the block versus per-tensor error comparison).
+ * d must be a multiple of 16 and at most 256; x 4-byte aligned, codes
+ * 16-byte aligned; x, codes and scales must not overlap.
  * x [B,S,H,d] fp32 with element strides (d contiguous) -> codes [B,S,H,d]
  * e4m3 contiguous and scales [B,H,ceil(S/128)] fp32 contiguous.
  * per_tensor = 0: one scale per (batch, head, 128-token block),

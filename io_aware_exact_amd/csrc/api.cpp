@@ -90,27 +90,35 @@ DecodePlan decode_plan(const fa_fwd_args* a) {
 
 fa_status check_fwd(const fa_fwd_args* a) {
   if (!a) return FA_ERR_NULL;
-  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->dtype != FA_BF16 && a->dtype != FA_FP8_E4M3) return FA_ERR_DTYPE;
+  const bool fp8 = a->dtype == FA_FP8_E4M3;
+  const int64_t es = fp8 ? 1 : 2;            // bytes per q/k/v element
   if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
   if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
   if (!a->q.ptr || !a->k.ptr || !a->v.ptr || !a->o.ptr || !a->lse) return FA_ERR_NULL;
+  if (fp8 && (!a->q_descale || !a->k_descale || !a->v_descale)) return FA_ERR_NULL;
   if (!aligned16(a->q.ptr) || !aligned16(a->k.ptr) || !aligned16(a->v.ptr) || !aligned16(a->o.ptr) ||
       ((uintptr_t)a->lse & 3u))
     return FA_ERR_ALIGN;
-  if (!strides_ok(a->q, 8) || !strides_ok(a->k, 8) || !strides_ok(a->v, 8) || !strides_ok(a->o, 8))
+  if (fp8 && (((uintptr_t)a->q_descale & 3u) || ((uintptr_t)a->k_descale & 3u) ||
+              ((uintptr_t)a->v_descale & 3u)))
+    return FA_ERR_ALIGN;
+  const int64_t smult = 16 / es;             // 16-byte rows
+  if (!strides_ok(a->q, smult) || !strides_ok(a->k, smult) || !strides_ok(a->v, smult) ||
+      !strides_ok(a->o, 8))
     return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
   if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (!fits32(a->Sq, a->q.stride_s, 2) || !fits32(a->Sq, a->o.stride_s, 2) ||
-      !fits32(a->Sk, a->k.stride_s, 2) || !fits32(a->Sk, a->v.stride_s, 2))
+  if (!fits32(a->Sq, a->q.stride_s, es) || !fits32(a->Sq, a->o.stride_s, 2) ||
+      !fits32(a->Sk, a->k.stride_s, es) || !fits32(a->Sk, a->v.stride_s, es))
     return FA_ERR_SHAPE;
   const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
   const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
-  const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2);
-  const Span sk = span4(a->k.ptr, a->B, a->Sk, a->Hkv, a->d, a->k.stride_b, a->k.stride_s, a->k.stride_h, 2);
-  const Span sv = span4(a->v.ptr, a->B, a->Sk, a->Hkv, a->d, a->v.stride_b, a->v.stride_s, a->v.stride_h, 2);
+  const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, es);
+  const Span sk = span4(a->k.ptr, a->B, a->Sk, a->Hkv, a->d, a->k.stride_b, a->k.stride_s, a->k.stride_h, es);
+  const Span sv = span4(a->v.ptr, a->B, a->Sk, a->Hkv, a->d, a->v.stride_b, a->v.stride_s, a->v.stride_h, es);
   if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sl) || overlap(sl, sq) ||
       overlap(sl, sk) || overlap(sl, sv))
     return FA_ERR_ALIAS;
@@ -259,6 +267,12 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
   p.num_m_tiles = (a->Sq + kBM - 1) / kBM;
   p.scale = a->softmax_scale;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  if (a->dtype == FA_FP8_E4M3) {
+    p.q_descale = a->q_descale;
+    p.k_descale = a->k_descale;
+    p.v_descale = a->v_descale;
+    return hip_status(launch_fwd_fp8(p, a->d, a->causal != 0, stream));
+  }
   const DecodePlan pl = decode_plan(a);
   if (pl.eligible && a->workspace && a->workspace_bytes >= pl.o_part_bytes + pl.lse_part_bytes) {
     DecodeParams d = {};
@@ -355,9 +369,18 @@ fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
 fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int32_t B, int32_t S,
                           int32_t H, int32_t d, int32_t per_tensor, void* codes, float* scales,
                           hipStream_t stream) {
-  (void)x; (void)sb; (void)ss; (void)sh; (void)B; (void)S; (void)H; (void)d; (void)per_tensor;
-  (void)codes; (void)scales; (void)stream;
-  return FA_ERR_DTYPE;
+  if (!x || !codes || !scales) return FA_ERR_NULL;
+  if (B < 0 || S < 0 || H < 1) return FA_ERR_SHAPE;
+  if (d < 16 || d > 256 || d % 16 != 0) return FA_ERR_HEADDIM;
+  if (sb < 0 || ss < 0 || sh < 0) return FA_ERR_SHAPE;
+  if (((uintptr_t)x & 3u) || ((uintptr_t)codes & 15u) || ((uintptr_t)scales & 3u)) return FA_ERR_ALIGN;
+  if (B == 0 || S == 0) return FA_OK;
+  const int64_t nb = ((int64_t)S + 127) / 128;
+  const Span sx = span4(x, B, S, H, d, sb, ss, sh, 4);
+  const Span sc = {(uintptr_t)codes, (uintptr_t)codes + (uintptr_t)((int64_t)B * S * H * d)};
+  const Span ss_ = {(uintptr_t)scales, (uintptr_t)scales + (uintptr_t)((int64_t)B * H * nb * 4)};
+  if (overlap(sx, sc) || overlap(sx, ss_) || overlap(sc, ss_)) return FA_ERR_ALIAS;
+  return hip_status(launch_quantize_fp8(x, sb, ss, sh, B, S, H, d, per_tensor != 0, codes, scales, stream));
 }
 
 }  // extern "C"

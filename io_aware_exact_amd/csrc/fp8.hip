@@ -1,0 +1,403 @@
+// FP8 (OCP E4M3) forward of IO-aware exact attention for gfx950, and the
+// block quantiser that prepares its inputs.
+//
+// Method ("FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+// Low-precision", summary, third contribution and results): the forward's two
+// products run on FP8 matrix units for roughly twice the 16-bit throughput,
+// and block-wise scaling of the FP8 inputs is what keeps the error well below
+// per-tensor quantisation.  The tiling and the online softmax are those of the
+// bf16 forward ("Flash Attention and Efficient Transformer Mechanisms", block
+// computation; Dao-AILab repository overview, online softmax with rescaling).
+//
+// Scales.  Q, K and V each carry one fp32 scale per (batch, head, 128-token
+// block): the real value of a code is e4m3(code) * scale.  With tiles of 128
+// query rows and 64 keys, a workgroup has one Q scale sq and each key tile J
+// one K scale sk_J and one V scale sv_J, so
+//   * the scores are s = (scale * sq * sk_J) * (q8 . k8): the whole factor,
+//     times log2(e), is the per-tile constant of the exp2 FMA;
+//   * p = exp2(s - m) is multiplied by 2^8 before rounding to e4m3, so that
+//     probabilities down to 2^-14 keep 3 mantissa bits (448 bounds 2^8 * 1);
+//   * V's scale is folded into the running rescale: the accumulator holds
+//     O_hat = O_acc / sv_J, updated as O_hat <- O_hat * alpha * sv_{J-1} / sv_J
+//     + P8 V8_J, and the epilogue writes O = sv_last * O_hat / (2^8 * l).
+//
+// gfx950 mapping.  As in the bf16 forward (S^T = K Q^T with query rows in the
+// MFMA columns, 4 waves x 32 rows, 2-stage LDS ring of 64-key tiles), with the
+// 32x32x64 f8f6f4 MFMA (format E4M3, unit block scales).  Each lane's 32
+// operand bytes are one k-slice of 32; A and B use the same byte order.
+//   * S^T: lane (row m, half hh) of K and of Q^T holds d = 64 c + 32 hh + j.
+//   * O^T += V^T P^T over 64 keys: byte 8 r + e of a lane in half hh is key
+//     16 r + 8 hh + e.  With the permuted K row order these are exactly the
+//     accumulator registers 8 (r % 2) + e of score block r / 2, and V^T is
+//     read from the row-major V tile with the 8-bit LDS transposing read
+//     (ds_read_b64_tr_b8: within 16 lanes, lane i gets byte i % 8 of the
+//     rows addressed by lanes i / 8 + 2 e, e = 0..7).
+#include "device_common.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int BM = 128;
+constexpr int BN = 64;
+constexpr int NTHREADS = 256;
+constexpr int QBLK = 128;          // tokens per quantisation block
+constexpr float P_PRESCALE = 256.f;
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2*)(p));
+}
+
+// Two fp32 values -> two e4m3 codes in the low 16 bits (hardware rounding to
+// nearest even; inputs here lie in [0, 256]).
+__device__ __forceinline__ int pack2_fp8(float a, float b) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+}
+
+template <int D>
+struct Fp8Tile {
+  static constexpr int STR = D + 16;      // LDS row stride in bytes (K and V)
+  static constexpr int NC = D / 64;       // 64-wide d chunks of S^T
+  static constexpr int ND = D / 32;       // 32-row d blocks of O^T
+  static constexpr int CH = D / 16;       // 16-byte chunks per row
+  static constexpr int RPP = NTHREADS / CH;
+  static constexpr int NP = BN / RPP;
+  static constexpr int STAGE = 2 * BN * STR;
+};
+
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = w & 7, s = w >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
+  using T = Fp8Tile<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int mt = L % p.num_m_tiles;
+  const int rest = L / p.num_m_tiles;
+  const int h = rest % p.Hq;
+  const int b = rest / p.Hq;
+  if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  const int g = h / p.group;
+  const int Lq = p.Sq, Lk = p.Sk;
+  const int q0 = mt * BM;
+  const int diag = Lk - Lq;
+
+  const uint8_t* qb = (const uint8_t*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+  const uint8_t* kb = (const uint8_t*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const uint8_t* vb = (const uint8_t*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  __bf16* ob = (__bf16*)p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
+  float* lseb = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
+  const int nqb = (Lq + QBLK - 1) / QBLK, nkb = (Lk + QBLK - 1) / QBLK;
+  const float sq = p.q_descale[((int64_t)b * p.Hq + h) * nqb + q0 / QBLK];
+  const float* ksc = p.k_descale + ((int64_t)b * p.Hkv + g) * nkb;
+  const float* vsc = p.v_descale + ((int64_t)b * p.Hkv + g) * nkb;
+
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, q0 + BM + diag);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- Q^T fragments (B operand): 32 bytes of row qrow per 64-wide d chunk
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss));
+  const int qrow = q0 + wave * 32 + l32;
+  i32x8 qf[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+    const uint32_t off = (uint32_t)(qrow * p.q_ss + 64 * c + 32 * hh);
+    const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
+    qf[c] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  // transposing-read source coordinates of this lane (see file comment)
+  const int G = lane >> 4, u = lane & 15;
+  const int tr_row = 8 * (G >> 1) + (u >> 1);
+  const int tr_col = 16 * (G & 1) + 8 * (u & 1);
+
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss));
+  const int lrow = tid / T::CH;
+  const int lcol = (tid % T::CH) * 16;
+  u32x4 kreg[T::NP], vreg[T::NP];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int w = 0; w < T::NP; ++w) {
+      const uint32_t r = (uint32_t)(j0 + lrow + w * T::RPP);
+      kreg[w] = buf_load16(rk, r * (uint32_t)p.k_ss + lcol);
+      vreg[w] = buf_load16(rv, r * (uint32_t)p.v_ss + lcol);
+    }
+  };
+  auto lstore = [&](int st) {
+    uint8_t* Ks = smem + st * T::STAGE;
+    uint8_t* Vs = Ks + BN * T::STR;
+#pragma unroll
+    for (int w = 0; w < T::NP; ++w) {
+      *(u32x4*)(Ks + (lrow + w * T::RPP) * T::STR + lcol) = kreg[w];
+      *(u32x4*)(Vs + (lrow + w * T::RPP) * T::STR + lcol) = vreg[w];
+    }
+  };
+
+  f32x16 oacc[T::ND];
+#pragma unroll
+  for (int i = 0; i < T::ND; ++i) oacc[i] = (f32x16){};
+  float m_run = -INFINITY;   // running max in log2 units
+  float l_run = 0.f;
+  float sv_prev = 1.f;
+  const float cq = p.scale_log2 * sq;
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  const int wave_last_row = q0 + wave * 32 + 31;
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    const int j0 = t * BN;
+    const bool more = t + 1 < ntiles;
+    if (more) gload(j0 + BN);
+    const float sv = vsc[j0 / QBLK];
+    const bool wave_active = !CAUSAL || j0 <= wave_last_row + diag;
+    if (wave_active) {
+      const uint8_t* Ks = smem + st * T::STAGE;
+      const uint8_t* Vs = Ks + BN * T::STR;
+      const float c2 = cq * ksc[j0 / QBLK];
+      f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const uint8_t* kp = Ks + (32 * kb2 + kperm) * T::STR + 64 * c + 32 * hh;
+          const u32x4 lo = *(const u32x4*)kp, hi = *(const u32x4*)(kp + 16);
+          const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          sacc[kb2] = mfma_fp8(kf, qf[c], sacc[kb2]);
+        }
+      const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > q0 + wave * 32 + diag);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(Lk - 1, qrow + diag) : Lk - 1;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kj = j0 + 32 * kb2 + 16 * (i >> 3) + 8 * hh + (i & 7);
+            if (kj > lim) sacc[kb2][i] = -INFINITY;
+          }
+      }
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
+      mx = fmaxf(mx, wave_xor32(mx)) * c2;
+      const float m_new = fmaxf(m_run, mx);
+      const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_base);
+      float rs = 0.f;
+      i32x8 pf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = fast_exp2(__builtin_fmaf(sacc[r >> 1][8 * (r & 1) + e], c2, -m_base));
+          rs += pv[e];
+        }
+        const int w0 = pack2_fp8(pv[0] * P_PRESCALE, pv[1] * P_PRESCALE);
+        const int w1 = pack2_fp8(pv[2] * P_PRESCALE, pv[3] * P_PRESCALE);
+        const int w2 = pack2_fp8(pv[4] * P_PRESCALE, pv[5] * P_PRESCALE);
+        const int w3 = pack2_fp8(pv[6] * P_PRESCALE, pv[7] * P_PRESCALE);
+        pf[2 * r] = (w0 & 0xffff) | (w1 << 16);
+        pf[2 * r + 1] = (w2 & 0xffff) | (w3 << 16);
+      }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      const float resc = alpha * (sv_prev / sv);
+#pragma unroll
+      for (int i = 0; i < T::ND; ++i) oacc[i] *= resc;
+      // O_hat^T += V8^T P8^T (64 keys per MFMA)
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) {
+        i32x8 vf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const i32x2 x = lds_read_tr8(Vs + (16 * r + tr_row) * T::STR + 32 * db + tr_col);
+          vf[2 * r] = x[0];
+          vf[2 * r + 1] = x[1];
+        }
+        oacc[db] = mfma_fp8(vf, pf, oacc[db]);
+      }
+      sv_prev = sv;   // O_hat is now relative to this tile's V scale
+    }
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = sv_last * O_hat / (2^8 l), LSE = ln 2 * m + ln l
+  const float l_tot = l_run + wave_xor32(l_run);
+  if (qrow < Lq) {
+    const float inv = l_tot > 0.f ? sv_prev / (P_PRESCALE * l_tot) : 0.f;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)((int64_t)Lq * p.o_ss * 2));
+    const uint32_t orow = (uint32_t)(qrow * p.o_ss) * 2;
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(oacc[db][4 * gi + r] * inv);
+        buf_store8(__builtin_bit_cast(u32x2, w), ro, orow + (uint32_t)(32 * db + 8 * gi + 4 * hh) * 2);
+      }
+    if (hh == 0) lseb[qrow] = l_tot > 0.f ? m_run * 0.6931471805599453f + logf(l_tot) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantiser: x fp32 [B,S,H,d] (strided) -> e4m3 codes [B,S,H,d] contiguous and
+// fp32 scales [B,H,ceil(S/128)].
+
+// fp32 -> OCP E4M3 code: nearest value, ties to the even code, saturating to
+// +-448; NaN -> 0x7F.  Written from the format definition (1 sign bit,
+// 4 exponent bits with bias 7, 3 mantissa bits, subnormal step 2^-9).
+__device__ __forceinline__ uint32_t encode_e4m3(float y) {
+  const uint32_t uy = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (uy >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);   // 0..8, exact product
+  const uint32_t ua = __builtin_bit_cast(uint32_t, a);
+  const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);             // round 23 -> 3 mantissa bits
+  return sign | ((r >> 20) - (120u << 3));
+}
+
+struct QuantParams {
+  const float* x;
+  int64_t sb, ss, sh;
+  uint8_t* codes;
+  float* scales;
+  int B, S, H, d, nb;
+};
+
+// one workgroup per (b, h, block): amax over 128 tokens x d
+__global__ __launch_bounds__(256) void quant_amax_kernel(QuantParams p, int per_tensor) {
+  const int blk = blockIdx.x % p.nb;
+  const int bh = blockIdx.x / p.nb;
+  const int h = bh % p.H, b = bh / p.H;
+  const int s0 = blk * QBLK, s1 = min(p.S, s0 + QBLK);
+  float m = 0.f;
+  const int n = (s1 - s0) * p.d;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int s = s0 + i / p.d, c = i % p.d;
+    m = fmaxf(m, fabsf(p.x[(int64_t)b * p.sb + (int64_t)s * p.ss + (int64_t)h * p.sh + c]));
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float amax = red[0];
+    p.scales[blockIdx.x] = per_tensor ? amax : (amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f);
+  }
+}
+
+// per-tensor: one workgroup turns the block maxima into the tensor scale
+__global__ __launch_bounds__(256) void quant_tensor_scale_kernel(QuantParams p) {
+  const int n = p.B * p.H * p.nb;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, p.scales[i]);
+  __shared__ float red[256];
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float amax = red[0];
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  for (int i = threadIdx.x; i < n; i += 256) p.scales[i] = s;
+}
+
+// one thread per 16 consecutive elements of a (b, s, h) row
+__global__ __launch_bounds__(256) void quant_encode_kernel(QuantParams p) {
+  const int per_row = p.d / 16;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.S * p.H * per_row;
+  if (idx >= total) return;
+  const int c16 = (int)(idx % per_row);
+  int64_t r = idx / per_row;
+  const int h = (int)(r % p.H);
+  r /= p.H;
+  const int s = (int)(r % p.S);
+  const int b = (int)(r / p.S);
+  const float sc = p.scales[((int64_t)b * p.H + h) * p.nb + s / QBLK];
+  const float* xr = p.x + (int64_t)b * p.sb + (int64_t)s * p.ss + (int64_t)h * p.sh + 16 * c16;
+  u32x4 out;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) word |= encode_e4m3(__fdiv_rn(xr[4 * w + e], sc)) << (8 * e);
+    out[w] = word;
+  }
+  *(u32x4*)(p.codes + (((int64_t)b * p.S + s) * p.H + h) * p.d + 16 * c16) = out;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  const long nblk = (long)p.num_m_tiles * p.Hq * p.B;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  return causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+}
+
+hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int B, int S,
+                               int H, int d, int per_tensor, void* codes, float* scales,
+                               hipStream_t stream) {
+  QuantParams p = {x, sb, ss, sh, (uint8_t*)codes, scales, B, S, H, d, (S + QBLK - 1) / QBLK};
+  const long nblk = (long)B * H * p.nb;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_amax_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, p, per_tensor);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (per_tensor) {
+    hipLaunchKernelGGL(quant_tensor_scale_kernel, dim3(1), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long n16 = (long)B * S * H * (d / 16);
+  const long grid = (n16 + 255) / 256;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}

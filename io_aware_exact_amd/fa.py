@@ -238,6 +238,47 @@ def attention(q, k, v, causal=False, scale=None):
     return _Attention.apply(q, k, v, causal, scale)
 
 
+def quantize_fp8(x, per_tensor=False):
+    """x [B,S,H,d] fp32 on the GPU (d contiguous) -> (codes uint8 [B,S,H,d]
+    OCP E4M3, scales fp32 [B,H,ceil(S/128)]).  Per-block: one scale per
+    (batch, head, 128 tokens); per-tensor: one scale written to every entry."""
+    assert x.dtype == torch.float32 and x.dim() == 4 and x.stride(3) == 1
+    B, S, H, d = x.shape
+    codes = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, (S + 127) // 128), dtype=torch.float32, device=x.device)
+    _check("fa_quantize_fp8", lib().fa_quantize_fp8(
+        x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, S, H, d, int(bool(per_tensor)),
+        codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=None,
+            out=None, lse=None):
+    """FP8 forward: q8 [B,Sq,Hq,d], k8/v8 [B,Sk,Hkv,d] E4M3 codes (uint8 or
+    float8_e4m3fn) with fp32 scales [B,H,ceil(S/128)].  Returns (o bf16, lse)."""
+    B, Sq, Hq, d = q8.shape
+    Sk, Hkv = k8.shape[1], k8.shape[2]
+    for t in (q8, k8, v8):
+        assert t.element_size() == 1
+    for t in (q_descale, k_descale, v_descale):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    a = FwdArgs(FA_FP8_E4M3, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
+                _t4(q8), _t4(k8), _t4(v8), _t4(out), lse.data_ptr(), q_descale.data_ptr(),
+                k_descale.data_ptr(), v_descale.data_ptr(), None, 0)
+    _check("fa_fwd", lib().fa_fwd(ctypes.byref(a), _stream()))
+    return out, lse
+
+
+def attention_fp8(q8, k8, v8, descales, causal=False, scale=None):
+    """FP8 forward (no backward); descales = (q_descale, k_descale, v_descale).
+    Returns o [B,Sq,Hq,d] bf16."""
+    return fwd_fp8(q8, k8, v8, *descales, causal=causal, scale=scale)[0]
+
+
 def attention_decode(q, k, v, causal=False, scale=None):
     """Forward for KV-cache decoding (few query rows against a long cache);
     returns o [B,Sq,Hq,d]."""

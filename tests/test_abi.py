@@ -54,6 +54,8 @@ def fwd_args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=3, Hkv=2), 5), (dict(Sq=-1), 2),
     (dict(dtype=7), 4), (dict(softmax_scale=float("nan")), 10),
+    (dict(softmax_scale=0.0), 10), (dict(softmax_scale=-0.5), 10),
+    (dict(dtype=2), 1),   # FP8 without descale arrays
     (dict(q=fa.FaTensor(0, 2048, 128, 64)), 1), (dict(lse=0), 1),
     (dict(q=fa.FaTensor(FAKE + 2, 2048, 128, 64)), 6),
     (dict(q=fa.FaTensor(FAKE, 2048, 130, 64)), 6),
@@ -73,3 +75,32 @@ def test_fwd_null_args():
 def test_fwd_empty_is_noop():
     a = fwd_args(Sq=0)
     assert fa.lib().fa_fwd(ctypes.byref(a), None) == 0
+
+
+def test_quantize_rejects():
+    L = fa.lib()
+    ok = dict(x=FAKE, sb=2048, ss=128, sh=64, B=1, S=16, H=2, d=64, pt=0, c=FAKE + (1 << 24),
+              s=FAKE + (2 << 24))
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.fa_quantize_fp8(a["x"], a["sb"], a["ss"], a["sh"], a["B"], a["S"], a["H"],
+                                 a["d"], a["pt"], a["c"], a["s"], None)
+    assert call(x=0) == 1
+    assert call(d=24) == 3 and call(d=512) == 3
+    assert call(H=0) == 2
+    assert call(c=FAKE + 8) == 6
+    assert call(c=FAKE + 64) == 8          # codes overlap the input
+    assert call(S=0) == 0                  # empty: nothing to do
+
+
+def test_workspace_size_queries():
+    L = fa.lib()
+    # decode-shaped: 1 query row x 4 heads per kv head -> split-KV workspace
+    a = fwd_args(Sq=1, Sk=4096, Hq=8, Hkv=2)
+    assert L.fa_fwd_workspace_size(ctypes.byref(a)) > 0
+    # prefill-shaped: no workspace
+    a = fwd_args(Sq=512, Sk=512)
+    assert L.fa_fwd_workspace_size(ctypes.byref(a)) == 0
+    assert L.fa_fwd_workspace_size(None) == 0

@@ -186,10 +186,30 @@ def leg_fp8(reps):
             "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
 
 
+def leg_sweep(reps):
+    """bf16 forward sweep at B*S = 16384 tokens, H = 16: TFLOP/s per
+    (d, causal) and S (flops halved when causal)."""
+    from io_aware_exact_amd import fa, inputs
+    out = {}
+    for d in (64, 128):
+        for causal in (False, True):
+            row = {}
+            for S in (512, 1024, 2048, 4096, 8192, 16384):
+                B, H = 16384 // S, 16
+                q, k, v = inputs.qkv(B, S, S, H, H, d, 1000, device="cuda")
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+                ms = time_calls(lambda: fa.fwd(q, k, v, causal, out=o, lse=lse), reps)
+                row[str(S)] = round(fwd_flops(B, S, S, H, d, causal) / ms / 1e9, 1)
+            out[f"d{d}_{'causal' if causal else 'noncausal'}"] = row
+    return out
+
+
 def extra_legs(args):
     out = {}
     for name, fn, reps in (("causal", leg_causal, 10), ("decode", leg_decode, 20),
-                           ("varlen", leg_varlen, 5), ("fp8", leg_fp8, 10)):
+                           ("varlen", leg_varlen, 5), ("fp8", leg_fp8, 10),
+                           ("sweep", leg_sweep, 5)):
         if args.only and args.only != name:
             continue
         out[name] = fn(reps)
@@ -205,7 +225,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
-    ap.add_argument("--only", choices=["decode", "varlen", "causal", "fp8"],
+    ap.add_argument("--only", choices=["decode", "varlen", "causal", "fp8", "sweep"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

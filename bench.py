@@ -205,8 +205,29 @@ def leg_sweep(reps):
     return out
 
 
+def leg_main(reps, with_bwd):
+    """The main workload alone (B=2, H=16, S=8192, d=128, non-causal): fwd, or
+    fwd then bwd, reps times -- for profiling."""
+    from io_aware_exact_amd import fa, inputs
+    W = WORKLOAD
+    B, S, H, d, causal = W["B"], W["S"], W["H"], W["d"], W["causal"]
+    q, k, v, do = inputs.qkv(B, S, S, H, H, d, W["seed"], device="cuda", with_dout=True)
+    o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fwd(q, k, v, causal, out=o, lse=lse)
+        if with_bwd:
+            fa.bwd(q, k, v, o, do, lse, causal)
+    ms = time_calls(step, reps)
+    ff = fwd_flops(B, S, S, H, d, causal) * (3.5 if with_bwd else 1.0)
+    return {"ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2)}
+
+
 def extra_legs(args):
     out = {}
+    if args.only in ("fwd", "fwdbwd"):
+        return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
     for name, fn, reps in (("causal", leg_causal, 10), ("decode", leg_decode, 20),
                            ("varlen", leg_varlen, 5), ("fp8", leg_fp8, 10),
                            ("sweep", leg_sweep, 5)):
@@ -225,7 +246,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
-    ap.add_argument("--only", choices=["decode", "varlen", "causal", "fp8", "sweep"],
+    ap.add_argument("--only", choices=["decode", "varlen", "causal", "fp8", "sweep", "fwd",
+                                       "fwdbwd"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

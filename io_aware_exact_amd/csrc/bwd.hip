@@ -91,13 +91,12 @@ template <int D>
 struct DkdvTile {
   static constexpr int BKV = 128;             // keys per workgroup (32 per wave)
   static constexpr int BQ = 64;               // query rows per streamed tile
-  static constexpr int STR = D + 8;           // LDS row stride (elements)
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
   static constexpr int CH = D / 8;
   static constexpr int RPP = NTHREADS / CH;
   static constexpr int NP = BQ / RPP;
-  static constexpr int TILE = BQ * STR;       // elements of one Q or dO tile
+  static constexpr int TILE = BQ * D;         // elements of one Q or dO tile (swizzled rows)
   static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
 };
 
@@ -187,8 +186,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     float* stats = (float*)(Os + T::TILE);
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) {
-      *(u32x4*)(Qs + (lrow + u * T::RPP) * T::STR + lcol) = qreg[u];
-      *(u32x4*)(Os + (lrow + u * T::RPP) * T::STR + lcol) = oreg[u];
+      *(u32x4*)(Qs + swz<D>(lrow + u * T::RPP, lcol)) = qreg[u];
+      *(u32x4*)(Os + swz<D>(lrow + u * T::RPP, lcol)) = oreg[u];
     }
     if (tid < 2 * T::BQ) stats[tid] = sval;
   };
@@ -234,7 +233,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
       for (int c = 0; c < T::NC; ++c) {
-        const int off = (32 * qb + prow) * T::STR + 16 * c + 8 * hh;
+        const int off = swz<D>(32 * qb + prow, 16 * c + 8 * hh);
         s = mfma32(*(const bf16x8*)(Qs + off), kf[c], s);
         dp = mfma32(*(const bf16x8*)(Os + off), vf[c], dp);
       }
@@ -264,10 +263,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int dbk = 0; dbk < T::ND; ++dbk) {
-          const int toff = (32 * qb + 16 * kc + tr_row) * T::STR + 32 * dbk + tr_col;
-          const bf16x8 oa = cat_bf16(lds_read_tr16(Os + toff), lds_read_tr16(Os + toff + 4 * T::STR));
+          const int trw = 32 * qb + 16 * kc + tr_row, trc = 32 * dbk + tr_col;
+          const int t0 = swz<D>(trw, trc), t1 = swz<D>(trw + 4, trc);
+          const bf16x8 oa = cat_bf16(lds_read_tr16(Os + t0), lds_read_tr16(Os + t1));
           dv[dbk] = mfma32(oa, pb[kc], dv[dbk]);
-          const bf16x8 qa = cat_bf16(lds_read_tr16(Qs + toff), lds_read_tr16(Qs + toff + 4 * T::STR));
+          const bf16x8 qa = cat_bf16(lds_read_tr16(Qs + t0), lds_read_tr16(Qs + t1));
           dk[dbk] = mfma32(qa, dsb[kc], dk[dbk]);
         }
       }
@@ -304,13 +304,12 @@ template <int D>
 struct DqTile {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
-  static constexpr int STR = D + 8;
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
   static constexpr int CH = D / 8;
   static constexpr int RPP = NTHREADS / CH;
   static constexpr int NP = BN / RPP;
-  static constexpr int TILE = BN * STR;
+  static constexpr int TILE = BN * D;         // swizzled rows
   static constexpr int STAGE = 2 * TILE;
 };
 
@@ -381,8 +380,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdParams p) {
     __bf16* Vs = Ks + T::TILE;
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) {
-      *(u32x4*)(Ks + (lrow + u * T::RPP) * T::STR + lcol) = kreg[u];
-      *(u32x4*)(Vs + (lrow + u * T::RPP) * T::STR + lcol) = vreg[u];
+      *(u32x4*)(Ks + swz<D>(lrow + u * T::RPP, lcol)) = kreg[u];
+      *(u32x4*)(Vs + swz<D>(lrow + u * T::RPP, lcol)) = vreg[u];
     }
   };
 
@@ -422,7 +421,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdParams p) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int c = 0; c < T::NC; ++c) {
-          const int off = (32 * kb2 + prow) * T::STR + 16 * c + 8 * hh;
+          const int off = swz<D>(32 * kb2 + prow, 16 * c + 8 * hh);
           s = mfma32(*(const bf16x8*)(Ks + off), qf[c], s);
           dp = mfma32(*(const bf16x8*)(Vs + off), of[c], dp);
         }
@@ -441,8 +440,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdParams p) {
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int dbk = 0; dbk < T::ND; ++dbk) {
-          const __bf16* kp = Ks + (16 * c + tr_row) * T::STR + 32 * dbk + tr_col;
-          const bf16x8 ka = cat_bf16(lds_read_tr16(kp), lds_read_tr16(kp + 4 * T::STR));
+          const int trw = 16 * c + tr_row, trc = 32 * dbk + tr_col;
+          const bf16x8 ka = cat_bf16(lds_read_tr16(Ks + swz<D>(trw, trc)),
+                                     lds_read_tr16(Ks + swz<D>(trw + 4, trc)));
           dq[dbk] = mfma32(ka, dsb[c], dq[dbk]);
         }
       }

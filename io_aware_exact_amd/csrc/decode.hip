@@ -38,7 +38,8 @@ constexpr int BNK = 32;   // keys per iteration (one MFMA block)
 
 template <int D>
 struct DecTile {
-  static constexpr int VSTR = D + 16;        // V row stride in LDS (elements)
+  static constexpr int VSTR = D + 32;        // V row stride in LDS (elements): 4 rows of
+                                             // a transposing read fall on disjoint banks
   static constexpr int NC = D / 16;          // 16-wide d chunks (K^T Q)
   static constexpr int ND = D / 32;          // 32-row d blocks of O^T
   static constexpr int CH = D / 8;           // 16-byte chunks per row

@@ -60,3 +60,24 @@ __device__ __forceinline__ void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, ui
 
 // s_waitcnt vmcnt(0): all outstanding vector-memory loads have returned.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Element index of (row, col) in a row-major LDS tile of bf16 rows of D
+// elements (D = 64 or 128, no padding) whose 16-byte chunks are XOR-permuted
+// per row.  The permutation keeps both access patterns of the kernels free of
+// bank conflicts on the 64 four-byte LDS banks:
+//   (1) 16 lanes each reading 16 bytes at one column of 16 consecutive rows
+//       (MFMA operands taken row-wise);
+//   (2) 32 lanes of the transposing read covering 4 consecutive rows, the
+//       first a multiple of 4, x 64 contiguous bytes (operands taken
+//       column-wise).
+// For D = 128 a row spans all banks: chunk c of row r goes to c ^ f(r) with
+// f(r) = 4 (r mod 4) + (r / 4 mod 4), distinct over 16 consecutive rows and
+// moving each of 4 consecutive rows to its own group of 4 chunks.  For D = 64
+// two rows share the banks (odd rows on the upper half) and
+// f(r) = 4 (r / 2 mod 2) + (r / 4 mod 4) does the same within each half.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  const int f = D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  return row * D + ((((col >> 3) ^ f)) << 3) + (col & 7);
+}

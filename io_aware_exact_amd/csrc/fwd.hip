@@ -49,8 +49,12 @@ constexpr int NTHREADS = 256;
 
 template <int D>
 struct FwdTile {
-  static constexpr int KSTR = D + 8;    // K row stride in LDS (elements)
-  static constexpr int VSTR = D + 16;   // V row stride in LDS (elements)
+  // LDS row strides (elements).  K is read in rows of 16 bytes per lane by 16
+  // lanes at once: a stride of 4 banks (mod 64) spreads 16 rows over all 64
+  // banks.  V is read transposed, 4 rows x 64 bytes per 32 lanes: a stride of
+  // 16 banks (mod 64) puts the 4 rows on disjoint banks.
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = D + 32;
   static constexpr int NC = D / 16;     // 16-wide chunks of d (QK^T)
   static constexpr int ND = D / 32;     // 32-row blocks of d (O^T)
   static constexpr int CH = D / 8;      // 16-byte chunks per row
@@ -162,6 +166,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float c2 = p.scale_log2;
+  const float lazy_margin = 8.f / c2;   // 2^8 growth of the probabilities, in score units
 
   if (ntiles > 0) {
     gload(0);
@@ -203,17 +208,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
             if (kj > lim) sacc[kb2][i] = -INFINITY;
           }
       }
-      // ---- online softmax: running max, rescale, exponentials, row sum
+      // ---- online softmax: running max, rescale, exponentials, row sum.
+      // The running max m only has to bound the scores well enough that
+      // exp2((s - m) c2) stays finite; the result O = O_acc / l is the same
+      // for any m.  So m, l and O_acc are rescaled only when some row's max
+      // grew by more than 2^8 in exp2 units (probabilities then stay <= 256,
+      // fine for fp32 sums and bf16 operands); after the first tiles this
+      // almost never happens and the 64 O_acc multiplies are skipped.
       float mx = sacc[0][0];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
       mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_base) * c2);
-      const float nb = -m_base * c2;
+      const bool grow = mx > m_run + lazy_margin;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.f;
+        if (grow) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+      }
+      const float nb = (m_run == -INFINITY) ? 0.f : -m_run * c2;
       float rs = 0.f;
       bf16x8 pf[4];
 #pragma unroll
@@ -227,10 +243,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
             pf[2 * kb2 + half][e] = (__bf16)pv;
           }
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+      l_run += rs;
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int c = 0; c < 4; ++c) {

@@ -314,7 +314,7 @@ struct DqTile {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   using T = DqTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::STAGE];
 

@@ -13,16 +13,18 @@
 //
 // gfx950 mapping (32x32x16 bf16 MFMA, operand layouts in device_common.h).
 //   * bwd_preprocess: D = rowsum(dO o O) in fp32, one 16-lane group per row.
-//   * bwd_dkdv: a workgroup of 4 waves owns 128 keys of one (batch, kv head);
-//     each wave keeps its 32 K and V rows in VGPRs as the B operands of
-//     S = Q K^T and dP = dO V^T, and its dK^T, dV^T accumulators for the
-//     whole sweep.  Query tiles of 64 rows (Q, dO, LSE, D) of every query
-//     head of the group stream through a double-buffered LDS ring.  Query
-//     rows are fed to the A operand in a permuted order so that accumulator
-//     registers 0..7 / 8..15 of a lane hold 8 consecutive queries: P and dS
-//     are then directly the B operands of dV^T += dO^T P and dK^T += Q^T dS
-//     (dO^T and Q^T come from the LDS transposing read).  Each key's gradient
-//     is a sum in a fixed order over (query head, query tile): no atomics.
+//   * bwd_dkdv: a workgroup of 8 waves owns 128 keys of one (batch, kv head);
+//     each 32-key group has a P-wave (K rows in VGPRs as the B operand of
+//     S = Q K^T, the dV^T accumulator) and a dS-wave (V rows for dP = dO V^T,
+//     the dK^T accumulator) that shares its SIMD; P goes from one to the
+//     other through LDS.  Query tiles of 64 rows (Q, dO, LSE, D) of every
+//     query head of the group stream through a double-buffered LDS ring.
+//     Query rows are fed to the A operand in a permuted order so that
+//     accumulator registers 0..7 / 8..15 of a lane hold 8 consecutive
+//     queries: P and dS are then directly the B operands of dV^T += dO^T P
+//     and dK^T += Q^T dS (dO^T and Q^T come from the LDS transposing read).
+//     Each key's gradient is a sum in a fixed order over (query head, query
+//     tile): no atomics.
 //   * bwd_dq: a workgroup of 4 waves owns 128 query rows; each wave keeps
 //     Q^T, dO^T, LSE and D of its 32 rows in registers and sweeps the K/V
 //     tiles (double-buffered in LDS) in order, computing S^T = K Q^T,
@@ -86,24 +88,32 @@ __global__ __launch_bounds__(NTHREADS) void bwd_preprocess_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for 128 keys of one (batch, kv head).
+// dK, dV for 128 keys of one (batch, kv head), with the work of each 32-key
+// group split between two waves on the same SIMD: the P-wave keeps K and the
+// dV^T accumulator (S = Q K^T, P = exp2(S c - LSE log2 e), dV^T += dO^T P) and
+// the dS-wave keeps V and the dK^T accumulator (dP = dO V^T, dS = P o (dP - D),
+// dK^T += Q^T dS), receiving P through LDS.  Each wave then holds one resident
+// operand and one accumulator, which lets two waves share a SIMD so that one
+// wave's VALU work runs beside the other's MFMAs; the MFMA work is unchanged.
 template <int D>
 struct DkdvTile {
-  static constexpr int BKV = 128;             // keys per workgroup (32 per wave)
-  static constexpr int BQ = 64;               // query rows per streamed tile
+  static constexpr int NT = 512;               // 8 waves: 4 key groups x 2 roles
+  static constexpr int BKV = 128;              // keys per workgroup (32 per key group)
+  static constexpr int BQ = 64;                // query rows per streamed tile (2 blocks of 32)
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
   static constexpr int CH = D / 8;
-  static constexpr int RPP = NTHREADS / CH;
+  static constexpr int RPP = NT / CH;
   static constexpr int NP = BQ / RPP;
-  static constexpr int TILE = BQ * D;         // elements of one Q or dO tile (swizzled rows)
+  static constexpr int TILE = BQ * D;          // elements of one Q or dO tile (swizzled rows)
   static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
+  static constexpr int PEX_BYTES = 4 * (BQ / 32) * 64 * 16 * 4;   // fp32 P per key group
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE_BYTES + T::PEX_BYTES];
 
   const int nkt = (p.Sk + T::BKV - 1) / T::BKV;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -114,26 +124,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int kgrp = wave & 3;                // key group (shared by the two roles)
+  const bool pwave = wave < 4;              // role: P-wave (else dS-wave)
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int Lq = p.Sq, Lk = p.Sk;
   const int diag = Lk - Lq;
   const int k0 = kt * T::BKV;
-  const int kw0 = k0 + 32 * wave;           // first key of this wave
+  const int kw0 = k0 + 32 * kgrp;           // first key of this key group
   const int key = kw0 + l32;                // key owned by this lane (C column)
 
-  // ---- resident K and V rows: B operands of S = Q K^T and dP = dO V^T
-  const __bf16* kb = (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
-  const __bf16* vb = (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
-  bf16x8 kf[T::NC], vf[T::NC];
+  // ---- resident operand: K (P-wave) or V (dS-wave), B operand of Q K^T / dO V^T
+  const __bf16* kvb = pwave ? (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh
+                            : (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  const int64_t kv_ss = pwave ? p.k_ss : p.v_ss;
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kvb, (uint32_t)((int64_t)Lk * kv_ss * 2));
+  bf16x8 bf[T::NC];
 #pragma unroll
-  for (int c = 0; c < T::NC; ++c) {
-    kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)(key * p.k_ss + 16 * c + 8 * hh) * 2));
-    vf[c] = __builtin_bit_cast(bf16x8, buf_load16(rv, (uint32_t)(key * p.v_ss + 16 * c + 8 * hh) * 2));
-  }
+  for (int c = 0; c < T::NC; ++c)
+    bf[c] = __builtin_bit_cast(bf16x8, buf_load16(rkv, (uint32_t)(key * kv_ss + 16 * c + 8 * hh) * 2));
 
   // ---- query tiles to visit: every head of the group, tiles from the first
   // one that can see this workgroup's keys
@@ -147,21 +157,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int lcol = (tid % T::CH) * 8;
   u32x4 qreg[T::NP], oreg[T::NP];
   float sval = 0.f;
-  __amdgpu_buffer_rsrc_t rq, rdo;
-  const float* lse_h = nullptr;
-  const float* del_h = nullptr;
-  auto head_setup = [&](int h) {
-    const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    const __bf16* db = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
-    rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
-    rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
-    lse_h = p.lse + ((int64_t)b * p.Hq + h) * Lq;
-    del_h = p.delta + ((int64_t)b * p.Hq + h) * Lq;
-  };
   auto gload = [&](int it) {
     const int h = p.group * g + it / per_head;
     const int q0 = (qt0 + it % per_head) * T::BQ;
-    head_setup(h);
+    const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    const __bf16* db = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) {
       const uint32_t r = (uint32_t)(q0 + lrow + u * T::RPP);
@@ -171,12 +173,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     // threads 0..63 fetch LSE (as log2 values), threads 64..127 fetch D
     if (tid < 2 * T::BQ) {
       const int r = q0 + (tid & (T::BQ - 1));
+      const int64_t rowbase = ((int64_t)b * p.Hq + h) * Lq;
       if (tid < T::BQ) {
-        float v = r < Lq ? lse_h[r] : INFINITY;
+        const float v = r < Lq ? p.lse[rowbase + r] : INFINITY;
         // no visible key (LSE = -inf) or padding: probabilities are zero
         sval = (v == -INFINITY) ? INFINITY : v * LOG2E;
       } else {
-        sval = r < Lq ? del_h[r] : 0.f;
+        sval = r < Lq ? p.delta[rowbase + r] : 0.f;
       }
     }
   };
@@ -191,19 +194,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
     if (tid < 2 * T::BQ) stats[tid] = sval;
   };
+  // P of key group kgrp, query block qb, as each lane's 16 accumulator values
+  float* pex = (float*)(smem + 2 * T::STAGE_BYTES) + (kgrp * (T::BQ / 32)) * 64 * 16;
 
-  f32x16 dk[T::ND], dv[T::ND];
+  f32x16 acc[T::ND];
 #pragma unroll
-  for (int i = 0; i < T::ND; ++i) {
-    dk[i] = (f32x16){};
-    dv[i] = (f32x16){};
-  }
+  for (int i = 0; i < T::ND; ++i) acc[i] = (f32x16){};
   const float c2 = p.scale_log2;
   const int prow = row_perm(l32);
   const int trG = lane >> 4;
   const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
   const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
-  const bool wave_has_keys = kw0 < Lk;
 
   if (niter > 0) {
     gload(0);
@@ -223,77 +224,99 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     const __bf16* Os = Qs + T::TILE;
     const float* lse2s = (const float*)(Os + T::TILE);
     const float* dels = lse2s + T::BQ;
+    // Every block is computed: query blocks that see none of this key
+    // group's keys (past the end, LSE = +inf; causal; keys past Lk) get P = 0
+    // from the masks, so their contributions vanish, and the loop body has
+    // no data-dependent branches around the MFMAs.
+    // ---- phase 1: both query blocks' S = Q K^T (P-wave) or dP = dO V^T
+    // (dS-wave), as two interleaved MFMA chains
+    const __bf16* As = pwave ? Qs : Os;
+    f32x16 s2[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
-    for (int qb = 0; qb < T::BQ / 32; ++qb) {
-      const int qr0 = q0 + 32 * qb;
-      // skip query blocks that see none of this wave's keys
-      bool active = wave_has_keys && qr0 < Lq;
-      if (CAUSAL) active = active && (qr0 + 31 + diag >= kw0);
-      if (!active) continue;
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+    for (int c = 0; c < T::NC; ++c) {
+      const bf16x8 a0 = *(const bf16x8*)(As + swz<D>(prow, 16 * c + 8 * hh));
+      const bf16x8 a1 = *(const bf16x8*)(As + swz<D>(32 + prow, 16 * c + 8 * hh));
+      s2[0] = mfma32(a0, bf[c], s2[0]);
+      s2[1] = mfma32(a1, bf[c], s2[1]);
+    }
+    bf16x8 pb[2][2];
+    if (pwave) {
 #pragma unroll
-      for (int c = 0; c < T::NC; ++c) {
-        const int off = swz<D>(32 * qb + prow, 16 * c + 8 * hh);
-        s = mfma32(*(const bf16x8*)(Qs + off), kf[c], s);
-        dp = mfma32(*(const bf16x8*)(Os + off), vf[c], dp);
-      }
-      const f32x4* l4 = (const f32x4*)(lse2s + 32 * qb + 8 * hh);
-      const f32x4* d4 = (const f32x4*)(dels + 32 * qb + 8 * hh);
-      const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
-      const f32x4 da = d4[0], db = d4[1], dc = d4[4], dd = d4[5];
-      const float lrow_v[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
-                                lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
-      const float drow_v[16] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3],
-                                dc[0], dc[1], dc[2], dc[3], dd[0], dd[1], dd[2], dd[3]};
-      const bool need_mask = (kw0 + 31 >= Lk) || (CAUSAL && qr0 + diag < kw0 + 31);
-      bf16x8 pb[2], dsb[2];
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qr0 = q0 + 32 * qb;
+        const f32x4* l4 = (const f32x4*)(lse2s + 32 * qb + 8 * hh);
+        const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+        const float lrow_v[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
+                                  lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
+        const bool need_mask = (kw0 + 31 >= Lk) || (CAUSAL && qr0 + diag < kw0 + 31);
+        f32x16 pv;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(__builtin_fmaf(s[i], c2, -lrow_v[i]));
+        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(s2[qb][i], c2, -lrow_v[i]));
         if (need_mask) {
-          const int iq = qr0 + perm_row_of_reg(i, hh);
-          if (key >= Lk || (CAUSAL && key > iq + diag)) pv = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int iq = qr0 + perm_row_of_reg(i, hh);
+            if (key >= Lk || (CAUSAL && key > iq + diag)) pv[i] = 0.f;
+          }
         }
-        const float dsv = pv * (dp[i] - drow_v[i]);
-        pb[i >> 3][i & 7] = (__bf16)pv;
-        dsb[i >> 3][i & 7] = (__bf16)dsv;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pb[qb][i >> 3][i & 7] = (__bf16)pv[i];
+        // lane-interleaved: 16 consecutive lanes write 256 contiguous bytes
+        f32x4* pe = (f32x4*)pex + qb * 4 * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pe[64 * j] = (f32x4){pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
       }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (A operands by transposing reads)
+    }
+    __syncthreads();   // P of every key group is in LDS
+    // ---- phase 2: P-wave: dV^T += dO^T P;  dS-wave: dS = P o (dP - D), dK^T += Q^T dS
+    if (!pwave) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4* d4 = (const f32x4*)(dels + 32 * qb + 8 * hh);
+        const f32x4 da = d4[0], db = d4[1], dc = d4[4], dd = d4[5];
+        const float drow_v[16] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3],
+                                  dc[0], dc[1], dc[2], dc[3], dd[0], dd[1], dd[2], dd[3]};
+        const f32x4* pe = (const f32x4*)pex + qb * 4 * 64 + lane;
+        f32x4 pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[j] = pe[64 * j];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pb[qb][i >> 3][i & 7] = (__bf16)(pr[i >> 2][i & 3] * (s2[qb][i] - drow_v[i]));
+      }
+    }
+    const __bf16* Ts = pwave ? Os : Qs;   // dO^T for dV, Q^T for dK
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int dbk = 0; dbk < T::ND; ++dbk) {
           const int trw = 32 * qb + 16 * kc + tr_row, trc = 32 * dbk + tr_col;
-          const int t0 = swz<D>(trw, trc), t1 = swz<D>(trw + 4, trc);
-          const bf16x8 oa = cat_bf16(lds_read_tr16(Os + t0), lds_read_tr16(Os + t1));
-          dv[dbk] = mfma32(oa, pb[kc], dv[dbk]);
-          const bf16x8 qa = cat_bf16(lds_read_tr16(Qs + t0), lds_read_tr16(Qs + t1));
-          dk[dbk] = mfma32(qa, dsb[kc], dk[dbk]);
+          const bf16x8 ta = cat_bf16(lds_read_tr16(Ts + swz<D>(trw, trc)),
+                                     lds_read_tr16(Ts + swz<D>(trw + 4, trc)));
+          acc[dbk] = mfma32(ta, pb[qb][kc], acc[dbk]);
         }
       }
     }
-    // the other stage was last read before the previous barrier
+    // the other stage was last read before the previous barrier; P is
+    // rewritten only after the barrier below
     if (more) lstore(st ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: dK = scale * dK^T^T, dV = dV^T^T, bf16, one key row per lane
+  // ---- epilogue: dV (P-wave) or dK = scale * dK (dS-wave), bf16, one key row per lane
   if (key < Lk) {
-    __bf16* dkb = (__bf16*)p.dk + (int64_t)b * p.dk_sb + (int64_t)g * p.dk_sh + (int64_t)key * p.dk_ss;
-    __bf16* dvb = (__bf16*)p.dv + (int64_t)b * p.dv_sb + (int64_t)g * p.dv_sh + (int64_t)key * p.dv_ss;
+    __bf16* out = pwave ? (__bf16*)p.dv + (int64_t)b * p.dv_sb + (int64_t)g * p.dv_sh + (int64_t)key * p.dv_ss
+                        : (__bf16*)p.dk + (int64_t)b * p.dk_sb + (int64_t)g * p.dk_sh + (int64_t)key * p.dk_ss;
+    const float f = pwave ? 1.f : p.scale;
 #pragma unroll
     for (int dbk = 0; dbk < T::ND; ++dbk)
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        bf16x4 wk, wv;
+        bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          wk[r] = (__bf16)(dk[dbk][4 * gi + r] * p.scale);
-          wv[r] = (__bf16)(dv[dbk][4 * gi + r]);
-        }
-        const int col = 32 * dbk + 8 * gi + 4 * hh;
-        *(bf16x4*)(dkb + col) = wk;
-        *(bf16x4*)(dvb + col) = wv;
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[dbk][4 * gi + r] * f);
+        *(bf16x4*)(out + 32 * dbk + 8 * gi + 4 * hh) = w;
       }
   }
 }
@@ -480,7 +503,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.Sk > 0) {
     const long nblk = (long)((p.Sk + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV) * p.Hkv * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(DkdvTile<D>::NT), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

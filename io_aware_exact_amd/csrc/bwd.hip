@@ -93,8 +93,11 @@ __global__ __launch_bounds__(NTHREADS) void bwd_preprocess_kernel(BwdParams p) {
 // dV^T accumulator (S = Q K^T, P = exp2(S c - LSE log2 e), dV^T += dO^T P) and
 // the dS-wave keeps V and the dK^T accumulator (dP = dO V^T, dS = P o (dP - D),
 // dK^T += Q^T dS), receiving P through LDS.  Each wave then holds one resident
-// operand and one accumulator, which lets two waves share a SIMD so that one
-// wave's VALU work runs beside the other's MFMAs; the MFMA work is unchanged.
+// operand and one accumulator, which lets two waves share a SIMD; the MFMA
+// work is unchanged.  The dS-wave runs one query tile behind the P-wave, so
+// in every iteration both roles have MFMA and VALU work and one barrier
+// suffices: iteration t has the P-wave on tile t and the dS-wave on tile
+// t - 1, whose P the P-wave left in LDS during iteration t - 1.
 template <int D>
 struct DkdvTile {
   static constexpr int NT = 512;               // 8 waves: 4 key groups x 2 roles
@@ -102,18 +105,17 @@ struct DkdvTile {
   static constexpr int BQ = 64;                // query rows per streamed tile (2 blocks of 32)
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
-  static constexpr int CH = D / 8;
-  static constexpr int RPP = NT / CH;
-  static constexpr int NP = BQ / RPP;
   static constexpr int TILE = BQ * D;          // elements of one Q or dO tile (swizzled rows)
   static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
-  static constexpr int PEX_BYTES = 4 * (BQ / 32) * 64 * 16 * 4;   // fp32 P per key group
+  static constexpr int NSTAGE = 3;             // tile t (P-wave), t - 1 (dS-wave), t + 1 (loading)
+  static constexpr int PEX_SLOT = 4 * 2 * 64 * 16 * 2;   // bf16 P of 4 key groups x 2 blocks
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES + 2 * PEX_SLOT;
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE_BYTES + T::PEX_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[T::LDS_BYTES];
 
   const int nkt = (p.Sk + T::BKV - 1) / T::BKV;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -152,23 +154,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   if (CAUSAL) qt0 = max(0, k0 - diag) / T::BQ;
   const int per_head = max(0, nqt - qt0);
   const int niter = per_head * p.group;
+  auto tile_q0 = [&](int it) { return (qt0 + it % per_head) * T::BQ; };
 
-  const int lrow = tid / T::CH;
-  const int lcol = (tid % T::CH) * 8;
-  u32x4 qreg[T::NP], oreg[T::NP];
+  auto stage = [&](int st) { return (__bf16*)(smem + st * T::STAGE_BYTES); };
+  // Q and dO tiles go from HBM straight into the swizzled LDS stage: each
+  // wave fills rows [8 w, 8 w + 8) of both tiles, one 1 KB block (RPI rows)
+  // per load, every lane fetching the logical chunk that belongs at its
+  // physical position in the block.
+  constexpr int RPI = 512 / D;               // rows per 1 KB block
+  constexpr int NLD = 8 / RPI;               // blocks per wave per tile
+  const int lrow_in = lane / (64 / RPI);     // row of this lane within a block
+  const int lpc = lane % (64 / RPI);         // physical 16-byte chunk
   float sval = 0.f;
   auto gload = [&](int it) {
     const int h = p.group * g + it / per_head;
-    const int q0 = (qt0 + it % per_head) * T::BQ;
+    const int q0 = tile_q0(it);
     const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     const __bf16* db = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
+    __bf16* Qs = stage((it) % T::NSTAGE);
+    __bf16* Os = Qs + T::TILE;
 #pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      const uint32_t r = (uint32_t)(q0 + lrow + u * T::RPP);
-      qreg[u] = buf_load16(rq, (r * (uint32_t)p.q_ss + lcol) * 2);
-      oreg[u] = buf_load16(rdo, (r * (uint32_t)p.do_ss + lcol) * 2);
+    for (int u = 0; u < NLD; ++u) {
+      const int row = 8 * (wave & 7) + RPI * u + lrow_in;            // row of the tile
+      const int lc = swz<D>(row, 8 * lpc) - row * D - 8 * lpc;         // logical - physical
+      const int col = 8 * lpc + lc;                                     // logical column (elements)
+      const uint32_t r = (uint32_t)(q0 + row);
+      buf_load16_lds(rq, (r * (uint32_t)p.q_ss + col) * 2, Qs + (8 * (wave & 7) + RPI * u) * D);
+      buf_load16_lds(rdo, (r * (uint32_t)p.do_ss + col) * 2, Os + (8 * (wave & 7) + RPI * u) * D);
     }
     // threads 0..63 fetch LSE (as log2 values), threads 64..127 fetch D
     if (tid < 2 * T::BQ) {
@@ -183,19 +197,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
   };
-  auto lstore = [&](int st) {
-    __bf16* Qs = (__bf16*)(smem + st * T::STAGE_BYTES);
-    __bf16* Os = Qs + T::TILE;
-    float* stats = (float*)(Os + T::TILE);
-#pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      *(u32x4*)(Qs + swz<D>(lrow + u * T::RPP, lcol)) = qreg[u];
-      *(u32x4*)(Os + swz<D>(lrow + u * T::RPP, lcol)) = oreg[u];
-    }
+  auto lstore_stats = [&](int st) {
+    float* stats = (float*)(stage(st) + 2 * T::TILE);
     if (tid < 2 * T::BQ) stats[tid] = sval;
   };
-  // P of key group kgrp, query block qb, as each lane's 16 accumulator values
-  float* pex = (float*)(smem + 2 * T::STAGE_BYTES) + (kgrp * (T::BQ / 32)) * 64 * 16;
+  // bf16 P of key group kgrp, query block qb, in P-exchange slot sl, stored
+  // lane-interleaved (16 consecutive lanes write 256 contiguous bytes)
+  auto pex = [&](int sl, int qb) {
+    return (u32x4*)(smem + T::NSTAGE * T::STAGE_BYTES + sl * T::PEX_SLOT) + ((kgrp * 2 + qb) * 2) * 64 + lane;
+  };
 
   f32x16 acc[T::ND];
 #pragma unroll
@@ -206,101 +216,124 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
   const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
 
+  // The chunk permutation of a swizzled tile depends on the row modulo 16
+  // only, so every operand address is a per-lane base plus a constant:
+  // swz(r + 16 k, c) = swz(r, c) + 16 k D.  The per-lane parts are added to
+  // the tile base once per iteration; the constants fold into the LDS
+  // instructions' offset fields.
+  int aoff[T::NC], toff[2][T::ND];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) aoff[c] = swz<D>(prow, 16 * c + 8 * hh);
+#pragma unroll
+  for (int dbk = 0; dbk < T::ND; ++dbk) {
+    toff[0][dbk] = swz<D>(tr_row, 32 * dbk + tr_col);
+    toff[1][dbk] = swz<D>(tr_row + 4, 32 * dbk + tr_col);
+  }
+
   if (niter > 0) {
     gload(0);
-    wait_vmem();
-    lstore(0);
+    lstore_stats(0);
   }
   wait_vmem();
   __syncthreads();
 
-  for (int it = 0; it < niter; ++it) {
-    const int st = it & 1;
-    const int q0 = (qt0 + it % per_head) * T::BQ;
+  // Every block is computed: query blocks that see none of this key group's
+  // keys (past the end, where LSE = +inf; above the causal diagonal; keys
+  // past Lk) get P = 0 from the masks, so their contributions vanish, and
+  // the MFMAs need no data-dependent branches.
+  for (int it = 0; it <= niter; ++it) {
     const bool more = it + 1 < niter;
     if (more) gload(it + 1);
-
-    const __bf16* Qs = (const __bf16*)(smem + st * T::STAGE_BYTES);
-    const __bf16* Os = Qs + T::TILE;
-    const float* lse2s = (const float*)(Os + T::TILE);
-    const float* dels = lse2s + T::BQ;
-    // Every block is computed: query blocks that see none of this key
-    // group's keys (past the end, LSE = +inf; causal; keys past Lk) get P = 0
-    // from the masks, so their contributions vanish, and the loop body has
-    // no data-dependent branches around the MFMAs.
-    // ---- phase 1: both query blocks' S = Q K^T (P-wave) or dP = dO V^T
-    // (dS-wave), as two interleaved MFMA chains
-    const __bf16* As = pwave ? Qs : Os;
-    f32x16 s2[2] = {(f32x16){}, (f32x16){}};
+    // P-wave on tile it; dS-wave on tile it - 1
+    const bool work = pwave ? it < niter : it > 0;
+    if (work) {
+      const int t = pwave ? it : it - 1;
+      const __bf16* Qs = stage(t % T::NSTAGE);
+      const __bf16* Os = Qs + T::TILE;
+      const float* stats = (const float*)(Os + T::TILE);
+      const __bf16* As = pwave ? Qs : Os;   // A operand rows: Q for S, dO for dP
+      const __bf16* Ts = pwave ? Os : Qs;   // transposed: dO^T for dV, Q^T for dK
+      // ---- S = Q K^T or dP = dO V^T for both query blocks, two interleaved chains
+      f32x16 s2[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
-    for (int c = 0; c < T::NC; ++c) {
-      const bf16x8 a0 = *(const bf16x8*)(As + swz<D>(prow, 16 * c + 8 * hh));
-      const bf16x8 a1 = *(const bf16x8*)(As + swz<D>(32 + prow, 16 * c + 8 * hh));
-      s2[0] = mfma32(a0, bf[c], s2[0]);
-      s2[1] = mfma32(a1, bf[c], s2[1]);
-    }
-    bf16x8 pb[2][2];
-    if (pwave) {
+      for (int c = 0; c < T::NC; ++c) {
+        const __bf16* ap = As + aoff[c];
+        const bf16x8 a0 = *(const bf16x8*)(ap);
+        const bf16x8 a1 = *(const bf16x8*)(ap + 32 * D);
+        s2[0] = mfma32(a0, bf[c], s2[0]);
+        s2[1] = mfma32(a1, bf[c], s2[1]);
+      }
+      // ---- B operands of the second product: P (P-wave) or dS (dS-wave)
+      bf16x8 ob[2][2];
+      if (pwave) {
+        const int q0 = tile_q0(t);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qr0 = q0 + 32 * qb;
-        const f32x4* l4 = (const f32x4*)(lse2s + 32 * qb + 8 * hh);
-        const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
-        const float lrow_v[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
-                                  lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
-        const bool need_mask = (kw0 + 31 >= Lk) || (CAUSAL && qr0 + diag < kw0 + 31);
-        f32x16 pv;
+        for (int qb = 0; qb < 2; ++qb) {
+          const int qr0 = q0 + 32 * qb;
+          const f32x4* l4 = (const f32x4*)(stats + 32 * qb + 8 * hh);
+          const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+          const float lrow_v[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
+                                    lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
+          const bool need_mask = (kw0 + 31 >= Lk) || (CAUSAL && qr0 + diag < kw0 + 31);
+          f32x16 pv;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(s2[qb][i], c2, -lrow_v[i]));
-        if (need_mask) {
+          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(s2[qb][i], c2, -lrow_v[i]));
+          if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int iq = qr0 + perm_row_of_reg(i, hh);
+              if (key >= Lk || (CAUSAL && key > iq + diag)) pv[i] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ob[qb][i >> 3][i & 7] = (__bf16)pv[i];
+          u32x4* pe = pex(t & 1, qb);
+          pe[0] = __builtin_bit_cast(u32x4, ob[qb][0]);
+          pe[64] = __builtin_bit_cast(u32x4, ob[qb][1]);
+        }
+      } else {
+        const float* dels = stats + T::BQ;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4* d4 = (const f32x4*)(dels + 32 * qb + 8 * hh);
+          const f32x4 da = d4[0], db = d4[1], dc = d4[4], dd = d4[5];
+          const float drow_v[16] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3],
+                                    dc[0], dc[1], dc[2], dc[3], dd[0], dd[1], dd[2], dd[3]};
+          const u32x4* pe = pex(t & 1, qb);
+          const bf16x8 p0 = __builtin_bit_cast(bf16x8, pe[0]);
+          const bf16x8 p1 = __builtin_bit_cast(bf16x8, pe[64]);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int iq = qr0 + perm_row_of_reg(i, hh);
-            if (key >= Lk || (CAUSAL && key > iq + diag)) pv[i] = 0.f;
+            const float pvv = (float)(i < 8 ? p0[i] : p1[i - 8]);
+            ob[qb][i >> 3][i & 7] = (__bf16)(pvv * (s2[qb][i] - drow_v[i]));
           }
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pb[qb][i >> 3][i & 7] = (__bf16)pv[i];
-        // lane-interleaved: 16 consecutive lanes write 256 contiguous bytes
-        f32x4* pe = (f32x4*)pex + qb * 4 * 64 + lane;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pe[64 * j] = (f32x4){pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
       }
-    }
-    __syncthreads();   // P of every key group is in LDS
-    // ---- phase 2: P-wave: dV^T += dO^T P;  dS-wave: dS = P o (dP - D), dK^T += Q^T dS
-    if (!pwave) {
+      // ---- acc += Ts^T ob for both query blocks
+      const __bf16* tb[2][T::ND];
+#pragma unroll
+      for (int dbk = 0; dbk < T::ND; ++dbk) {
+        tb[0][dbk] = Ts + toff[0][dbk];
+        tb[1][dbk] = Ts + toff[1][dbk];
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const f32x4* d4 = (const f32x4*)(dels + 32 * qb + 8 * hh);
-        const f32x4 da = d4[0], db = d4[1], dc = d4[4], dd = d4[5];
-        const float drow_v[16] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3],
-                                  dc[0], dc[1], dc[2], dc[3], dd[0], dd[1], dd[2], dd[3]};
-        const f32x4* pe = (const f32x4*)pex + qb * 4 * 64 + lane;
-        f32x4 pr[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pr[j] = pe[64 * j];
+        for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pb[qb][i >> 3][i & 7] = (__bf16)(pr[i >> 2][i & 3] * (s2[qb][i] - drow_v[i]));
-      }
-    }
-    const __bf16* Ts = pwave ? Os : Qs;   // dO^T for dV, Q^T for dK
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int dbk = 0; dbk < T::ND; ++dbk) {
-          const int trw = 32 * qb + 16 * kc + tr_row, trc = 32 * dbk + tr_col;
-          const bf16x8 ta = cat_bf16(lds_read_tr16(Ts + swz<D>(trw, trc)),
-                                     lds_read_tr16(Ts + swz<D>(trw + 4, trc)));
-          acc[dbk] = mfma32(ta, pb[qb][kc], acc[dbk]);
+          for (int dbk = 0; dbk < T::ND; ++dbk) {
+            const int rb = (32 * qb + 16 * kc) * D;
+            const bf16x8 ta = cat_bf16(lds_read_tr16(tb[0][dbk] + rb), lds_read_tr16(tb[1][dbk] + rb));
+            acc[dbk] = mfma32(ta, ob[qb][kc], acc[dbk]);
+          }
         }
       }
     }
-    // the other stage was last read before the previous barrier; P is
-    // rewritten only after the barrier below
-    if (more) lstore(st ^ 1);
+    // gload(it + 1) filled stage (it + 1) % 3, last read by the dS-wave in
+    // iteration it - 1; P slot it % 2 is read in iteration it + 1; both are
+    // complete and visible after the wait and barrier below
+    if (more) lstore_stats((it + 1) % T::NSTAGE);
+    wait_vmem();
     __syncthreads();
   }
 

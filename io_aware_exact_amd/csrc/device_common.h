@@ -58,6 +58,14 @@ __device__ __forceinline__ void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, ui
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address `lds`
+// (one 1 KB block per wave); lanes past the buffer end write zeros.  The data
+// is in LDS once vmcnt has drained.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 16, off, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(0): all outstanding vector-memory loads have returned.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

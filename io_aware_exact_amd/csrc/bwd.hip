@@ -388,7 +388,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int qrow = q0 + 32 * wave + l32;
@@ -450,6 +450,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
   const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
   const int wave_last_row = q0 + 32 * wave + 31;
+  // swizzled operand addresses: per-lane bases plus constants (the chunk
+  // permutation depends on the row modulo 16 only)
+  int aoff[T::NC], toff[2][T::ND];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) aoff[c] = swz<D>(prow, 16 * c + 8 * hh);
+#pragma unroll
+  for (int dbk = 0; dbk < T::ND; ++dbk) {
+    toff[0][dbk] = swz<D>(tr_row, 32 * dbk + tr_col);
+    toff[1][dbk] = swz<D>(tr_row + 4, 32 * dbk + tr_col);
+  }
 
   if (ntiles > 0) {
     gload(0);
@@ -477,7 +487,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int c = 0; c < T::NC; ++c) {
-          const int off = swz<D>(32 * kb2 + prow, 16 * c + 8 * hh);
+          const int off = aoff[c] + 32 * kb2 * D;
           s = mfma32(*(const bf16x8*)(Ks + off), qf[c], s);
           dp = mfma32(*(const bf16x8*)(Vs + off), of[c], dp);
         }
@@ -492,13 +502,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
         }
       }
       // dQ^T += K^T dS^T  (K^T by transposing reads)
+      const __bf16* tb[2][T::ND];
+#pragma unroll
+      for (int dbk = 0; dbk < T::ND; ++dbk) {
+        tb[0][dbk] = Ks + toff[0][dbk];
+        tb[1][dbk] = Ks + toff[1][dbk];
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int dbk = 0; dbk < T::ND; ++dbk) {
-          const int trw = 16 * c + tr_row, trc = 32 * dbk + tr_col;
-          const bf16x8 ka = cat_bf16(lds_read_tr16(Ks + swz<D>(trw, trc)),
-                                     lds_read_tr16(Ks + swz<D>(trw + 4, trc)));
+          const bf16x8 ka = cat_bf16(lds_read_tr16(tb[0][dbk] + 16 * c * D),
+                                     lds_read_tr16(tb[1][dbk] + 16 * c * D));
           dq[dbk] = mfma32(ka, dsb[c], dq[dbk]);
         }
       }

@@ -167,11 +167,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     m_run = m_new;
 #pragma unroll
     for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+    const __bf16* vbase = Vs + tr_row * T::VSTR + tr_col;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) {
-        const __bf16* vp = Vs + (16 * c + tr_row) * T::VSTR + 32 * db + tr_col;
+        const __bf16* vp = vbase + 16 * c * T::VSTR + 32 * db;
         const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
         oacc[db] = mfma32(vf, pf[c], oacc[db]);
       }

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -188,11 +188,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
       const __bf16* Vs = Ks + BN * T::KSTR;
       // ---- S^T = K Q^T for two 32-key blocks
       f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+      // per-lane bases plus compile-time constants (folded into the LDS
+      // instructions' offset fields)
+      const __bf16* kbase = Ks + kperm * T::KSTR + 8 * hh;
 #pragma unroll
       for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const bf16x8 kf = *(const bf16x8*)(Ks + (32 * kb2 + kperm) * T::KSTR + 16 * c + 8 * hh);
+          const bf16x8 kf = *(const bf16x8*)(kbase + 32 * kb2 * T::KSTR + 16 * c);
           sacc[kb2] = mfma32(kf, qf[c], sacc[kb2]);
         }
       }
@@ -245,11 +248,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
         }
       l_run += rs;
       // ---- O^T += V^T P^T
+      const __bf16* vbase = Vs + tr_row * T::VSTR + tr_col;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int db = 0; db < T::ND; ++db) {
-          const __bf16* vp = Vs + (16 * c + tr_row) * T::VSTR + 32 * db + tr_col;
+          const __bf16* vp = vbase + 16 * c * T::VSTR + 32 * db;
           const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
           oacc[db] = mfma32(vf, pf[c], oacc[db]);
         }

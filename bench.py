@@ -10,12 +10,16 @@ for the backward (five GEMM-shaped products: the recomputed scores, dP, dV,
 dK, dQ), so fwd+bwd = 14*B*H*Sq*Sk*d.  Any extra recomputation the kernels do
 is not counted.
 
-Printed: one JSON line with the whole-step TFLOP/s, the forward alone, the
-forward kernel's roofline fraction against the dense bf16 MFMA peak
-(256 CU x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s), and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+Printed: one JSON line with the whole-step TFLOP/s; each kernel of the step
+timed on its own (HIP events on the stream it is launched on); the roofline
+of the dominant kernel (the dK/dV backward kernel: four of the five backward
+products) against the dense bf16 MFMA peak (256 CU x 2.4 GHz x 4096
+flop/clk/CU = 2516.6 TFLOP/s); secondary workloads (causal, decode, varlen,
+FP8, the forward sweep); and the fp64 CPU oracle timed on a bounded sample of
+the step.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -37,24 +41,30 @@ def fwd_flops(B, Sq, Sk, H, d, causal):
     return 4.0 * B * H * Sq * Sk * d / (2 if causal else 1)
 
 
-def kernel_source_hash():
+def kernel_source_hash(files):
+    """Hash of the kernel sources a counter record was taken on."""
     h = hashlib.sha256()
-    for name in ("fwd.hip", "device_common.h"):
+    for name in files:
         with open(os.path.join(ROOT, "io_aware_exact_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per forward launch from the committed counter summary, or
-    None if it was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "fwd_bf16_b2_h16_s8192_d128_traffic.json")
+BWD_SOURCES = ("bwd.hip", "device_common.h", "fa_internal.h")
+FWD_SOURCES = ("fwd.hip", "device_common.h", "fa_internal.h")
+
+
+def traffic_from_profile(name, files):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    profiles/<name>_traffic.json, or None if it is missing or was taken on a
+    different kernel source."""
+    path = os.path.join(ROOT, "profiles", name + "_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -281,17 +291,14 @@ def main():
     q, k, v, do = inputs.qkv(B, S, S, H, H, d, W["seed"], device="cuda", with_dout=True)
     o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-    have_bwd = True
-    try:
-        fa.fwd(q, k, v, causal, out=o, lse=lse)
-        fa.bwd(q, k, v, o, do, lse, causal)
-    except fa.FaError:
-        have_bwd = False
+    grads = tuple(torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    a = fa.bwd_args(q, k, v, o, do, lse, *grads, causal, None)
+    ws = torch.empty(max(1, int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a)))),
+                     dtype=torch.uint8, device="cuda")
 
     def step():
         fa.fwd(q, k, v, causal, out=o, lse=lse)
-        if have_bwd:
-            fa.bwd(q, k, v, o, do, lse, causal)
+        fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -308,25 +315,38 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # forward kernel alone (one launch per fa_fwd call) on the same stream
-    f0 = torch.cuda.Event(enable_timing=True)
-    f1 = torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(args.steps):
-        fa.fwd(q, k, v, causal, out=o, lse=lse)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    ms_fwd = f0.elapsed_time(f1) / args.steps
+    # each kernel of the step alone, launched back to back on the same stream
+    # (one launch per call: fa_fwd, and fa_bwd restricted to one stage; the
+    # workspace already holds D from the step above)
+    reps = max(args.steps, 10)
+    ms_fwd = time_calls(lambda: fa.fwd(q, k, v, causal, out=o, lse=lse), reps)
+    ms_pre = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
+                                       stages=fa.FA_BWD_PREPROCESS), reps)
+    ms_dkdv = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
+                                        stages=fa.FA_BWD_DKDV), reps)
+    ms_dq = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
+                                      stages=fa.FA_BWD_DQ), reps)
 
     ff = fwd_flops(B, S, S, H, d, causal)
-    step_flops = ff * (3.5 if have_bwd else 1.0)
+    gemm = ff / 2                       # one GEMM-shaped product: 2*B*H*Sq*Sk*d
+    step_flops = 3.5 * ff
     value = step_flops / (ms_step * 1e-3) / 1e12
-    fwd_tflops = ff / (ms_fwd * 1e-3) / 1e12
+
+    def tf(flops, ms):
+        return round(flops / ms / 1e9, 2)
+
+    kernels = {
+        "fwd_bf16_kernel": {"ms": round(ms_fwd, 4), "algorithmic_tflops": tf(2 * gemm, ms_fwd)},
+        "bwd_preprocess_kernel": {"ms": round(ms_pre, 4)},
+        "bwd_dkdv_kernel": {"ms": round(ms_dkdv, 4), "algorithmic_tflops": tf(4 * gemm, ms_dkdv)},
+        "bwd_dq_kernel": {"ms": round(ms_dq, 4), "algorithmic_tflops": tf(gemm, ms_dq),
+                          "executed_tflops": tf(3 * gemm, ms_dq)},
+    }
+    dk_tf = 4 * gemm / ms_dkdv / 1e9
     err_o, err_lse = sampled_check(q, k, v, o, lse, causal)
 
     line = {
-        "metric": "attention fwd+bwd TFLOP/s (bf16, d=128)" if have_bwd
-                  else "attention fwd TFLOP/s (bf16, d=128)",
+        "metric": "attention fwd+bwd TFLOP/s (bf16, d=128)",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -339,22 +359,26 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic iid N(0,1), seed 2000",
-        "config": {"workload": f"exact attention {'fwd+bwd' if have_bwd else 'fwd'}, "
-                               f"B={B} H={H} Sq=Sk={S} d={d} non-causal",
+        "config": {"workload": f"exact attention fwd+bwd, B={B} H={H} Sq=Sk={S} d={d} non-causal",
                    "B": B, "H": H, "Sq": S, "Sk": S, "d": d, "causal": causal},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"tflops": round(fwd_tflops, 2), "ms": round(ms_fwd, 4),
-                "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
-        "roofline": {"kernel": "fwd_bf16_kernel<128,false,false>", "bound": "mfma",
-                     "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile()},
+        "fwd": {"tflops": tf(ff, ms_fwd), "ms": round(ms_fwd, 4),
+                "frac_of_peak": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "kernels": kernels,
+        "roofline": {"kernel": "bwd_dkdv_kernel<128,false>", "bound": "mfma",
+                     "achieved": round(dk_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dk_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile("bwd_dkdv_b2_h16_s8192_d128", BWD_SOURCES)},
+        "roofline_fwd": {"kernel": "fwd_bf16_kernel<128,false,false>", "bound": "mfma",
+                         "achieved": tf(ff, ms_fwd), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profile("fwd_bf16_b2_h16_s8192_d128", FWD_SOURCES)},
         "check": {"o_max_abs": err_o, "lse_max_abs": err_lse},
     }
     if not args.no_extra:
         line["extra"] = extra_legs(args)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(q, k, v, do, causal, have_bwd)
+        line["cpu_baseline"] = cpu_baseline(q, k, v, do, causal, True)
     print(json.dumps(line), flush=True)
 
 

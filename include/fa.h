@@ -34,7 +34,8 @@
  *   - inputs are bf16 (or OCP e4m3 for the FP8 forward); accumulation is fp32;
  *     outputs O, dQ, dK, dV are bf16, rounded to nearest even.
  *
- * Ownership.  Every pointer is a DEVICE pointer owned by the caller.  The
+ * Ownership.  Every pointer is a DEVICE pointer owned by the caller; a
+ * tensor pointer may be NULL exactly when that tensor has no elements.  The
  * library never allocates, frees or keeps a pointer past the enqueued work,
  * and never synchronises the stream: all work is enqueued on `stream`.
  * Outputs are fully overwritten.
@@ -141,7 +142,18 @@ typedef struct {
  * gradient dout [B,Sq,Hq,d], and the forward's lse [B,Hq,Sq].  Outputs dq
  * [B,Sq,Hq,d], dk and dv [B,Sk,Hkv,d] (bf16; for GQA, dk/dv sum over the query
  * heads of each kv head).  workspace: at least fa_bwd_workspace_size bytes,
- * 256-byte aligned.  The result is bitwise reproducible run to run. */
+ * 256-byte aligned.  The result is bitwise reproducible run to run.
+ *
+ * stages: 0 (or FA_BWD_ALL) runs the whole backward.  Otherwise a bitmask of
+ * FA_BWD_PREPROCESS (D = rowsum(dO o O) into the workspace), FA_BWD_DKDV and
+ * FA_BWD_DQ, run in that order; the last two read D from the workspace, so
+ * running them without FA_BWD_PREPROCESS is meaningful only after a call that
+ * ran it with the same inputs and workspace (otherwise the gradients are
+ * garbage; nothing faults).  Lets a caller time or overlap the stages. */
+#define FA_BWD_ALL 0
+#define FA_BWD_PREPROCESS 1
+#define FA_BWD_DKDV 2
+#define FA_BWD_DQ 4
 typedef struct {
   fa_dtype dtype;
   int32_t B, Sq, Sk, Hq, Hkv, d;
@@ -151,6 +163,7 @@ typedef struct {
   const float* lse;
   void* workspace;
   size_t workspace_bytes;
+  int32_t stages;
 } fa_bwd_args;
 
 /* Returns FA_ABI_VERSION. */

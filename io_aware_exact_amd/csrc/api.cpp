@@ -97,8 +97,12 @@ fa_status check_fwd(const fa_fwd_args* a) {
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
   if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
-  if (!a->q.ptr || !a->k.ptr || !a->v.ptr || !a->o.ptr || !a->lse) return FA_ERR_NULL;
-  if (fp8 && (!a->q_descale || !a->k_descale || !a->v_descale)) return FA_ERR_NULL;
+  // a pointer may be NULL exactly when its tensor has no elements
+  const bool q_side = (int64_t)a->B * a->Sq > 0, k_side = (int64_t)a->B * a->Sk > 0;
+  if (q_side && (!a->q.ptr || !a->o.ptr || !a->lse)) return FA_ERR_NULL;
+  if (k_side && (!a->k.ptr || !a->v.ptr)) return FA_ERR_NULL;
+  if (fp8 && q_side && !a->q_descale) return FA_ERR_NULL;
+  if (fp8 && k_side && (!a->k_descale || !a->v_descale)) return FA_ERR_NULL;
   if (!aligned16(a->q.ptr) || !aligned16(a->k.ptr) || !aligned16(a->v.ptr) || !aligned16(a->o.ptr) ||
       ((uintptr_t)a->lse & 3u))
     return FA_ERR_ALIGN;
@@ -140,8 +144,10 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
   if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
-  if (!a->q || !a->k || !a->v || !a->o || !a->lse || !a->cu_seqlens_q || !a->cu_seqlens_k)
-    return FA_ERR_NULL;
+  if (!a->cu_seqlens_q || !a->cu_seqlens_k) return FA_ERR_NULL;
+  // a pointer may be NULL exactly when its tensor has no elements
+  if (a->total_q > 0 && (!a->q || !a->o || !a->lse)) return FA_ERR_NULL;
+  if (a->total_k > 0 && (!a->k || !a->v)) return FA_ERR_NULL;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
       ((uintptr_t)a->lse & 3u) || ((uintptr_t)a->cu_seqlens_q & 3u) || ((uintptr_t)a->cu_seqlens_k & 3u))
     return FA_ERR_ALIGN;
@@ -178,10 +184,14 @@ fa_status check_bwd(const fa_bwd_args* a) {
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
   if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
+  if (a->stages < 0 || a->stages > (FA_BWD_PREPROCESS | FA_BWD_DKDV | FA_BWD_DQ)) return FA_ERR_SHAPE;
   const fa_tensor* ts[8] = {&a->q, &a->k, &a->v, &a->o, &a->dout, &a->dq, &a->dk, &a->dv};
+  // a pointer may be NULL exactly when its tensor has no elements
+  const bool q_side = (int64_t)a->B * a->Sq > 0, k_side = (int64_t)a->B * a->Sk > 0;
+  const bool is_q_side[8] = {true, false, false, true, true, true, false, false};
   for (int i = 0; i < 8; ++i)
-    if (!ts[i]->ptr) return FA_ERR_NULL;
-  if (!a->lse) return FA_ERR_NULL;
+    if (!ts[i]->ptr && (is_q_side[i] ? q_side : k_side)) return FA_ERR_NULL;
+  if (!a->lse && q_side) return FA_ERR_NULL;
   for (int i = 0; i < 8; ++i)
     if (!aligned16(ts[i]->ptr) || !strides_ok(*ts[i], 8)) return FA_ERR_ALIGN;
   if ((uintptr_t)a->lse & 3u) return FA_ERR_ALIGN;
@@ -330,16 +340,16 @@ fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
   const fa_status s = check_bwd(a);
   if (s != FA_OK) return s;
   if (a->B == 0 || a->Sq == 0 || a->Sk == 0) {
-    // no query rows or no keys: dQ, dK, dV are all zero
+    // no query rows or no keys: dQ, dK, dV are all zero (a fill kernel, not a
+    // memset, so that the call can be captured into a graph)
     const fa_tensor* outs[3] = {&a->dq, &a->dk, &a->dv};
     const int64_t S[3] = {a->Sq, a->Sk, a->Sk};
     const int64_t H[3] = {a->Hq, a->Hkv, a->Hkv};
     for (int i = 0; i < 3; ++i) {
       const fa_tensor& t = *outs[i];
       if (a->B == 0 || S[i] == 0) continue;
-      const bool dense = t.stride_h == a->d && t.stride_s == H[i] * a->d && t.stride_b == S[i] * t.stride_s;
-      if (!dense) return FA_ERR_SHAPE;
-      if (hipMemsetAsync(t.ptr, 0, (size_t)(a->B * S[i] * H[i] * a->d * 2), stream) != hipSuccess)
+      if (launch_zero_bf16(t.ptr, a->B, S[i], H[i], a->d, t.stride_b, t.stride_s, t.stride_h, stream) !=
+          hipSuccess)
         return FA_ERR_HIP;
     }
     return FA_OK;
@@ -363,7 +373,8 @@ fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
   p.causal = a->causal != 0;
   p.scale = a->softmax_scale;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
-  return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, stream));
+  const int stages = a->stages == FA_BWD_ALL ? (FA_BWD_PREPROCESS | FA_BWD_DKDV | FA_BWD_DQ) : a->stages;
+  return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, stages, stream));
 }
 
 fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int32_t B, int32_t S,

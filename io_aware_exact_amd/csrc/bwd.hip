@@ -537,9 +537,24 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// Zero fill of a strided bf16 [B,S,H,d] tensor, 8 elements per thread.
+__global__ __launch_bounds__(256) void zero_bf16_kernel(__bf16* ptr, int64_t S, int64_t H, int64_t d,
+                                                       int64_t sb, int64_t ss, int64_t sh, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t per_row = d / 8;
+  const int64_t c = (i % per_row) * 8;
+  int64_t r = i / per_row;
+  const int64_t h = r % H;
+  r /= H;
+  const int64_t s = r % S;
+  const int64_t b = r / S;
+  *(u32x4*)(ptr + b * sb + s * ss + h * sh + c) = (u32x4){0u, 0u, 0u, 0u};
+}
+
 template <int D, bool CAUSAL>
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  {
+hipError_t launch_bwd(const BwdParams& p, int stages, hipStream_t stream) {
+  if (stages & 1) {
     constexpr int RPB = NTHREADS / (D / 8);
     const long rows = (long)p.B * p.Sq * p.Hq;
     const long nblk = (rows + RPB - 1) / RPB;
@@ -548,24 +563,36 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.Sk > 0) {
+  if ((stages & 2) && p.Sk > 0) {
     const long nblk = (long)((p.Sk + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV) * p.Hkv * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(DkdvTile<D>::NT), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (stages & 4) {
     const long nblk = (long)((p.Sq + DqTile<D>::BM - 1) / DqTile<D>::BM) * p.Hq * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
   }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_bwd<128, true>(p, stream) : launch_bwd<128, false>(p, stream);
-  return causal ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, int stages, hipStream_t stream) {
+  if (d == 128) return causal ? launch_bwd<128, true>(p, stages, stream) : launch_bwd<128, false>(p, stages, stream);
+  return causal ? launch_bwd<64, true>(p, stages, stream) : launch_bwd<64, false>(p, stages, stream);
+}
+
+hipError_t launch_zero_bf16(void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb,
+                            int64_t ss, int64_t sh, hipStream_t stream) {
+  const int64_t n8 = B * S * H * (d / 8);
+  if (n8 <= 0) return hipSuccess;
+  const int64_t grid = (n8 + 255) / 256;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (__bf16*)ptr, S, H, d,
+                     sb, ss, sh, n8);
+  return hipGetLastError();
 }

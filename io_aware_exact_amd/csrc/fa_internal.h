@@ -79,4 +79,7 @@ hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t s
                                int H, int d, int per_tensor, void* codes, float* scales,
                                hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, int stages, hipStream_t stream);
+// Zero a bf16 [B,S,H,d] tensor with element strides (d contiguous).
+hipError_t launch_zero_bf16(void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb,
+                            int64_t ss, int64_t sh, hipStream_t stream);

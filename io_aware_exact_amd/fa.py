@@ -66,7 +66,10 @@ class BwdArgs(ctypes.Structure):
                 ("q", FaTensor), ("k", FaTensor), ("v", FaTensor), ("o", FaTensor),
                 ("dout", FaTensor), ("dq", FaTensor), ("dk", FaTensor), ("dv", FaTensor),
                 ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("stages", ctypes.c_int32)]
+
+
+FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 
 
 # Every symbol include/fa.h declares.
@@ -194,7 +197,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
     return out, lse
 
 
-def bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace=None):
+def bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace=None, stages=0):
     B, Sq, Hq, d = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
     dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
@@ -202,18 +205,23 @@ def bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return BwdArgs(dt, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
                    _t4(q), _t4(k), _t4(v), _t4(o), _t4(dout), _t4(dq), _t4(dk), _t4(dv),
-                   lse.data_ptr(), ws_ptr, ws_bytes)
+                   lse.data_ptr(), ws_ptr, ws_bytes, int(stages))
 
 
-def bwd(q, k, v, o, dout, lse, causal=False, scale=None):
-    """Dense backward.  Returns (dq, dk, dv) bf16."""
-    dq = torch.empty_like(q, dtype=torch.bfloat16)
-    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
-    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
-    a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale)
-    nbytes = lib().fa_bwd_workspace_size(ctypes.byref(a))
-    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q.device)
-    a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, ws)
+def bwd(q, k, v, o, dout, lse, causal=False, scale=None, out=None, workspace=None, stages=0):
+    """Dense backward.  Returns (dq, dk, dv) bf16.  `out` = (dq, dk, dv) and
+    `workspace` (uint8 device tensor) may be passed in to reuse buffers;
+    `stages` selects FA_BWD_* stages (0: all)."""
+    if out is None:
+        out = (torch.empty_like(q, dtype=torch.bfloat16),
+               torch.empty(k.shape, dtype=torch.bfloat16, device=k.device),
+               torch.empty(v.shape, dtype=torch.bfloat16, device=v.device))
+    dq, dk, dv = out
+    if workspace is None:
+        a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale)
+        nbytes = lib().fa_bwd_workspace_size(ctypes.byref(a))
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q.device)
+    a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace, stages)
     _check("fa_bwd", lib().fa_bwd(ctypes.byref(a), _stream()))
     return dq, dk, dv
 

@@ -104,3 +104,9 @@ def test_workspace_size_queries():
     a = fwd_args(Sq=512, Sk=512)
     assert L.fa_fwd_workspace_size(ctypes.byref(a)) == 0
     assert L.fa_fwd_workspace_size(None) == 0
+
+
+def test_bwd_rejects_bad_stages():
+    t = fa.FaTensor(FAKE, 2048, 128, 64)
+    a = fa.BwdArgs(0, 1, 16, 16, 2, 2, 64, 0, 0.125, t, t, t, t, t, t, t, t, FAKE, FAKE, 1 << 20, 9)
+    assert fa.lib().fa_bwd(ctypes.byref(a), None) == 2

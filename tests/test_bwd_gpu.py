@@ -97,3 +97,43 @@ def test_full_size_sampled_slices(causal):
     # no NaN anywhere
     for x in (dq, dk, dv):
         assert bool(torch.isfinite(x).all())
+
+
+def test_stages_equal_whole_call():
+    """Running the preprocess, dK/dV and dQ stages as separate calls gives
+    bitwise the same gradients as one call."""
+    q, k, v, do = inputs.qkv(1, 300, 300, 4, 2, 128, 12, device="cuda", with_dout=True)
+    o, lse = fa.fwd(q, k, v, True)
+    full = fa.bwd(q, k, v, o, do, lse, True)
+    out = tuple(torch.full_like(x, float("nan")) for x in full)
+    a = fa.bwd_args(q, k, v, o, do, lse, *out, True, None)
+    ws = torch.empty(max(1, int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a)))),
+                     dtype=torch.uint8, device="cuda")
+    for st in (fa.FA_BWD_PREPROCESS, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.bwd(q, k, v, o, do, lse, True, out=out, workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    for x, y in zip(out, full):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("which", ["no_queries", "no_keys"])
+def test_empty_side_gives_zero_gradients(which):
+    """Sq = 0 (no query rows: dK = dV = 0) or Sk = 0 (no keys: dQ = 0); the
+    empty tensors are zero-length views of real buffers."""
+    B, S, H, d = 2, 70, 2, 64
+    q, k, v, do = inputs.qkv(B, S, S, H, H, d, 13, device="cuda", with_dout=True)
+    if which == "no_queries":
+        q, do = q[:, :0], do[:, :0]
+    else:
+        k, v = k[:, :0], v[:, :0]
+    o = torch.zeros_like(q)
+    lse = torch.full((B, H, q.shape[1]), float("-inf"), device="cuda")
+    dq = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    gk = Guarded(tuple(k.shape), torch.bfloat16)
+    gv = Guarded(tuple(v.shape), torch.bfloat16)
+    gk.t.fill_(float("nan")), gv.t.fill_(float("nan"))
+    fa.bwd(q, k, v, o, do, lse, False, out=(dq, gk.t, gv.t))
+    torch.cuda.synchronize()
+    gk.check_guards(), gv.check_guards()
+    for t in (dq, gk.t, gv.t):
+        assert bool((t == 0).all())

@@ -103,3 +103,14 @@ def test_varlen_equals_dense_per_sequence():
         ks, ke = int(ck[z]), int(ck[z + 1])
         od, ld = fa.fwd(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], True)
         assert torch.equal(od[0], o[qs:qe]) and torch.equal(ld[0], lse[:, qs:qe])
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_no_keys(decode):
+    """Sk = 0: every row sees no key, so O = 0 and LSE = -inf (no NaN); the
+    empty K/V are zero-length views, on the tiled and the split-KV paths."""
+    q, k, v = inputs.qkv(2, 1 if decode else 100, 10, 8, 2, 128, 14, device="cuda")
+    k, v = k[:, :0], v[:, :0]
+    o, lse = (fa.fwd_decode if decode else fa.fwd)(q, k, v, True)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())

@@ -77,13 +77,29 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
 
-  // ---- which (batch, head, query tile)
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  int mt = L % p.num_m_tiles;
-  const int rest = L / p.num_m_tiles;
-  const int h = rest % p.Hq;
-  const int b = rest / p.Hq;
-  if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  // ---- which (batch, head, query tile).  Dense: consecutive tiles of one
+  // head share an XCD (L2 reuse of its K/V); causal tiles heaviest first.
+  // Packed sequences have very different lengths, so there the order is
+  // query-tile-major (all heads and sequences at the same tile index run
+  // together, heaviest index first) and the hardware's round-robin over the
+  // XCDs is kept: a contiguous range per XCD would give one XCD whole long
+  // sequences and another short ones.
+  int mt, h, b;
+  if (VARLEN) {
+    const int L = blockIdx.x;
+    const int bh = p.Hq * p.B;
+    mt = L / bh;
+    h = (L % bh) % p.Hq;
+    b = (L % bh) / p.Hq;
+    if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    mt = L % p.num_m_tiles;
+    const int rest = L / p.num_m_tiles;
+    h = rest % p.Hq;
+    b = rest / p.Hq;
+    if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  }
   const int g = h / p.group;
 
   int Lq = p.Sq, Lk = p.Sk;

@@ -31,8 +31,9 @@
  *     j <= i + (Sk - Sq); a row that sees no key gets O = 0, LSE = -inf;
  *   - LSE is the natural-log log-sum-exp of the scaled, masked scores, fp32,
  *     laid out [B, Hq, Sq] (dense) or [Hq, T_q] (varlen), contiguous;
- *   - inputs are bf16 (or OCP e4m3 for the FP8 forward); accumulation is fp32;
- *     outputs O, dQ, dK, dV are bf16, rounded to nearest even.
+ *   - inputs are bf16 (or OCP e4m3 for the FP8 forward, or fp32 for the fp32
+ *     forward); accumulation is fp32; outputs O, dQ, dK, dV are bf16 (fp32
+ *     for the fp32 forward), rounded to nearest even.
  *
  * Ownership.  Every pointer is a DEVICE pointer owned by the caller; a
  * tensor pointer may be NULL exactly when that tensor has no elements.  The
@@ -74,7 +75,7 @@ typedef enum {
   FA_ERR_SCALE = 10       /* softmax scale is not a finite number > 0 */
 } fa_status;
 
-typedef enum { FA_BF16 = 0, FA_FP8_E4M3 = 2 } fa_dtype;
+typedef enum { FA_BF16 = 0, FA_FP32 = 1, FA_FP8_E4M3 = 2 } fa_dtype;
 
 /* A dense [B, S, H, d] tensor: base pointer and element strides of the B, S
  * and H dimensions (the d dimension has stride 1).  Strides must be
@@ -85,7 +86,9 @@ typedef struct {
 } fa_tensor;
 
 /* Dense forward.  q [B,Sq,Hq,d], k and v [B,Sk,Hkv,d] in `dtype`; o
- * [B,Sq,Hq,d] bf16; lse [B,Hq,Sq] fp32 contiguous (required).
+ * [B,Sq,Hq,d] fp32 for FA_FP32, else bf16; lse [B,Hq,Sq] fp32 contiguous
+ * (required).  FA_FP32 computes everything in fp32 (no rounding of the
+ * inputs or the probabilities); it is meant for checking, not speed.
  * FP8 only: q_descale [B,Hq,ceil(Sq/128)], k_descale and v_descale
  * [B,Hkv,ceil(Sk/128)], fp32 contiguous: the real value of an element is its
  * e4m3 value times the scale of its (batch, head, 128-token block).

@@ -90,9 +90,10 @@ DecodePlan decode_plan(const fa_fwd_args* a) {
 
 fa_status check_fwd(const fa_fwd_args* a) {
   if (!a) return FA_ERR_NULL;
-  if (a->dtype != FA_BF16 && a->dtype != FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if (a->dtype != FA_BF16 && a->dtype != FA_FP8_E4M3 && a->dtype != FA_FP32) return FA_ERR_DTYPE;
   const bool fp8 = a->dtype == FA_FP8_E4M3;
-  const int64_t es = fp8 ? 1 : 2;            // bytes per q/k/v element
+  const int64_t es = fp8 ? 1 : (a->dtype == FA_FP32 ? 4 : 2);   // bytes per q/k/v element
+  const int64_t oes = a->dtype == FA_FP32 ? 4 : 2;                // bytes per o element
   if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
@@ -111,14 +112,14 @@ fa_status check_fwd(const fa_fwd_args* a) {
     return FA_ERR_ALIGN;
   const int64_t smult = 16 / es;             // 16-byte rows
   if (!strides_ok(a->q, smult) || !strides_ok(a->k, smult) || !strides_ok(a->v, smult) ||
-      !strides_ok(a->o, 8))
+      !strides_ok(a->o, 16 / oes))
     return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
   if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (!fits32(a->Sq, a->q.stride_s, es) || !fits32(a->Sq, a->o.stride_s, 2) ||
+  if (!fits32(a->Sq, a->q.stride_s, es) || !fits32(a->Sq, a->o.stride_s, oes) ||
       !fits32(a->Sk, a->k.stride_s, es) || !fits32(a->Sk, a->v.stride_s, es))
     return FA_ERR_SHAPE;
-  const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
+  const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, oes);
   const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
   const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, es);
   const Span sk = span4(a->k.ptr, a->B, a->Sk, a->Hkv, a->d, a->k.stride_b, a->k.stride_s, a->k.stride_h, es);
@@ -277,6 +278,7 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
   p.num_m_tiles = (a->Sq + kBM - 1) / kBM;
   p.scale = a->softmax_scale;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  if (a->dtype == FA_FP32) return hip_status(launch_fwd_f32(p, a->d, a->causal != 0, stream));
   if (a->dtype == FA_FP8_E4M3) {
     p.q_descale = a->q_descale;
     p.k_descale = a->k_descale;

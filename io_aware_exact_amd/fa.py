@@ -15,7 +15,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_BF16 = 0
+FA_FP32 = 1
 FA_FP8_E4M3 = 2
+_DTYPES = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}
 
 
 class FaError(RuntimeError):
@@ -131,7 +133,7 @@ def _scale(d, scale):
 def fwd_args(q, k, v, out, lse, causal, scale, workspace=None):
     B, Sq, Hq, d = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
-    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    dt = _DTYPES.get(q.dtype, -1)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return FwdArgs(dt, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
@@ -150,13 +152,15 @@ def fwd_workspace_bytes(q, k, v, causal=False, scale=None):
 
 
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None):
-    """Dense forward.  q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16 on the GPU.
-    Returns (o [B,Sq,Hq,d] bf16, lse [B,Hq,Sq] fp32).  With a `workspace`
+    """Dense forward.  q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] bf16 (or fp32) on the
+    GPU.  Returns (o [B,Sq,Hq,d] bf16 (fp32 for fp32 inputs), lse [B,Hq,Sq]
+    fp32).  With a `workspace`
     (uint8 device tensor of fwd_workspace_bytes) decode-shaped calls take the
     split-KV path."""
     B, Sq, Hq, d = q.shape
     if out is None:
-        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q.device)
+        odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+        out = torch.empty((B, Sq, Hq, d), dtype=odt, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     a = fwd_args(q, k, v, out, lse, causal, scale, workspace)

@@ -110,3 +110,10 @@ def test_bwd_rejects_bad_stages():
     t = fa.FaTensor(FAKE, 2048, 128, 64)
     a = fa.BwdArgs(0, 1, 16, 16, 2, 2, 64, 0, 0.125, t, t, t, t, t, t, t, t, FAKE, FAKE, 1 << 20, 9)
     assert fa.lib().fa_bwd(ctypes.byref(a), None) == 2
+
+
+def test_fwd_varlen_rejects_fp32():
+    a = fa.FwdVarlenArgs(1, 1, 2, 2, 64, 16, 16, 16, 16, 0, 0.125, FAKE, FAKE + (1 << 24),
+                         FAKE + (2 << 24), FAKE + (3 << 24), 128, 64, 128, 64, 128, 64, 128, 64,
+                         FAKE + (4 << 24), FAKE + (5 << 24), FAKE + (6 << 24))
+    assert fa.lib().fa_fwd_varlen(ctypes.byref(a), None) == 4

@@ -114,3 +114,38 @@ def test_no_keys(decode):
     o, lse = (fa.fwd_decode if decode else fa.fwd)(q, k, v, True)
     torch.cuda.synchronize()
     assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+# fp32 path: inputs and probabilities are not rounded below fp32, so the bars
+# are those of fp32 arithmetic (a few fp32 ulps of O ~ 1 and LSE ~ 10 after a
+# sum over up to a thousand products): O <= 1e-4 max-abs, LSE <= 1e-5 max-abs.
+F32_O_MAX_ABS = 1e-4
+F32_LSE_MAX_ABS = 1e-5
+
+
+def run_dense_f32(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
+    print(f"fp32 B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}", flush=True)
+    q, k, v = inputs.qkv(B, Sq, Sk, Hq, Hkv, d, seed, dtype=torch.float32, device="cuda")
+    go = Guarded((B, Sq, Hq, d), torch.float32)
+    gl = Guarded((B, Hq, Sq), torch.float32)
+    fa.fwd(q, k, v, causal, scale, out=go.t, lse=gl.t)
+    torch.cuda.synchronize()
+    go.check_guards()
+    gl.check_guards()
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, causal, scale)
+    check_o("O", go.t.cpu().numpy(), o_ref, max_abs=F32_O_MAX_ABS, mean_abs=F32_O_MAX_ABS, rel=1e-5)
+    check_lse("LSE", gl.t.cpu().numpy(), lse_ref, max_abs=F32_LSE_MAX_ABS)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_config_fp32(causal):
+    # B=1, H=2, Sq=Sk=256, d=64, iid N(0,1) in fp32, scale 1/sqrt(d)
+    run_dense_f32(1, 256, 256, 2, 2, 64, causal, seed=0)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 1, 64), (2, 127, 129, 4, 2, 128),
+                                   (1, 300, 200, 2, 2, 64), (1, 200, 1000, 8, 1, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes_fp32(shape, causal):
+    B, Sq, Sk, Hq, Hkv, d = shape
+    run_dense_f32(B, Sq, Sk, Hq, Hkv, d, causal, seed=50 + sum(shape))

@@ -15,11 +15,13 @@
 // one K scale sk_J and one V scale sv_J, so
 //   * the scores are s = (scale * sq * sk_J) * (q8 . k8): the whole factor,
 //     times log2(e), is the per-tile constant of the exp2 FMA;
-//   * p = exp2(s - m) is multiplied by 2^8 before rounding to e4m3, so that
-//     probabilities down to 2^-14 keep 3 mantissa bits (448 bounds 2^8 * 1);
+//   * p = exp2(s - m) is stored in e4m3 as 2^8 p (the factor rides in the
+//     exp2 FMA constant), so that probabilities down to 2^-14 keep 3 mantissa
+//     bits (448 bounds 2^8 * 1);
 //   * V's scale is folded into the running rescale: the accumulator holds
 //     O_hat = O_acc / sv_J, updated as O_hat <- O_hat * alpha * sv_{J-1} / sv_J
-//     + P8 V8_J, and the epilogue writes O = sv_last * O_hat / (2^8 * l).
+//     + P8 V8_J (skipped when the factor is 1: same V block, no new row max),
+//     and the epilogue writes O = sv_last * O_hat / l with l = sum 2^8 p.
 //
 // gfx950 mapping.  As in the bf16 forward (S^T = K Q^T with query rows in the
 // MFMA columns, 4 waves x 32 rows, 2-stage LDS ring of 64-key tiles), with the
@@ -41,7 +43,9 @@ constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NTHREADS = 256;
 constexpr int QBLK = 128;          // tokens per quantisation block
-constexpr float P_PRESCALE = 256.f;
+// Probabilities are stored in e4m3 as 2^P_LOG2 p <= 2^8 < 448; values down
+// to 2^-(6 + P_LOG2) keep 3 mantissa bits.
+constexpr float P_LOG2 = 8.f;
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
@@ -53,10 +57,11 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2*)(p));
 }
 
-// Two fp32 values -> two e4m3 codes in the low 16 bits (hardware rounding to
-// nearest even; inputs here lie in [0, 256]).
-__device__ __forceinline__ int pack2_fp8(float a, float b) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// Four fp32 values -> four e4m3 codes in one word, a in the low byte
+// (hardware rounding to nearest even; inputs here lie in [0, 256]).
+__device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 template <int D>
@@ -156,9 +161,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   f32x16 oacc[T::ND];
 #pragma unroll
   for (int i = 0; i < T::ND; ++i) oacc[i] = (f32x16){};
-  float m_run = -INFINITY;   // running max in log2 units
-  float l_run = 0.f;
-  float sv_prev = 1.f;
+  float m_run = -INFINITY;   // running max in log2 units of the scaled scores
+  float l_run = 0.f;         // sum of 2^P_LOG2 p
+  float sv_prev = 1.f;       // V scale the accumulator is currently in units of
   const float cq = p.scale_log2 * sq;
 
   if (ntiles > 0) {
@@ -174,18 +179,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
     const int j0 = t * BN;
     const bool more = t + 1 < ntiles;
     if (more) gload(j0 + BN);
-    const float sv = vsc[j0 / QBLK];
     const bool wave_active = !CAUSAL || j0 <= wave_last_row + diag;
     if (wave_active) {
       const uint8_t* Ks = smem + st * T::STAGE;
       const uint8_t* Vs = Ks + BN * T::STR;
       const float c2 = cq * ksc[j0 / QBLK];
+      const float sv = vsc[j0 / QBLK];
+      const uint8_t* kbase = Ks + kperm * T::STR + 32 * hh;
       f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
       for (int c = 0; c < T::NC; ++c)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const uint8_t* kp = Ks + (32 * kb2 + kperm) * T::STR + 64 * c + 32 * hh;
+          const uint8_t* kp = kbase + 32 * kb2 * T::STR + 64 * c;
           const u32x4 lo = *(const u32x4*)kp, hi = *(const u32x4*)(kp + 16);
           const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -208,9 +214,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
       mx = fmaxf(mx, wave_xor32(mx)) * c2;
-      const float m_new = fmaxf(m_run, mx);
-      const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_base);
+      const bool grow = mx > m_run;
+      const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+      if (grow) m_run = mx;
+      l_run *= alpha;
+      // O_hat <- O_hat alpha sv_prev / sv; skipped when that factor is 1 in
+      // every lane (same V block, no row max grew)
+      const float resc = alpha * (sv_prev / sv);
+      if (__builtin_amdgcn_ballot_w64(resc != 1.f) != 0) {
+#pragma unroll
+        for (int i = 0; i < T::ND; ++i) oacc[i] *= resc;
+      }
+      sv_prev = sv;
+      // p8 = 2^P_LOG2 exp2(s c2 - m): the prescale rides in the FMA constant
+      const float nb = (m_run == -INFINITY ? 0.f : -m_run) + P_LOG2;
       float rs = 0.f;
       i32x8 pf;
 #pragma unroll
@@ -218,43 +235,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(__builtin_fmaf(sacc[r >> 1][8 * (r & 1) + e], c2, -m_base));
+          pv[e] = fast_exp2(__builtin_fmaf(sacc[r >> 1][8 * (r & 1) + e], c2, nb));
           rs += pv[e];
         }
-        const int w0 = pack2_fp8(pv[0] * P_PRESCALE, pv[1] * P_PRESCALE);
-        const int w1 = pack2_fp8(pv[2] * P_PRESCALE, pv[3] * P_PRESCALE);
-        const int w2 = pack2_fp8(pv[4] * P_PRESCALE, pv[5] * P_PRESCALE);
-        const int w3 = pack2_fp8(pv[6] * P_PRESCALE, pv[7] * P_PRESCALE);
-        pf[2 * r] = (w0 & 0xffff) | (w1 << 16);
-        pf[2 * r + 1] = (w2 & 0xffff) | (w3 << 16);
+        pf[2 * r] = pack4_fp8(pv[0], pv[1], pv[2], pv[3]);
+        pf[2 * r + 1] = pack4_fp8(pv[4], pv[5], pv[6], pv[7]);
       }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      const float resc = alpha * (sv_prev / sv);
-#pragma unroll
-      for (int i = 0; i < T::ND; ++i) oacc[i] *= resc;
+      l_run += rs;
       // O_hat^T += V8^T P8^T (64 keys per MFMA)
+      const uint8_t* vbase = Vs + tr_row * T::STR + tr_col;
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) {
         i32x8 vf;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const i32x2 x = lds_read_tr8(Vs + (16 * r + tr_row) * T::STR + 32 * db + tr_col);
+          const i32x2 x = lds_read_tr8(vbase + 16 * r * T::STR + 32 * db);
           vf[2 * r] = x[0];
           vf[2 * r + 1] = x[1];
         }
         oacc[db] = mfma_fp8(vf, pf, oacc[db]);
       }
-      sv_prev = sv;   // O_hat is now relative to this tile's V scale
     }
     if (more) lstore(st ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: O = sv_last * O_hat / (2^8 l), LSE = ln 2 * m + ln l
+  // ---- epilogue: O = sv_last O_hat / l, LSE = ln 2 (m - P_LOG2) + ln l
   const float l_tot = l_run + wave_xor32(l_run);
   if (qrow < Lq) {
-    const float inv = l_tot > 0.f ? sv_prev / (P_PRESCALE * l_tot) : 0.f;
+    const float inv = l_tot > 0.f ? sv_prev / l_tot : 0.f;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)((int64_t)Lq * p.o_ss * 2));
     const uint32_t orow = (uint32_t)(qrow * p.o_ss) * 2;
 #pragma unroll
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
         for (int r = 0; r < 4; ++r) w[r] = (__bf16)(oacc[db][4 * gi + r] * inv);
         buf_store8(__builtin_bit_cast(u32x2, w), ro, orow + (uint32_t)(32 * db + 8 * gi + 4 * hh) * 2);
       }
-    if (hh == 0) lseb[qrow] = l_tot > 0.f ? m_run * 0.6931471805599453f + logf(l_tot) : -INFINITY;
+    if (hh == 0) lseb[qrow] = l_tot > 0.f ? (m_run - P_LOG2) * 0.6931471805599453f + logf(l_tot) : -INFINITY;
   }
 }
 

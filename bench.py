@@ -51,7 +51,7 @@ def kernel_source_hash(files):
 
 
 BWD_SOURCES = ("bwd.hip", "device_common.h", "fa_internal.h")
-FWD_SOURCES = ("fwd.hip", "device_common.h", "fa_internal.h")
+FWD_SOURCES = ("fwd_pp.hip", "device_common.h", "fa_internal.h")
 
 
 def traffic_from_profile(name, files):
@@ -336,7 +336,7 @@ def main():
         return round(flops / ms / 1e9, 2)
 
     kernels = {
-        "fwd_bf16_kernel": {"ms": round(ms_fwd, 4), "algorithmic_tflops": tf(2 * gemm, ms_fwd)},
+        "fwd_bf16_pp_kernel": {"ms": round(ms_fwd, 4), "algorithmic_tflops": tf(2 * gemm, ms_fwd)},
         "bwd_preprocess_kernel": {"ms": round(ms_pre, 4)},
         "bwd_dkdv_kernel": {"ms": round(ms_dkdv, 4), "algorithmic_tflops": tf(4 * gemm, ms_dkdv)},
         "bwd_dq_kernel": {"ms": round(ms_dq, 4), "algorithmic_tflops": tf(gemm, ms_dq),
@@ -369,7 +369,7 @@ def main():
                      "achieved": round(dk_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dk_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile("bwd_dkdv_b2_h16_s8192_d128", BWD_SOURCES)},
-        "roofline_fwd": {"kernel": "fwd_bf16_kernel<128,false,false>", "bound": "mfma",
+        "roofline_fwd": {"kernel": "fwd_bf16_pp_kernel<128,false,false>", "bound": "mfma",
                          "achieved": tf(ff, ms_fwd), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profile("fwd_bf16_b2_h16_s8192_d128", FWD_SOURCES)},

@@ -74,6 +74,8 @@ struct DecodeParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen,
                            hipStream_t stream);
+hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varlen,
+                              hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int B, int S,

@@ -1,0 +1,364 @@
+// Forward kernel of IO-aware exact attention for gfx950 with two wave groups
+// in ping-pong (bf16 in, fp32 accumulate, bf16 out, fp32 LSE).
+//
+// Method: as the tiled forward ("Flash Attention and Efficient Transformer
+// Mechanisms", block computation; Dao-AILab repository overview, online
+// softmax with rescaling).  The schedule follows the idea of hiding the
+// low-throughput softmax under matrix products ("FlashAttention-3: Fast and
+// Accurate Attention with Asynchrony and Low-precision", second
+// contribution), built for CDNA4 from barriers instead of asynchronous
+// tensor cores:
+//   * a workgroup of 8 waves owns 256 query rows (32 per wave); waves 0-3
+//     (group A) and 4-7 (group B) share the four SIMDs pairwise;
+//   * work alternates in phases separated by workgroup barriers: in every
+//     phase one group issues MFMAs -- P V for tile t-1 and the scores of tile
+//     t -- while the other runs the softmax of its newest scores, so the two
+//     waves of a SIMD always have different pipes to use;
+//   * group A takes the MFMA role in even phases, B in odd ones; phase f reads
+//     K of tile f/2 and V of tile f/2 - 1, and the loads issued in phase 2t
+//     (K_{t+1}, V_t) are written to the free LDS stages at the end of phase
+//     2t+1.
+// Operand layouts, the transposed score orientation, lazy rescaling and
+// masking are those of the one-group forward kernel.
+#include "device_common.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int BM = 256;
+constexpr int BN = 64;
+constexpr int NT = 512;
+
+template <int D>
+struct PpTile {
+  static constexpr int KSTR = D + 8;    // K rows: 16 rows x 16 bytes per 16 lanes
+  static constexpr int VSTR = D + 32;   // V rows: read transposed, 4 rows x 64 bytes
+  static constexpr int NC = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int CH = D / 8;
+  static constexpr int RPP = NT / CH;
+  static constexpr int NP = BN / RPP;
+  static constexpr int KSTAGE = BN * KSTR;
+  static constexpr int VSTAGE = BN * VSTR;
+  static constexpr int LDS_ELEMS = 2 * (KSTAGE + VSTAGE);
+};
+
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = w & 7, s = w >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+// Workgroup barrier that the instruction scheduler may not move work across:
+// register-only work (the exponentials) would otherwise drift into the
+// neighbouring phase and the two groups would no longer alternate.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
+  using T = PpTile<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
+
+  int mt, h, b;
+  if (VARLEN) {
+    const int L = blockIdx.x;
+    const int bh = p.Hq * p.B;
+    mt = L / bh;
+    h = (L % bh) % p.Hq;
+    b = (L % bh) / p.Hq;
+    if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    mt = L % p.num_m_tiles;
+    const int rest = L / p.num_m_tiles;
+    h = rest % p.Hq;
+    b = rest / p.Hq;
+    if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
+  }
+  const int g = h / p.group;
+  int Lq = p.Sq, Lk = p.Sk;
+  int64_t qtok = 0, ktok = 0;
+  if (VARLEN) {
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    Lq = p.cu_q[b + 1] - qs;
+    Lk = p.cu_k[b + 1] - ks;
+    qtok = qs;
+    ktok = ks;
+  }
+  const int q0 = mt * BM;
+  if (q0 >= Lq) return;   // workgroup-uniform: no barrier is reached
+  const int diag = Lk - Lq;
+
+  const __bf16* qb = (const __bf16*)p.q + (VARLEN ? qtok * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+  const __bf16* kb = (const __bf16*)p.k + (VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
+  __bf16* ob = (__bf16*)p.o + (VARLEN ? qtok * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
+  float* lseb = p.lse + (VARLEN ? qtok : (int64_t)b * p.lse_sb) + (int64_t)h * p.lse_sh;
+
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, q0 + BM + diag);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                  // 0: group A, 1: group B
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- Q^T fragments (B operand of S^T = K Q^T), resident for the sweep
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
+  const int qrow = q0 + wave * 32 + l32;
+  bf16x8 qf[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * p.q_ss + 16 * c + 8 * hh) * 2));
+
+  const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  const int trG = lane >> 4;
+  const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
+  const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
+
+  // ---- K/V staging through registers into two LDS stages each
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  const int lrow = tid / T::CH;
+  const int lcol = (tid % T::CH) * 8;
+  const uint32_t koff = (uint32_t)(lrow * p.k_ss + lcol) * 2;
+  const uint32_t voff = (uint32_t)(lrow * p.v_ss + lcol) * 2;
+  u32x4 kreg[T::NP], vreg[T::NP];
+  auto kstage = [&](int st) { return smem + st * T::KSTAGE; };
+  auto vstage = [&](int st) { return smem + 2 * T::KSTAGE + st * T::VSTAGE; };
+  auto gload_k = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u)
+      kreg[u] = buf_load16(rk, koff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.k_ss * 2);
+  };
+  auto gload_v = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u)
+      vreg[u] = buf_load16(rv, voff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.v_ss * 2);
+  };
+  auto lstore_k = [&](int st) {
+    __bf16* Ks = kstage(st);
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) *(u32x4*)(Ks + (lrow + u * T::RPP) * T::KSTR + lcol) = kreg[u];
+  };
+  auto lstore_v = [&](int st) {
+    __bf16* Vs = vstage(st);
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) *(u32x4*)(Vs + (lrow + u * T::RPP) * T::VSTR + lcol) = vreg[u];
+  };
+
+  f32x16 oacc[T::ND];
+#pragma unroll
+  for (int i = 0; i < T::ND; ++i) oacc[i] = (f32x16){};
+  f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+  bf16x8 pf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pf[c] = (bf16x8){};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c2 = p.scale_log2;
+  const float lazy_margin = 8.f / c2;   // 2^8 growth of the probabilities, in score units
+  const int wave_first_row = q0 + wave * 32;
+
+  // O^T += V^T P^T for tile t (V in stage t & 1)
+  auto pv_product = [&](int t) {
+    const __bf16* vbase = vstage(t & 1) + tr_row * T::VSTR + tr_col;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) {
+        const __bf16* vp = vbase + 16 * c * T::VSTR + 32 * db;
+        const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
+        oacc[db] = mfma32(vf, pf[c], oacc[db]);
+      }
+    }
+    // keep the transposing reads one MFMA group ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::ND, 0);
+#pragma unroll
+    for (int i = 0; i < 3 * T::ND; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, T::ND, 0);
+  };
+  // S^T = K Q^T for tile t (K in stage t & 1)
+  auto scores = [&](int t) {
+    const __bf16* kbase = kstage(t & 1) + kperm * T::KSTR + 8 * hh;
+    sacc[0] = (f32x16){};
+    sacc[1] = (f32x16){};
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8 kf = *(const bf16x8*)(kbase + 32 * kb2 * T::KSTR + 16 * c);
+        sacc[kb2] = mfma32(kf, qf[c], sacc[kb2]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * T::NC - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // mask, running max, lazy rescale, exponentials and row sum of tile t.
+  // O = O_acc / l is the same for any running max that keeps the
+  // exponentials finite, so m, l and O_acc are rescaled only when some row's
+  // max grew by more than 2^8 in exp2 units.
+  auto softmax = [&](int t) {
+    const int j0 = t * BN;
+    const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > wave_first_row + diag);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Lk - 1, qrow + diag) : Lk - 1;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = j0 + 32 * kb2 + 16 * (i >> 3) + 8 * hh + (i & 7);
+          if (kj > lim) sacc[kb2][i] = -INFINITY;
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const bool grow = mx > m_run + lazy_margin;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.f;
+      if (grow) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+    }
+    const float nb = (m_run == -INFINITY) ? 0.f : -m_run * c2;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = fast_exp2(__builtin_fmaf(sacc[kb2][8 * half + e], c2, nb));
+          rs += pv;
+          pf[2 * kb2 + half][e] = (__bf16)pv;
+        }
+      }
+    l_run += rs;
+    __asm__ volatile("" : "+v"(l_run));   // the row sum belongs to this phase
+  };
+
+  if (ntiles > 0) {
+    gload_k(0);
+    lstore_k(0);
+  }
+  wait_vmem();  // Q fragments have landed on every path into the loop
+  __syncthreads();
+
+  // A wave sees tile t iff t < nt_w (monotone in t under the causal mask).
+  int nt_w = ntiles;
+  if (CAUSAL) {
+    const int last_key = wave_first_row + 31 + diag;
+    nt_w = last_key < 0 ? 0 : min(ntiles, last_key / BN + 1);
+  }
+  const bool is_a = grp == 0;
+
+  // The two groups run separate programs with the same number of barriers.
+  // Global loads of K_{t+1} and V_t are issued in phase 2t and written to LDS
+  // at the end of phase 2t+1, into the stages last read in phase 2t-1.
+  if (ntiles > 0) {
+    if (is_a) {
+      if (ntiles > 1) gload_k(BN);
+      gload_v(0);
+      if (nt_w > 0) scores(0);
+      phase_barrier();                                   // phase 0
+      if (nt_w > 0) softmax(0);
+      if (ntiles > 1) lstore_k(1);
+      lstore_v(0);
+      phase_barrier();                                   // phase 1
+      for (int t = 1; t < ntiles; ++t) {
+        const bool more = t + 1 < ntiles;
+        if (more) gload_k((t + 1) * BN);
+        gload_v(t * BN);
+        if (t - 1 < nt_w) pv_product(t - 1);
+        if (t < nt_w) scores(t);
+        phase_barrier();                                 // phase 2t
+        if (t < nt_w) softmax(t);
+        if (more) lstore_k((t + 1) & 1);
+        lstore_v(t & 1);
+        phase_barrier();                                 // phase 2t+1
+      }
+      if (ntiles - 1 < nt_w) pv_product(ntiles - 1);
+      phase_barrier();                                   // phase 2n
+    } else {
+      if (ntiles > 1) gload_k(BN);
+      gload_v(0);
+      phase_barrier();                                   // phase 0
+      if (nt_w > 0) scores(0);
+      if (ntiles > 1) lstore_k(1);
+      lstore_v(0);
+      phase_barrier();                                   // phase 1
+      for (int t = 1; t < ntiles; ++t) {
+        const bool more = t + 1 < ntiles;
+        if (more) gload_k((t + 1) * BN);
+        gload_v(t * BN);
+        if (t - 1 < nt_w) softmax(t - 1);
+        phase_barrier();                                 // phase 2t
+        if (t - 1 < nt_w) pv_product(t - 1);
+        if (t < nt_w) scores(t);
+        if (more) lstore_k((t + 1) & 1);
+        lstore_v(t & 1);
+        phase_barrier();                                 // phase 2t+1
+      }
+      if (ntiles - 1 < nt_w) softmax(ntiles - 1);
+      phase_barrier();                                   // phase 2n
+      if (ntiles - 1 < nt_w) pv_product(ntiles - 1);     // phase 2n+1
+    }
+  }
+
+  // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
+  const float l_tot = l_run + wave_xor32(l_run);
+  if (qrow < Lq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)((int64_t)Lq * p.o_ss * 2));
+    const uint32_t orow = (uint32_t)(qrow * p.o_ss) * 2;
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(oacc[db][4 * gi + r] * inv);
+        buf_store8(__builtin_bit_cast(u32x2, w), ro, orow + (uint32_t)(32 * db + 8 * gi + 4 * hh) * 2);
+      }
+    if (hh == 0) lseb[qrow] = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch(FwdParams p, hipStream_t stream) {
+  const int rows = p.Sq;   // dense: Sq; varlen: max query length
+  p.num_m_tiles = (rows + BM - 1) / BM;
+  const long nblk = (long)p.num_m_tiles * p.Hq * p.B;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  if (causal) return varlen ? launch<128, true, true>(p, stream) : launch<128, true, false>(p, stream);
+  return varlen ? launch<128, false, true>(p, stream) : launch<128, false, false>(p, stream);
+}

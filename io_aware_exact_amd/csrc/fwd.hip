@@ -1,5 +1,7 @@
 // Forward kernel of IO-aware exact attention for gfx950 (bf16 in, fp32
-// accumulate, bf16 out, fp32 LSE).
+// accumulate, bf16 out, fp32 LSE), one group of four waves per workgroup.
+// Serves d = 64, where the softmax outweighs the matrix work per tile;
+// d = 128 runs the two-group kernel of fwd_pp.hip.
 //
 // Method (pages on IO-aware exact attention): blocks of Q, K and V are moved
 // from HBM into on-chip memory and partial outputs are computed there

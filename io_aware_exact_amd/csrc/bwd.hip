@@ -355,24 +355,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ for 128 query rows of one (batch, query head).
+// dQ for 128 query rows of one (batch, query head).  Tile t's MFMA block
+// computes dQ^T += K_{t-1}^T dS_{t-1}^T together with S^T and dP^T of tile
+// t, and the VALU block that follows forms dS^T of tile t: one MFMA block and
+// one VALU block per tile.  K and V tiles come straight from HBM into
+// swizzled LDS stages (LDS DMA), K in three stages (K_{t-1} is still read in
+// iteration t), V in two.
 template <int D>
 struct DqTile {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
-  static constexpr int CH = D / 8;
-  static constexpr int RPP = NTHREADS / CH;
-  static constexpr int NP = BN / RPP;
-  static constexpr int TILE = BN * D;         // swizzled rows
-  static constexpr int STAGE = 2 * TILE;
+  static constexpr int TILE = BN * D;         // swizzled rows, no padding
+  static constexpr int KSTAGES = 3;
+  static constexpr int VSTAGES = 2;
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   using T = DqTile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 smem[(T::KSTAGES + T::VSTAGES) * T::TILE];
 
   const int nmt = (p.Sq + T::BM - 1) / T::BM;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -417,39 +420,51 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   int kend = Lk;
   if (CAUSAL) kend = min(Lk, q0 + T::BM + diag);
   const int ntiles = kend > 0 ? (kend + T::BN - 1) / T::BN : 0;
+  // tiles this wave sees: t < nt_w (monotone under the causal mask)
+  const int wrow0 = q0 + 32 * wave;
+  int nt_w = wrow0 < Lq ? ntiles : 0;
+  if (CAUSAL) {
+    const int last_key = wrow0 + 31 + diag;
+    nt_w = last_key < 0 ? 0 : min(nt_w, last_key / T::BN + 1);
+  }
 
+  // ---- K/V tiles: HBM -> swizzled LDS stage by DMA; each wave fills rows
+  // [16 w, 16 w + 16) of both tiles, one 1 KB block (RPI rows) per load,
+  // every lane fetching the logical chunk that belongs at its physical place
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
-  const int lrow = tid / T::CH;
-  const int lcol = (tid % T::CH) * 8;
-  u32x4 kreg[T::NP], vreg[T::NP];
-  auto gload = [&](int j0) {
+  constexpr int RPI = 512 / D;               // rows per 1 KB block
+  constexpr int RPW = T::BN / 4;             // tile rows filled by each wave
+  constexpr int NLD = RPW / RPI;             // blocks per wave per tile
+  const int lrow_in = lane / (64 / RPI);
+  const int lpc = lane % (64 / RPI);
+  auto kstage = [&](int s) { return smem + s * T::TILE; };
+  auto vstage = [&](int s) { return smem + (T::KSTAGES + s) * T::TILE; };
+  auto dma = [&](int t) {
+    const int j0 = t * T::BN;
+    __bf16* Ks = kstage(t % 3);
+    __bf16* Vs = vstage(t & 1);
 #pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      const uint32_t r = (uint32_t)(j0 + lrow + u * T::RPP);
-      kreg[u] = buf_load16(rk, (r * (uint32_t)p.k_ss + lcol) * 2);
-      vreg[u] = buf_load16(rv, (r * (uint32_t)p.v_ss + lcol) * 2);
-    }
-  };
-  auto lstore = [&](int st) {
-    __bf16* Ks = smem + st * T::STAGE;
-    __bf16* Vs = Ks + T::TILE;
-#pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      *(u32x4*)(Ks + swz<D>(lrow + u * T::RPP, lcol)) = kreg[u];
-      *(u32x4*)(Vs + swz<D>(lrow + u * T::RPP, lcol)) = vreg[u];
+    for (int u = 0; u < NLD; ++u) {
+      const int row = RPW * wave + RPI * u + lrow_in;
+      const int col = swz<D>(row, 8 * lpc) - row * D;                 // logical column of this chunk
+      const uint32_t r = (uint32_t)(j0 + row);
+      buf_load16_lds(rk, (r * (uint32_t)p.k_ss + col) * 2, Ks + (RPW * wave + RPI * u) * D);
+      buf_load16_lds(rv, (r * (uint32_t)p.v_ss + col) * 2, Vs + (RPW * wave + RPI * u) * D);
     }
   };
 
   f32x16 dq[T::ND];
 #pragma unroll
   for (int i = 0; i < T::ND; ++i) dq[i] = (f32x16){};
+  bf16x8 dsb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dsb[i] = (bf16x8){};
   const float c2 = p.scale_log2;
   const int prow = row_perm(l32);
   const int trG = lane >> 4;
   const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
   const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
-  const int wave_last_row = q0 + 32 * wave + 31;
   // swizzled operand addresses: per-lane bases plus constants (the chunk
   // permutation depends on the row modulo 16 only)
   int aoff[T::NC], toff[2][T::ND];
@@ -461,27 +476,34 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
     toff[1][dbk] = swz<D>(tr_row + 4, 32 * dbk + tr_col);
   }
 
-  if (ntiles > 0) {
-    gload(0);
-    wait_vmem();
-    lstore(0);
-  }
-  wait_vmem();
+  // dQ^T += K^T dS^T of tile t (K^T by transposing reads)
+  auto dq_product = [&](int t) {
+    const __bf16* Ks = kstage(t % 3);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int dbk = 0; dbk < T::ND; ++dbk) {
+        const bf16x8 ka = cat_bf16(lds_read_tr16(Ks + toff[0][dbk] + 16 * c * D),
+                                   lds_read_tr16(Ks + toff[1][dbk] + 16 * c * D));
+        dq[dbk] = mfma32(ka, dsb[c], dq[dbk]);
+      }
+  };
+
+  if (ntiles > 0) dma(0);
+  wait_vmem();   // Q, dO fragments and tile 0 have landed
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
     const int j0 = t * T::BN;
-    const bool more = t + 1 < ntiles;
-    if (more) gload(j0 + T::BN);
-
-    const bool wave_active = (q0 + 32 * wave < Lq) && (!CAUSAL || j0 <= wave_last_row + diag);
-    if (wave_active) {
-      const __bf16* Ks = smem + st * T::STAGE;
-      const __bf16* Vs = Ks + T::TILE;
-      const bool need_mask = (j0 + T::BN > Lk) || (CAUSAL && j0 + T::BN - 1 > q0 + 32 * wave + diag);
+    // tile t + 1 goes to K stage (t+1)%3 and V stage (t+1)&1, last read in
+    // iteration t - 1
+    if (t + 1 < ntiles) dma(t + 1);
+    if (t >= 1 && t - 1 < nt_w) dq_product(t - 1);
+    if (t < nt_w) {
+      const __bf16* Ks = kstage(t % 3);
+      const __bf16* Vs = vstage(t & 1);
+      const bool need_mask = (j0 + T::BN > Lk) || (CAUSAL && j0 + T::BN - 1 > wrow0 + diag);
       const int lim = CAUSAL ? min(Lk - 1, qrow + diag) : Lk - 1;
-      bf16x8 dsb[4];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -501,27 +523,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
           dsb[2 * kb2 + (i >> 3)][i & 7] = (__bf16)(pv * (dp[i] - dlt));
         }
       }
-      // dQ^T += K^T dS^T  (K^T by transposing reads)
-      const __bf16* tb[2][T::ND];
-#pragma unroll
-      for (int dbk = 0; dbk < T::ND; ++dbk) {
-        tb[0][dbk] = Ks + toff[0][dbk];
-        tb[1][dbk] = Ks + toff[1][dbk];
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int dbk = 0; dbk < T::ND; ++dbk) {
-          const bf16x8 ka = cat_bf16(lds_read_tr16(tb[0][dbk] + 16 * c * D),
-                                     lds_read_tr16(tb[1][dbk] + 16 * c * D));
-          dq[dbk] = mfma32(ka, dsb[c], dq[dbk]);
-        }
-      }
     }
-    // the other stage was last read before the previous barrier
-    if (more) lstore(st ^ 1);
+    wait_vmem();
     __syncthreads();
   }
+  if (ntiles > 0 && ntiles - 1 < nt_w) dq_product(ntiles - 1);
 
   if (qrow < Lq) {
     __bf16* dqb = (__bf16*)p.dq + (int64_t)b * p.dq_sb + (int64_t)h * p.dq_sh + (int64_t)qrow * p.dq_ss;

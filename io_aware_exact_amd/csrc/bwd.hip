@@ -154,47 +154,69 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   if (CAUSAL) qt0 = max(0, k0 - diag) / T::BQ;
   const int per_head = max(0, nqt - qt0);
   const int niter = per_head * p.group;
-  auto tile_q0 = [&](int it) { return (qt0 + it % per_head) * T::BQ; };
 
   auto stage = [&](int st) { return (__bf16*)(smem + st * T::STAGE_BYTES); };
   // Q and dO tiles go from HBM straight into the swizzled LDS stage: each
   // wave fills rows [8 w, 8 w + 8) of both tiles, one 1 KB block (RPI rows)
   // per load, every lane fetching the logical chunk that belongs at its
-  // physical position in the block.
+  // physical position in the block.  The per-lane part of every address is
+  // fixed; a tile adds its first row.  The tile to load next is tracked as
+  // (head in group, query tile) counters, so no division is needed, and the
+  // buffer resources change only when the head does.
   constexpr int RPI = 512 / D;               // rows per 1 KB block
   constexpr int NLD = 8 / RPI;               // blocks per wave per tile
   const int lrow_in = lane / (64 / RPI);     // row of this lane within a block
   const int lpc = lane % (64 / RPI);         // physical 16-byte chunk
-  float sval = 0.f;
-  auto gload = [&](int it) {
-    const int h = p.group * g + it / per_head;
-    const int q0 = tile_q0(it);
+  uint32_t qoff[NLD], dooff[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int row = 8 * (wave & 7) + RPI * u + lrow_in;                // row of the tile
+    const int col = swz<D>(row, 8 * lpc) - row * D;                     // logical column (elements)
+    qoff[u] = (uint32_t)(row * p.q_ss + col) * 2;
+    dooff[u] = (uint32_t)(row * p.do_ss + col) * 2;
+  }
+  int ld_h = 0, ld_qt = 0;                   // next tile to load: head in group, tile in head
+  __amdgpu_buffer_rsrc_t rq, rdo;
+  const float* lse_h = nullptr;
+  const float* del_h = nullptr;
+  auto set_head = [&](int hi) {
+    const int h = p.group * g + hi;
     const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     const __bf16* db = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
-    __bf16* Qs = stage((it) % T::NSTAGE);
+    rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
+    rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
+    const int64_t rowbase = ((int64_t)b * p.Hq + h) * Lq;
+    lse_h = p.lse + rowbase;
+    del_h = p.delta + rowbase;
+  };
+  if (niter > 0) set_head(0);
+  float sval = 0.f;
+  // loads the tile (ld_h, ld_qt) into stage st and advances the counters
+  auto gload = [&](int st) {
+    const int q0 = (qt0 + ld_qt) * T::BQ;
+    __bf16* Qs = stage(st);
     __bf16* Os = Qs + T::TILE;
+    const uint32_t qbase = (uint32_t)q0 * (uint32_t)p.q_ss * 2;
+    const uint32_t dobase = (uint32_t)q0 * (uint32_t)p.do_ss * 2;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int row = 8 * (wave & 7) + RPI * u + lrow_in;            // row of the tile
-      const int lc = swz<D>(row, 8 * lpc) - row * D - 8 * lpc;         // logical - physical
-      const int col = 8 * lpc + lc;                                     // logical column (elements)
-      const uint32_t r = (uint32_t)(q0 + row);
-      buf_load16_lds(rq, (r * (uint32_t)p.q_ss + col) * 2, Qs + (8 * (wave & 7) + RPI * u) * D);
-      buf_load16_lds(rdo, (r * (uint32_t)p.do_ss + col) * 2, Os + (8 * (wave & 7) + RPI * u) * D);
+      buf_load16_lds(rq, qbase + qoff[u], Qs + (8 * (wave & 7) + RPI * u) * D);
+      buf_load16_lds(rdo, dobase + dooff[u], Os + (8 * (wave & 7) + RPI * u) * D);
     }
     // threads 0..63 fetch LSE (as log2 values), threads 64..127 fetch D
     if (tid < 2 * T::BQ) {
       const int r = q0 + (tid & (T::BQ - 1));
-      const int64_t rowbase = ((int64_t)b * p.Hq + h) * Lq;
       if (tid < T::BQ) {
-        const float v = r < Lq ? p.lse[rowbase + r] : INFINITY;
+        const float v = r < Lq ? lse_h[r] : INFINITY;
         // no visible key (LSE = -inf) or padding: probabilities are zero
         sval = (v == -INFINITY) ? INFINITY : v * LOG2E;
       } else {
-        sval = r < Lq ? p.delta[rowbase + r] : 0.f;
+        sval = r < Lq ? del_h[r] : 0.f;
       }
+    }
+    if (++ld_qt == per_head) {
+      ld_qt = 0;
+      if (++ld_h < p.group) set_head(ld_h);
     }
   };
   auto lstore_stats = [&](int st) {
@@ -237,18 +259,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   wait_vmem();
   __syncthreads();
 
+  // stages of the P-wave's tile (it % 3), the dS-wave's tile ((it - 1) % 3)
+  // and the tile being loaded ((it + 1) % 3); the P-wave's query tile
+  int st_cur = 0, st_prev = 2, st_next = 1;
+  int pw_qt = 0;
+
   // Every block is computed: query blocks that see none of this key group's
   // keys (past the end, where LSE = +inf; above the causal diagonal; keys
   // past Lk) get P = 0 from the masks, so their contributions vanish, and
   // the MFMAs need no data-dependent branches.
   for (int it = 0; it <= niter; ++it) {
     const bool more = it + 1 < niter;
-    if (more) gload(it + 1);
+    if (more) gload(st_next);
     // P-wave on tile it; dS-wave on tile it - 1
     const bool work = pwave ? it < niter : it > 0;
     if (work) {
       const int t = pwave ? it : it - 1;
-      const __bf16* Qs = stage(t % T::NSTAGE);
+      const __bf16* Qs = stage(pwave ? st_cur : st_prev);
       const __bf16* Os = Qs + T::TILE;
       const float* stats = (const float*)(Os + T::TILE);
       const __bf16* As = pwave ? Qs : Os;   // A operand rows: Q for S, dO for dP
@@ -266,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       // ---- B operands of the second product: P (P-wave) or dS (dS-wave)
       bf16x8 ob[2][2];
       if (pwave) {
-        const int q0 = tile_q0(t);
+        const int q0 = (qt0 + pw_qt) * T::BQ;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int qr0 = q0 + 32 * qb;
@@ -329,12 +356,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    // gload(it + 1) filled stage (it + 1) % 3, last read by the dS-wave in
+    // gload filled stage (it + 1) % 3, last read by the dS-wave in
     // iteration it - 1; P slot it % 2 is read in iteration it + 1; both are
     // complete and visible after the wait and barrier below
-    if (more) lstore_stats((it + 1) % T::NSTAGE);
+    if (more) lstore_stats(st_next);
     wait_vmem();
     __syncthreads();
+    const int st_free = st_prev;
+    st_prev = st_cur;
+    st_cur = st_next;
+    st_next = st_free;
+    if (++pw_qt == per_head) pw_qt = 0;
   }
 
   // ---- epilogue: dV (P-wave) or dK = scale * dK (dS-wave), bf16, one key row per lane

@@ -169,6 +169,41 @@ typedef struct {
   int32_t stages;
 } fa_bwd_args;
 
+/* Packed variable-length backward (bf16), the gradient of fa_fwd_varlen.
+ * Layouts are those of fa_fwd_varlen_args: q, o, dout and dq are [Tq,Hq,d],
+ * k, v, dk and dv are [Tk,Hkv,d] (token and head strides in elements, d
+ * contiguous), lse is the forward's [Hq,Tq] fp32 (contiguous), cu_seqlens_*
+ * are int32 device arrays of nseq+1 entries, max_seqlen_* bound every
+ * sequence length, total_q = Tq and total_k = Tk.  Sequence z's gradients
+ * involve only its own rows (causal alignment per sequence); for GQA, dk and
+ * dv sum over the query heads of each kv head.  workspace: at least
+ * fa_bwd_varlen_workspace_size bytes, 256-byte aligned (D = rowsum(dO o O),
+ * [Hq,Tq] fp32).  A pointer may be NULL exactly when its tensor has no
+ * elements.  Bitwise reproducible run to run; each sequence's gradients are
+ * bitwise those of fa_bwd on that sequence alone.  Same errors as fa_bwd. */
+typedef struct {
+  fa_dtype dtype;
+  int32_t nseq, Hq, Hkv, d, max_seqlen_q, max_seqlen_k, total_q, total_k;
+  int32_t causal;
+  float softmax_scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_stride_t, q_stride_h, k_stride_t, k_stride_h, v_stride_t, v_stride_h;
+  int64_t o_stride_t, o_stride_h, do_stride_t, do_stride_h;
+  int64_t dq_stride_t, dq_stride_h, dk_stride_t, dk_stride_h, dv_stride_t, dv_stride_h;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} fa_bwd_varlen_args;
+
 /* Returns FA_ABI_VERSION. */
 int32_t fa_abi_version(void);
 
@@ -194,6 +229,12 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args* args, hipStream_t stream);
 
 /* Dense backward; see fa_bwd_args. */
 fa_status fa_bwd(const fa_bwd_args* args, hipStream_t stream);
+
+/* Workspace bytes fa_bwd_varlen needs for these arguments. */
+size_t fa_bwd_varlen_workspace_size(const fa_bwd_varlen_args* args);
+
+/* Packed variable-length backward; see fa_bwd_varlen_args. */
+fa_status fa_bwd_varlen(const fa_bwd_varlen_args* args, hipStream_t stream);
 
 /* FP8 quantiser (input preparation for the FP8 forward; "FlashAttention-3:
  * Fast and Accurate Attention with Asynchrony and Low-precision", third

@@ -228,6 +228,70 @@ fa_status check_bwd(const fa_bwd_args* a) {
   return FA_OK;
 }
 
+size_t bwd_varlen_delta_bytes(const fa_bwd_varlen_args* a) {
+  const size_t n = (size_t)(a->Hq > 0 ? a->Hq : 0) * (size_t)(a->total_q > 0 ? a->total_q : 0) * 4;
+  return align256(n);
+}
+
+fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
+  if (!a) return FA_ERR_NULL;
+  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->nseq < 0 || a->Hq < 1 || a->Hkv < 1 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0 ||
+      a->total_q < 0 || a->total_k < 0)
+    return FA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
+  if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
+  if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
+  if (!a->cu_seqlens_q || !a->cu_seqlens_k) return FA_ERR_NULL;
+  // a pointer may be NULL exactly when its tensor has no elements
+  if (a->total_q > 0 && (!a->q || !a->o || !a->dout || !a->dq || !a->lse)) return FA_ERR_NULL;
+  if (a->total_k > 0 && (!a->k || !a->v || !a->dk || !a->dv)) return FA_ERR_NULL;
+  const void* ps[8] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv};
+  for (int i = 0; i < 8; ++i)
+    if (!aligned16(ps[i])) return FA_ERR_ALIGN;
+  if (((uintptr_t)a->lse & 3u) || ((uintptr_t)a->cu_seqlens_q & 3u) || ((uintptr_t)a->cu_seqlens_k & 3u))
+    return FA_ERR_ALIGN;
+  const int64_t st[16] = {a->q_stride_t,  a->q_stride_h,  a->k_stride_t,  a->k_stride_h,
+                          a->v_stride_t,  a->v_stride_h,  a->o_stride_t,  a->o_stride_h,
+                          a->do_stride_t, a->do_stride_h, a->dq_stride_t, a->dq_stride_h,
+                          a->dk_stride_t, a->dk_stride_h, a->dv_stride_t, a->dv_stride_h};
+  for (int i = 0; i < 16; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_ALIGN;
+  const int64_t qtiles = ((int64_t)a->max_seqlen_q + 127) / 128, ktiles = ((int64_t)a->max_seqlen_k + 127) / 128;
+  if (qtiles * a->Hq * (int64_t)a->nseq > 0x7fffffffLL || ktiles * a->Hkv * (int64_t)a->nseq > 0x7fffffffLL)
+    return FA_ERR_SHAPE;
+  if ((int64_t)a->total_q * a->Hq > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
+  if (!fits32(a->max_seqlen_q, a->q_stride_t, 2) || !fits32(a->max_seqlen_q, a->do_stride_t, 2) ||
+      !fits32(a->max_seqlen_k, a->k_stride_t, 2) || !fits32(a->max_seqlen_k, a->v_stride_t, 2))
+    return FA_ERR_SHAPE;
+  const size_t need = bwd_varlen_delta_bytes(a);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
+  // outputs must not overlap each other, the inputs or the workspace
+  const int64_t Tq = a->total_q, Tk = a->total_k, Hq = a->Hq, Hkv = a->Hkv, d = a->d;
+  const Span in[8] = {
+      span4(a->q, 1, Tq, Hq, d, 0, a->q_stride_t, a->q_stride_h, 2),
+      span4(a->k, 1, Tk, Hkv, d, 0, a->k_stride_t, a->k_stride_h, 2),
+      span4(a->v, 1, Tk, Hkv, d, 0, a->v_stride_t, a->v_stride_h, 2),
+      span4(a->o, 1, Tq, Hq, d, 0, a->o_stride_t, a->o_stride_h, 2),
+      span4(a->dout, 1, Tq, Hq, d, 0, a->do_stride_t, a->do_stride_h, 2),
+      {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)(Hq * Tq * 4)},
+      {(uintptr_t)a->cu_seqlens_q, (uintptr_t)a->cu_seqlens_q + (uintptr_t)(a->nseq + 1) * 4},
+      {(uintptr_t)a->cu_seqlens_k, (uintptr_t)a->cu_seqlens_k + (uintptr_t)(a->nseq + 1) * 4}};
+  const Span out[4] = {
+      span4(a->dq, 1, Tq, Hq, d, 0, a->dq_stride_t, a->dq_stride_h, 2),
+      span4(a->dk, 1, Tk, Hkv, d, 0, a->dk_stride_t, a->dk_stride_h, 2),
+      span4(a->dv, 1, Tk, Hkv, d, 0, a->dv_stride_t, a->dv_stride_h, 2),
+      {(uintptr_t)a->workspace, (uintptr_t)a->workspace + need}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(out[i], in[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
 // The tiled bf16 forward.  At d = 128 the two-group kernel (one group's
 // softmax runs while the other group's MFMAs run) is faster; at d = 64 the
 // softmax costs about twice the matrix work per tile, so alternating the
@@ -385,7 +449,56 @@ fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
   p.scale = a->softmax_scale;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
   const int stages = a->stages == FA_BWD_ALL ? (FA_BWD_PREPROCESS | FA_BWD_DKDV | FA_BWD_DQ) : a->stages;
-  return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, stages, stream));
+  return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, false, stages, stream));
+}
+
+size_t fa_bwd_varlen_workspace_size(const fa_bwd_varlen_args* a) {
+  if (!a) return 0;
+  return bwd_varlen_delta_bytes(a);
+}
+
+fa_status fa_bwd_varlen(const fa_bwd_varlen_args* a, hipStream_t stream) {
+  const fa_status s = check_bwd_varlen(a);
+  if (s != FA_OK) return s;
+  if (a->nseq == 0 || a->total_q == 0 || a->total_k == 0) {
+    // no query rows or no keys anywhere: the gradients are zero
+    if (a->total_q > 0 &&
+        launch_zero_bf16(a->dq, 1, a->total_q, a->Hq, a->d, 0, a->dq_stride_t, a->dq_stride_h, stream) !=
+            hipSuccess)
+      return FA_ERR_HIP;
+    if (a->total_k > 0) {
+      if (launch_zero_bf16(a->dk, 1, a->total_k, a->Hkv, a->d, 0, a->dk_stride_t, a->dk_stride_h, stream) !=
+              hipSuccess ||
+          launch_zero_bf16(a->dv, 1, a->total_k, a->Hkv, a->d, 0, a->dv_stride_t, a->dv_stride_h, stream) !=
+              hipSuccess)
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+  }
+  BwdParams p = {};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.dout = a->dout;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.lse = a->lse;
+  p.delta = (float*)a->workspace;
+  p.dq_acc = nullptr;
+  p.q_ss = a->q_stride_t; p.q_sh = a->q_stride_h;
+  p.k_ss = a->k_stride_t; p.k_sh = a->k_stride_h;
+  p.v_ss = a->v_stride_t; p.v_sh = a->v_stride_h;
+  p.o_ss = a->o_stride_t; p.o_sh = a->o_stride_h;
+  p.do_ss = a->do_stride_t; p.do_sh = a->do_stride_h;
+  p.dq_ss = a->dq_stride_t; p.dq_sh = a->dq_stride_h;
+  p.dk_ss = a->dk_stride_t; p.dk_sh = a->dk_stride_h;
+  p.dv_ss = a->dv_stride_t; p.dv_sh = a->dv_stride_h;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.total_q = a->total_q;
+  p.B = a->nseq; p.Sq = a->max_seqlen_q; p.Sk = a->max_seqlen_k; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.causal = a->causal != 0;
+  p.scale = a->softmax_scale;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  const int stages = FA_BWD_PREPROCESS | FA_BWD_DKDV | FA_BWD_DQ;
+  return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, true, stages, stream));
 }
 
 fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int32_t B, int32_t S,

@@ -112,17 +112,38 @@ struct DkdvTile {
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES + 2 * PEX_SLOT;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvTile<D>;
   __shared__ __attribute__((aligned(16))) char smem[T::LDS_BYTES];
 
-  const int nkt = (p.Sk + T::BKV - 1) / T::BKV;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = L % nkt;
-  const int rest = L / nkt;
-  const int g = rest % p.Hkv;
-  const int b = rest / p.Hkv;
+  // Dense: consecutive key tiles of one kv head share an XCD.  Packed
+  // sequences: key-tile-major (every sequence and kv head at one key tile
+  // index together) on the hardware's round-robin over the XCDs.
+  int kt, g, b;
+  if (VARLEN) {
+    const int gb = p.Hkv * p.B;
+    kt = blockIdx.x / gb;
+    g = (blockIdx.x % gb) % p.Hkv;
+    b = (blockIdx.x % gb) / p.Hkv;
+  } else {
+    const int nkt = (p.Sk + T::BKV - 1) / T::BKV;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    kt = L % nkt;
+    const int rest = L / nkt;
+    g = rest % p.Hkv;
+    b = rest / p.Hkv;
+  }
+  int Lq = p.Sq, Lk = p.Sk;
+  int64_t qtok = 0, ktok = 0;
+  if (VARLEN) {
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    Lq = p.cu_q[b + 1] - qs;
+    Lk = p.cu_k[b + 1] - ks;
+    qtok = qs;
+    ktok = ks;
+  }
+  if (kt * T::BKV >= Lk) return;   // workgroup-uniform: past this sequence's keys
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -131,15 +152,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   const bool pwave = wave < 4;              // role: P-wave (else dS-wave)
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int Lq = p.Sq, Lk = p.Sk;
   const int diag = Lk - Lq;
   const int k0 = kt * T::BKV;
   const int kw0 = k0 + 32 * kgrp;           // first key of this key group
   const int key = kw0 + l32;                // key owned by this lane (C column)
 
   // ---- resident operand: K (P-wave) or V (dS-wave), B operand of Q K^T / dO V^T
-  const __bf16* kvb = pwave ? (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh
-                            : (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  const __bf16* kvb = pwave ? (const __bf16*)p.k + (VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh
+                            : (const __bf16*)p.v + (VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
   const int64_t kv_ss = pwave ? p.k_ss : p.v_ss;
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kvb, (uint32_t)((int64_t)Lk * kv_ss * 2));
   bf16x8 bf[T::NC];
@@ -181,11 +201,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   const float* del_h = nullptr;
   auto set_head = [&](int hi) {
     const int h = p.group * g + hi;
-    const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    const __bf16* db = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
+    const __bf16* qb = (const __bf16*)p.q + (VARLEN ? qtok * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+    const __bf16* db = (const __bf16*)p.dout + (VARLEN ? qtok * p.do_ss : (int64_t)b * p.do_sb) + (int64_t)h * p.do_sh;
     rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
     rdo = make_rsrc(db, (uint32_t)((int64_t)Lq * p.do_ss * 2));
-    const int64_t rowbase = ((int64_t)b * p.Hq + h) * Lq;
+    // LSE and D: [B, Hq, Sq] dense, [Hq, Tq] packed
+    const int64_t rowbase = VARLEN ? (int64_t)h * p.total_q + qtok : ((int64_t)b * p.Hq + h) * Lq;
     lse_h = p.lse + rowbase;
     del_h = p.delta + rowbase;
   };
@@ -371,8 +392,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // ---- epilogue: dV (P-wave) or dK = scale * dK (dS-wave), bf16, one key row per lane
   if (key < Lk) {
-    __bf16* out = pwave ? (__bf16*)p.dv + (int64_t)b * p.dv_sb + (int64_t)g * p.dv_sh + (int64_t)key * p.dv_ss
-                        : (__bf16*)p.dk + (int64_t)b * p.dk_sb + (int64_t)g * p.dk_sh + (int64_t)key * p.dk_ss;
+    __bf16* out = pwave ? (__bf16*)p.dv + (VARLEN ? ktok * p.dv_ss : (int64_t)b * p.dv_sb) + (int64_t)g * p.dv_sh +
+                              (int64_t)key * p.dv_ss
+                        : (__bf16*)p.dk + (VARLEN ? ktok * p.dk_ss : (int64_t)b * p.dk_sb) + (int64_t)g * p.dk_sh +
+                              (int64_t)key * p.dk_ss;
     const float f = pwave ? 1.f : p.scale;
 #pragma unroll
     for (int dbk = 0; dbk < T::ND; ++dbk)
@@ -404,22 +427,42 @@ struct DqTile {
   static constexpr int VSTAGES = 2;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   using T = DqTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[(T::KSTAGES + T::VSTAGES) * T::TILE];
 
+  // Dense: consecutive query tiles of one head share an XCD.  Packed
+  // sequences: query-tile-major on the hardware's round-robin.  Causal:
+  // heaviest tiles first.
   const int nmt = (p.Sq + T::BM - 1) / T::BM;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  int mt = L % nmt;
-  const int rest = L / nmt;
-  const int h = rest % p.Hq;
-  const int b = rest / p.Hq;
+  int mt, h, b;
+  if (VARLEN) {
+    const int bh = p.Hq * p.B;
+    mt = blockIdx.x / bh;
+    h = (blockIdx.x % bh) % p.Hq;
+    b = (blockIdx.x % bh) / p.Hq;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    mt = L % nmt;
+    const int rest = L / nmt;
+    h = rest % p.Hq;
+    b = rest / p.Hq;
+  }
   if (CAUSAL) mt = nmt - 1 - mt;
   const int g = h / p.group;
-  const int Lq = p.Sq, Lk = p.Sk;
+  int Lq = p.Sq, Lk = p.Sk;
+  int64_t qtok = 0, ktok = 0;
+  if (VARLEN) {
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    Lq = p.cu_q[b + 1] - qs;
+    Lk = p.cu_k[b + 1] - ks;
+    qtok = qs;
+    ktok = ks;
+  }
   const int diag = Lk - Lq;
   const int q0 = mt * T::BM;
+  if (q0 >= Lq) return;   // workgroup-uniform: past this sequence's rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -428,10 +471,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   const int hh = lane >> 5;
   const int qrow = q0 + 32 * wave + l32;
 
-  const __bf16* qb = (const __bf16*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-  const __bf16* dob = (const __bf16*)p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
-  const __bf16* kb = (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
-  const __bf16* vb = (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  const __bf16* qb = (const __bf16*)p.q + (VARLEN ? qtok * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+  const __bf16* dob = (const __bf16*)p.dout + (VARLEN ? qtok * p.do_ss : (int64_t)b * p.do_sb) + (int64_t)h * p.do_sh;
+  const __bf16* kb = (const __bf16*)p.k + (VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
 
   // ---- resident Q^T, dO^T fragments (B operands), LSE and D of this row
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)((int64_t)Lq * p.q_ss * 2));
@@ -444,9 +487,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   }
   float lse2 = INFINITY, dlt = 0.f;
   if (qrow < Lq) {
-    const float v = p.lse[((int64_t)b * p.Hq + h) * Lq + qrow];
+    // LSE and D: [B, Hq, Sq] dense, [Hq, Tq] packed
+    const int64_t ri = (VARLEN ? (int64_t)h * p.total_q + qtok : ((int64_t)b * p.Hq + h) * Lq) + qrow;
+    const float v = p.lse[ri];
     lse2 = (v == -INFINITY) ? INFINITY : v * LOG2E;
-    dlt = p.delta[((int64_t)b * p.Hq + h) * Lq + qrow];
+    dlt = p.delta[ri];
   }
 
   int kend = Lk;
@@ -562,7 +607,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   if (ntiles > 0 && ntiles - 1 < nt_w) dq_product(ntiles - 1);
 
   if (qrow < Lq) {
-    __bf16* dqb = (__bf16*)p.dq + (int64_t)b * p.dq_sb + (int64_t)h * p.dq_sh + (int64_t)qrow * p.dq_ss;
+    __bf16* dqb = (__bf16*)p.dq + (VARLEN ? qtok * p.dq_ss : (int64_t)b * p.dq_sb) + (int64_t)h * p.dq_sh +
+                  (int64_t)qrow * p.dq_ss;
 #pragma unroll
     for (int dbk = 0; dbk < T::ND; ++dbk)
 #pragma unroll
@@ -590,28 +636,35 @@ __global__ __launch_bounds__(256) void zero_bf16_kernel(__bf16* ptr, int64_t S, 
   *(u32x4*)(ptr + b * sb + s * ss + h * sh + c) = (u32x4){0u, 0u, 0u, 0u};
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd(const BwdParams& p, int stages, hipStream_t stream) {
   if (stages & 1) {
+    // packed rows [Tq, Hq, d] are the dense layout with B = 1, Sq = Tq, and D
+    // [Hq, Tq] is its [B, Hq, Sq]
+    BwdParams pp = p;
+    if (VARLEN) {
+      pp.B = 1;
+      pp.Sq = p.total_q;
+    }
     constexpr int RPB = NTHREADS / (D / 8);
-    const long rows = (long)p.B * p.Sq * p.Hq;
+    const long rows = (long)pp.B * pp.Sq * pp.Hq;
     const long nblk = (rows + RPB - 1) / RPB;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, pp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((stages & 2) && p.Sk > 0) {
     const long nblk = (long)((p.Sk + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV) * p.Hkv * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(DkdvTile<D>::NT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(DkdvTile<D>::NT), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 4) {
     const long nblk = (long)((p.Sq + DqTile<D>::BM - 1) / DqTile<D>::BM) * p.Hq * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -619,9 +672,14 @@ hipError_t launch_bwd(const BwdParams& p, int stages, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, int stages, hipStream_t stream) {
-  if (d == 128) return causal ? launch_bwd<128, true>(p, stages, stream) : launch_bwd<128, false>(p, stages, stream);
-  return causal ? launch_bwd<64, true>(p, stages, stream) : launch_bwd<64, false>(p, stages, stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool varlen, int stages,
+                           hipStream_t stream) {
+  if (d == 128) {
+    if (causal) return varlen ? launch_bwd<128, true, true>(p, stages, stream) : launch_bwd<128, true, false>(p, stages, stream);
+    return varlen ? launch_bwd<128, false, true>(p, stages, stream) : launch_bwd<128, false, false>(p, stages, stream);
+  }
+  if (causal) return varlen ? launch_bwd<64, true, true>(p, stages, stream) : launch_bwd<64, true, false>(p, stages, stream);
+  return varlen ? launch_bwd<64, false, true>(p, stages, stream) : launch_bwd<64, false, false>(p, stages, stream);
 }
 
 hipError_t launch_zero_bf16(void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb,

@@ -45,6 +45,9 @@ struct BwdParams {
   int64_t dq_sb, dq_ss, dq_sh;
   int64_t dk_sb, dk_ss, dk_sh;
   int64_t dv_sb, dv_ss, dv_sh;
+  const int* cu_q;            // packed sequences: token offsets [B + 1] (else NULL)
+  const int* cu_k;
+  int total_q;                // packed sequences: Tq (LSE and D are [Hq, Tq])
   int B, Sq, Sk, Hq, Hkv, group;
   int causal;
   float scale;
@@ -82,7 +85,8 @@ hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t s
                                int H, int d, int per_tensor, void* codes, float* scales,
                                hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, int stages, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool varlen, int stages,
+                           hipStream_t stream);
 // Zero a bf16 [B,S,H,d] tensor with element strides (d contiguous).
 hipError_t launch_zero_bf16(void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb,
                             int64_t ss, int64_t sh, hipStream_t stream);

@@ -71,13 +71,35 @@ class BwdArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("stages", ctypes.c_int32)]
 
 
+class BwdVarlenArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("nseq", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+                ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
+                ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
+                ("o_stride_t", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
+                ("do_stride_t", ctypes.c_int64), ("do_stride_h", ctypes.c_int64),
+                ("dq_stride_t", ctypes.c_int64), ("dq_stride_h", ctypes.c_int64),
+                ("dk_stride_t", ctypes.c_int64), ("dk_stride_h", ctypes.c_int64),
+                ("dv_stride_t", ctypes.c_int64), ("dv_stride_h", ctypes.c_int64),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 
 
 # Every symbol include/fa.h declares.
 EXPORTS = ["fa_abi_version", "fa_status_string", "fa_fwd_workspace_size",
            "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
-           "fa_quantize_fp8"]
+           "fa_bwd_varlen_workspace_size", "fa_bwd_varlen", "fa_quantize_fp8"]
 
 _lib = None
 
@@ -104,6 +126,10 @@ def lib():
         L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), vp]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.POINTER(BwdArgs), vp]
+        L.fa_bwd_varlen_workspace_size.restype = ctypes.c_size_t
+        L.fa_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(BwdVarlenArgs)]
+        L.fa_bwd_varlen.restype = ctypes.c_int
+        L.fa_bwd_varlen.argtypes = [ctypes.POINTER(BwdVarlenArgs), vp]
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         L.fa_quantize_fp8.restype = ctypes.c_int
         L.fa_quantize_fp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
@@ -230,6 +256,47 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, out=None, workspace=Non
     return dq, dk, dv
 
 
+def bwd_varlen_args(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
+                    max_seqlen_q, max_seqlen_k, causal, scale, workspace=None):
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    for x in (q, k, v, o, dout, dq, dk, dv):
+        assert x.dim() == 3 and x.stride(2) == 1, "packed [T,H,d] with d contiguous"
+    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return BwdVarlenArgs(dt, cu_seqlens_q.numel() - 1, Hq, Hkv, d, int(max_seqlen_q),
+                         int(max_seqlen_k), Tq, Tk, int(bool(causal)), _scale(d, scale),
+                         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                         o.stride(0), o.stride(1), dout.stride(0), dout.stride(1),
+                         dq.stride(0), dq.stride(1), dk.stride(0), dk.stride(1),
+                         dv.stride(0), dv.stride(1), cu_seqlens_q.data_ptr(),
+                         cu_seqlens_k.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes)
+
+
+def bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+               causal=False, scale=None, out=None, workspace=None):
+    """Packed variable-length backward.  q, o, dout [Tq,Hq,d], k/v [Tk,Hkv,d]
+    bf16, lse [Hq,Tq] from fwd_varlen.  Returns (dq, dk, dv) bf16."""
+    if out is None:
+        out = (torch.empty(q.shape, dtype=torch.bfloat16, device=q.device),
+               torch.empty(k.shape, dtype=torch.bfloat16, device=k.device),
+               torch.empty(v.shape, dtype=torch.bfloat16, device=v.device))
+    dq, dk, dv = out
+    if workspace is None:
+        a = bwd_varlen_args(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
+                            max_seqlen_q, max_seqlen_k, causal, scale)
+        nbytes = lib().fa_bwd_varlen_workspace_size(ctypes.byref(a))
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q.device)
+    a = bwd_varlen_args(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
+                        max_seqlen_q, max_seqlen_k, causal, scale, workspace)
+    _check("fa_bwd_varlen", lib().fa_bwd_varlen(ctypes.byref(a), _stream()))
+    return dq, dk, dv
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, causal, scale):
@@ -297,8 +364,26 @@ def attention_decode(q, k, v, causal=False, scale=None):
     return fwd_decode(q, k, v, causal, scale)[0]
 
 
+class _AttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):
+        o, lse = fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu_q, cu_k)
+        ctx.meta = (max_q, max_k, causal, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, causal, scale = ctx.meta
+        dq, dk, dv = bwd_varlen(q, k, v, o, do.contiguous(), lse, cu_q, cu_k, max_q, max_k,
+                                causal, scale)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                      causal=False, scale=None):
-    """Packed variable-length forward; returns o [Tq,Hq,d]."""
-    return fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                      causal, scale)[0]
+    """Packed variable-length attention with autograd: q [Tq,Hq,d], k/v
+    [Tk,Hkv,d] bf16, cu_seqlens_* int32 [nseq+1]; returns o [Tq,Hq,d]."""
+    return _AttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, causal, scale)

@@ -221,3 +221,41 @@ def attention_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal=False,
             o[q0 + pos, h, :] = res[0]
             lse[h, q0 + pos] = res[1]
     return o, lse
+
+
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, causal=False,
+                         scale=None, seqs=None):
+    """Packed variable-length forward + backward: the dense backward run on
+    each packed sequence alone (sequence z sees only its own keys, causal
+    alignment per sequence).  q, dout [Tq,Hq,d], k/v [Tk,Hkv,d] ->
+    (o [Tq,Hq,d], lse [Hq,Tq], dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]);
+    dk/dv are summed over each kv head's query heads.  `seqs` restricts the
+    work to some sequences; the other rows are left at zero (lse: nan)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    o = np.zeros((Tq, Hq, d))
+    lse = np.full((Hq, Tq), np.nan)
+    dq = np.zeros((Tq, Hq, d))
+    dk = np.zeros((Tk, Hkv, d))
+    dv = np.zeros((Tk, Hkv, d))
+    nseq = len(cq) - 1
+    for z in (range(nseq) if seqs is None else seqs):
+        q0, q1, k0, k1 = cq[z], cq[z + 1], ck[z], ck[z + 1]
+        if q1 == q0:
+            continue        # no query rows: every gradient of this sequence is zero
+        if k1 == k0:
+            # no keys: the rows attend to nothing, O = 0, LSE = -inf, dQ = 0
+            lse[:, q0:q1] = -np.inf
+            continue
+        oz, lz, dqz, dkz, dvz = attention_bwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1],
+                                              dout[None, q0:q1], causal, scale)
+        o[q0:q1] = oz[0]
+        lse[:, q0:q1] = lz[0]
+        dq[q0:q1] = dqz[0]
+        dk[k0:k1] = dkz[0]
+        dv[k0:k1] = dvz[0]
+    return o, lse, dq, dk, dv
+

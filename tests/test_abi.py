@@ -117,3 +117,39 @@ def test_fwd_varlen_rejects_fp32():
                          FAKE + (2 << 24), FAKE + (3 << 24), 128, 64, 128, 64, 128, 64, 128, 64,
                          FAKE + (4 << 24), FAKE + (5 << 24), FAKE + (6 << 24))
     assert fa.lib().fa_fwd_varlen(ctypes.byref(a), None) == 4
+
+
+def bwd_varlen_args(**kw):
+    base = dict(dtype=0, nseq=2, Hq=2, Hkv=2, d=64, mq=16, mk=16, Tq=32, Tk=32, causal=0,
+                scale=0.125, ws=FAKE + (12 << 24), ws_bytes=1 << 20)
+    base.update(kw)
+    ptr = {n: FAKE + (i << 24) for i, n in enumerate(
+        ["q", "k", "v", "o", "do", "dq", "dk", "dv", "cuq", "cuk", "lse"])}
+    ptr.update({n: kw[n] for n in ptr if n in kw})
+    st = base["Hq"] * base["d"]
+    return fa.BwdVarlenArgs(base["dtype"], base["nseq"], base["Hq"], base["Hkv"], base["d"],
+                            base["mq"], base["mk"], base["Tq"], base["Tk"], base["causal"],
+                            base["scale"], ptr["q"], ptr["k"], ptr["v"], ptr["o"], ptr["do"],
+                            ptr["dq"], ptr["dk"], ptr["dv"], *([st, base["d"]] * 8),
+                            ptr["cuq"], ptr["cuk"], ptr["lse"], base["ws"], base["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=1), 4), (dict(d=96), 3), (dict(Hq=3, Hkv=2), 5), (dict(nseq=-1), 2),
+    (dict(scale=0.0), 10), (dict(scale=float("inf")), 10),
+    (dict(cuq=0), 1), (dict(dq=0), 1), (dict(lse=0), 1),
+    (dict(dk=FAKE + (6 << 24) + 2), 6), (dict(ws=FAKE + (12 << 24) + 64), 6),
+    (dict(ws=0), 7), (dict(ws_bytes=16), 7),
+    (dict(dq=FAKE + 64), 8),               # dq overlaps q
+])
+def test_bwd_varlen_rejects(kw, status):
+    a = bwd_varlen_args(**kw)
+    assert fa.lib().fa_bwd_varlen(ctypes.byref(a), None) == status
+
+
+def test_bwd_varlen_null_and_workspace_query():
+    L = fa.lib()
+    assert L.fa_bwd_varlen(None, None) == 1
+    assert L.fa_bwd_varlen_workspace_size(None) == 0
+    a = bwd_varlen_args(Hq=4, Hkv=2, Tq=1000)
+    assert L.fa_bwd_varlen_workspace_size(ctypes.byref(a)) == 4 * 1000 * 4 // 256 * 256 + 256 * (4 * 1000 * 4 % 256 != 0)

@@ -348,3 +348,50 @@ def test_bwd_selected_slices():
 
 def test_num_threads_positive():
     assert oracle.num_threads() >= 1
+
+
+def test_varlen_bwd_matches_block_diagonal_autograd():
+    """The packed backward oracle (the dense backward run per sequence) against
+    fp64 autograd through the whole packed batch with a block-diagonal mask,
+    including an empty sequence, one with no keys and one with no queries."""
+    lens_q = [5, 0, 17, 9, 3, 0]
+    lens_k = [7, 4, 17, 9, 0, 0]
+    cq, ck = [0], [0]
+    for a, b in zip(lens_q, lens_k):
+        cq.append(cq[-1] + a)
+        ck.append(ck[-1] + b)
+    Tq, Tk = cq[-1], ck[-1]
+    q = rnd((Tq, 4, 8), 41)
+    k = rnd((Tk, 2, 8), 42)
+    v = rnd((Tk, 2, 8), 43)
+    do = rnd((Tq, 4, 8), 44)
+    for causal in (False, True):
+        o, lse, dq, dk, dv = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, causal, 0.3)
+        seq_q = np.repeat(np.arange(len(lens_q)), lens_q)
+        seq_k = np.repeat(np.arange(len(lens_k)), lens_k)
+        pos_q = np.concatenate([np.arange(L) for L in lens_q])
+        pos_k = np.concatenate([np.arange(L) for L in lens_k])
+        allowed = seq_q[:, None] == seq_k[None, :]
+        if causal:
+            diag = np.array(lens_k)[seq_q] - np.array(lens_q)[seq_q]
+            allowed &= pos_k[None, :] <= pos_q[:, None] + diag[:, None]
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        kr = tk.repeat_interleave(2, dim=1)
+        vr = tv.repeat_interleave(2, dim=1)
+        s = torch.einsum("ihd,jhd->hij", tq, kr) * 0.3
+        s = s.masked_fill(~torch.from_numpy(allowed)[None], float("-inf"))
+        m = torch.amax(s, -1, keepdim=True)
+        m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+        e = torch.exp(s - m)
+        den = e.sum(-1, keepdim=True)
+        p = e / torch.where(den > 0, den, torch.ones_like(den))
+        o_ref = torch.einsum("hij,jhd->ihd", p, vr)
+        o_ref.backward(torch.from_numpy(do))
+        rows = seq_q >= 0
+        np.testing.assert_allclose(o[rows], o_ref.detach().numpy()[rows], atol=1e-12)
+        np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+        # rows with no visible key: LSE = -inf
+        no_key = ~allowed.any(1)
+        assert np.all(np.isneginf(lse[:, no_key]))

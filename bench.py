@@ -106,14 +106,22 @@ def sampled_check(q, k, v, o, lse, causal):
     return float(np.abs(o_got - o_ref).max()), float(np.abs(l_got - lse_ref).max())
 
 
-def time_calls(fn, reps, warmup=2):
-    """Average ms of fn() over reps back-to-back calls on the current stream."""
+def time_calls(fn, reps, warmup=2, warm_ms=100.0):
+    """Average ms of fn() over reps back-to-back calls on the current stream,
+    after at least `warmup` calls and about `warm_ms` of untimed work (the
+    first launches on fresh buffers run slower)."""
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(warmup):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = e0.elapsed_time(e1) / max(warmup, 1)
+    for _ in range(min(int(warm_ms / max(per_call, 1e-3)), 200)):
+        fn()
+    torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
         fn()
@@ -157,24 +165,36 @@ def leg_decode(reps):
 
 
 def leg_varlen(reps):
-    """Packed varlen + GQA forward: 16 sequences, lengths uniform on
-    [128, 32768] (seed 3000), Hq=32, Hkv=8, d=128, causal."""
+    """Packed varlen + GQA forward and backward: 16 sequences, lengths uniform
+    on [128, 32768] (seed 3000), Hq=32, Hkv=8, d=128, causal; dO ~ N(0,1)
+    (seed 3002).  Gradient and workspace buffers are allocated before timing."""
     from io_aware_exact_amd import fa, inputs
     lens = inputs.varlen_lengths(16, 128, 32768, 3000)
     Hq, Hkv, d = 32, 8, 128
     q, k, v = inputs.packed_qkv(lens, lens, Hq, Hkv, d, 3001, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3002)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
     cu = inputs.cu_seqlens(lens, device="cuda")
-    T = sum(lens)
+    T, mx = sum(lens), max(lens)
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
-    ms = time_calls(lambda: fa.fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), True,
-                                          out=o, lse=lse), reps)
+    ms = time_calls(lambda: fa.fwd_varlen(q, k, v, cu, cu, mx, mx, True, out=o, lse=lse), reps)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    a = fa.bwd_varlen_args(q, k, v, o, do, lse, *grads, cu, cu, mx, mx, True, None)
+    ws = torch.empty(max(int(fa.lib().fa_bwd_varlen_workspace_size(ctypes.byref(a))), 1),
+                     dtype=torch.uint8, device="cuda")
+    ms_b = time_calls(lambda: fa.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, True,
+                                            out=grads, workspace=ws), reps)
     pairs = sum(L * (L + 1) // 2 for L in lens)
     flops_half = sum(2.0 * Hq * d * L * L for L in lens)
     return {"workload": "varlen 16 seqs U[128,32768] Hq=32 Hkv=8 d=128 causal",
             "total_tokens": T, "ms": round(ms, 3),
             "tflops": round(flops_half / ms / 1e9, 2),
-            "tflops_exact_pairs": round(4.0 * Hq * d * pairs / ms / 1e9, 2)}
+            "tflops_exact_pairs": round(4.0 * Hq * d * pairs / ms / 1e9, 2),
+            "bwd_ms": round(ms_b, 3),
+            "fwd_bwd_tflops": round(3.5 * flops_half / (ms + ms_b) / 1e9, 2),
+            "fwd_bwd_tflops_exact_pairs": round(14.0 * Hq * d * pairs / (ms + ms_b) / 1e9, 2)}
 
 
 def leg_fp8(reps):
@@ -365,7 +385,7 @@ def main():
         "fwd": {"tflops": tf(ff, ms_fwd), "ms": round(ms_fwd, 4),
                 "frac_of_peak": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4)},
         "kernels": kernels,
-        "roofline": {"kernel": "bwd_dkdv_kernel<128,false>", "bound": "mfma",
+        "roofline": {"kernel": "bwd_dkdv_kernel<128,false,false>", "bound": "mfma",
                      "achieved": round(dk_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dk_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile("bwd_dkdv_b2_h16_s8192_d128", BWD_SOURCES)},

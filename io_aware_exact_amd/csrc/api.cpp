@@ -11,6 +11,13 @@ namespace {
 
 constexpr int kBM = 128;   // query rows per forward workgroup
 
+// Workgroups of a packed-sequence grid (varlen_order): rows padded to a
+// multiple of 8, tiles (per query head of a kv group) to whole runs of at
+// most 8.  Holds for every kernel's run length.
+static int64_t varlen_grid_bound(int64_t rows, int64_t tiles, int64_t group) {
+  return (rows + 7) / 8 * 8 * (tiles + 8) * group;
+}
+
 struct Span {
   uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
 };
@@ -157,7 +164,7 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
   for (int i = 0; i < 8; ++i)
     if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->max_seqlen_q + kBM - 1) / kBM;
-  if (tiles * a->Hq * (int64_t)a->nseq > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (varlen_grid_bound((int64_t)a->Hkv * a->nseq, tiles, a->Hq / a->Hkv) > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!fits32(a->max_seqlen_q, a->q_stride_t, 2) || !fits32(a->max_seqlen_q, a->o_stride_t, 2) ||
       !fits32(a->max_seqlen_k, a->k_stride_t, 2) || !fits32(a->max_seqlen_k, a->v_stride_t, 2))
     return FA_ERR_SHAPE;
@@ -258,7 +265,8 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
   for (int i = 0; i < 16; ++i)
     if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_ALIGN;
   const int64_t qtiles = ((int64_t)a->max_seqlen_q + 127) / 128, ktiles = ((int64_t)a->max_seqlen_k + 127) / 128;
-  if (qtiles * a->Hq * (int64_t)a->nseq > 0x7fffffffLL || ktiles * a->Hkv * (int64_t)a->nseq > 0x7fffffffLL)
+  if (varlen_grid_bound((int64_t)a->Hkv * a->nseq, qtiles, a->Hq / a->Hkv) > 0x7fffffffLL ||
+      varlen_grid_bound((int64_t)a->Hkv * a->nseq, ktiles, 1) > 0x7fffffffLL)
     return FA_ERR_SHAPE;
   if ((int64_t)a->total_q * a->Hq > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
   if (!fits32(a->max_seqlen_q, a->q_stride_t, 2) || !fits32(a->max_seqlen_q, a->do_stride_t, 2) ||

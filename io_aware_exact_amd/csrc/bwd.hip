@@ -55,12 +55,6 @@ __device__ __forceinline__ int perm_row_of_reg(int i, int hh) {
   return (i < 8) ? 8 * hh + i : 16 + 8 * hh + (i - 8);
 }
 
-__device__ __forceinline__ int xcd_remap(int w, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int x = w & 7, s = w >> 3;
-  return x * q + (x < r ? x : r) + s;
-}
-
 // ---------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic (fp32), written to delta[b][h][i].
 template <int D>
@@ -118,14 +112,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[T::LDS_BYTES];
 
   // Dense: consecutive key tiles of one kv head share an XCD.  Packed
-  // sequences: key-tile-major (every sequence and kv head at one key tile
-  // index together) on the hardware's round-robin over the XCDs.
+  // sequences: runs of key tiles of one (sequence, kv head) per XCD, lowest
+  // key tiles (the heaviest when causal) first.
   int kt, g, b;
   if (VARLEN) {
-    const int gb = p.Hkv * p.B;
-    kt = blockIdx.x / gb;
-    g = (blockIdx.x % gb) % p.Hkv;
-    b = (blockIdx.x % gb) / p.Hkv;
+    int row;
+    if (!varlen_order(blockIdx.x, p.Hkv * p.B, kDkdvVarlenRun, row, kt)) return;
+    g = row % p.Hkv;
+    b = row / p.Hkv;
   } else {
     const int nkt = (p.Sk + T::BKV - 1) / T::BKV;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -433,15 +427,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 smem[(T::KSTAGES + T::VSTAGES) * T::TILE];
 
   // Dense: consecutive query tiles of one head share an XCD.  Packed
-  // sequences: query-tile-major on the hardware's round-robin.  Causal:
-  // heaviest tiles first.
+  // sequences: runs of query tiles of the query heads of one (sequence, kv
+  // head) per XCD, which all read that K/V.  Causal: heaviest tiles first.
   const int nmt = (p.Sq + T::BM - 1) / T::BM;
   int mt, h, b;
   if (VARLEN) {
-    const int bh = p.Hq * p.B;
-    mt = blockIdx.x / bh;
-    h = (blockIdx.x % bh) % p.Hq;
-    b = (blockIdx.x % bh) / p.Hq;
+    int row, t;
+    if (!varlen_order(blockIdx.x, p.Hkv * p.B, kDqVarlenRun * p.group, row, t)) return;
+    mt = t / p.group;
+    if (mt >= nmt) return;   // padding of the last run
+    h = (row % p.Hkv) * p.group + (t - mt * p.group);
+    b = row / p.Hkv;
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     mt = L % nmt;
@@ -655,14 +651,18 @@ hipError_t launch_bwd(const BwdParams& p, int stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 2) && p.Sk > 0) {
-    const long nblk = (long)((p.Sk + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV) * p.Hkv * p.B;
+    const int nkt = (p.Sk + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
+    const long nblk = VARLEN ? varlen_grid(p.Hkv * p.B, nkt, kDkdvVarlenRun)
+                             : (long)nkt * p.Hkv * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(DkdvTile<D>::NT), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 4) {
-    const long nblk = (long)((p.Sq + DqTile<D>::BM - 1) / DqTile<D>::BM) * p.Hq * p.B;
+    const int nmt = (p.Sq + DqTile<D>::BM - 1) / DqTile<D>::BM;
+    const long nblk = VARLEN ? varlen_grid(p.Hkv * p.B, nmt * p.group, kDqVarlenRun * p.group)
+                             : (long)nmt * p.Hq * p.B;
     if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();

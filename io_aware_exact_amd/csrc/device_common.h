@@ -89,3 +89,36 @@ __device__ __forceinline__ int swz(int row, int col) {
   const int f = D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
   return row * D + ((((col >> 3) ^ f)) << 3) + (col & 7);
 }
+
+// Workgroup orders.  The hardware deals workgroup w of a dispatch to XCD
+// w % 8, and each XCD has its own L2.
+//
+// Dense shapes: map dispatch index w of n to a logical tile index so that
+// logical neighbours share an XCD (each XCD gets one contiguous range).
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = w & 7, s = w >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+// Packed sequences: the work is `rows` rows of tiles (a row is one sequence
+// and head, whose tiles read one operand stream).  Each XCD takes runs of
+// `run` consecutive tiles of one row, so the workgroups resident on it read
+// the same stream through its L2; the rows of a run group are dealt over the
+// eight XCDs with a rotation that advances with the group, so that the
+// heaviest rows do not all land on one XCD.  A contiguous range per XCD (as
+// above) would hand whole long sequences to one XCD.  The grid holds
+// varlen_grid(rows, ntiles, run) workgroups; returns false on its padding.
+__host__ __device__ __forceinline__ long varlen_grid(int rows, int ntiles, int run) {
+  return 8L * ((rows + 7) / 8) * run * ((ntiles + run - 1) / run);
+}
+__device__ __forceinline__ bool varlen_order(int w, int rows, int run, int& row, int& tile) {
+  const int x = w & 7, n = w >> 3;
+  const int r8 = (rows + 7) >> 3;
+  const int k = n % run;
+  const int rest = n / run;
+  const int grp = rest / r8;
+  row = (rest - grp * r8) * 8 + ((x + grp) & 7);
+  tile = grp * run + k;
+  return row < rows;
+}

@@ -3,6 +3,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Packed-sequence workgroup orders (varlen_order in device_common.h): query
+// or key tiles per XCD run, per query head of a kv group.
+constexpr int kFwdVarlenRun = 4;      // fwd_bf16_kernel (128-row tiles, 2 workgroups per CU)
+constexpr int kFwdPpVarlenRun = 2;    // fwd_bf16_pp_kernel (256-row tiles, 1 per CU)
+constexpr int kDkdvVarlenRun = 8;     // bwd_dkdv_kernel (128 keys, 1 per CU)
+constexpr int kDqVarlenRun = 4;       // bwd_dq_kernel (128 rows, 2 per CU)
+
 struct FwdParams {
   const void* q;
   const void* k;

@@ -75,12 +75,6 @@ struct Fp8Tile {
   static constexpr int STAGE = 2 * BN * STR;
 };
 
-__device__ __forceinline__ int xcd_remap(int w, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int x = w & 7, s = w >> 3;
-  return x * q + (x < r ? x : r) + s;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   using T = Fp8Tile<D>;

@@ -66,14 +66,6 @@ struct FwdTile {
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
-// Map a dispatch index to a logical tile index so that logical neighbours
-// share an XCD: dispatch index w runs on XCD w % 8.
-__device__ __forceinline__ int xcd_remap(int w, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int x = w & 7, s = w >> 3;
-  return x * q + (x < r ? x : r) + s;
-}
-
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
@@ -81,18 +73,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // ---- which (batch, head, query tile).  Dense: consecutive tiles of one
   // head share an XCD (L2 reuse of its K/V); causal tiles heaviest first.
-  // Packed sequences have very different lengths, so there the order is
-  // query-tile-major (all heads and sequences at the same tile index run
-  // together, heaviest index first) and the hardware's round-robin over the
-  // XCDs is kept: a contiguous range per XCD would give one XCD whole long
-  // sequences and another short ones.
+  // Packed sequences: runs of query tiles of the query heads of one
+  // (sequence, kv head) per XCD, rows rotated over the XCDs (varlen_order).
   int mt, h, b;
   if (VARLEN) {
-    const int L = blockIdx.x;
-    const int bh = p.Hq * p.B;
-    mt = L / bh;
-    h = (L % bh) % p.Hq;
-    b = (L % bh) / p.Hq;
+    int row, t;
+    if (!varlen_order(blockIdx.x, p.Hkv * p.B, kFwdVarlenRun * p.group, row, t)) return;
+    mt = t / p.group;
+    if (mt >= p.num_m_tiles) return;   // padding of the last run
+    h = (row % p.Hkv) * p.group + (t - mt * p.group);
+    b = row / p.Hkv;
     if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -302,7 +292,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  const long nblk = (long)p.num_m_tiles * p.Hq * p.B;
+  const long nblk = VARLEN ? varlen_grid(p.Hkv * p.B, p.num_m_tiles * p.group, kFwdVarlenRun * p.group)
+                           : (long)p.num_m_tiles * p.Hq * p.B;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);

@@ -35,12 +35,6 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int xcd_remap(int w, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int x = w & 7, s = w >> 3;
-  return x * q + (x < r ? x : r) + s;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_f32_kernel(FwdParams p) {
   using T = F32Tile<D>;

@@ -43,12 +43,6 @@ struct PpTile {
   static constexpr int LDS_ELEMS = 2 * (KSTAGE + VSTAGE);
 };
 
-__device__ __forceinline__ int xcd_remap(int w, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int x = w & 7, s = w >> 3;
-  return x * q + (x < r ? x : r) + s;
-}
-
 // Workgroup barrier that the instruction scheduler may not move work across:
 // register-only work (the exponentials) would otherwise drift into the
 // neighbouring phase and the two groups would no longer alternate.
@@ -63,13 +57,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   using T = PpTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
 
+  // Dense: consecutive query tiles of one head share an XCD.  Packed
+  // sequences: runs of query tiles of the query heads of one (sequence, kv
+  // head) per XCD (varlen_order).  Causal: heaviest tiles first.
   int mt, h, b;
   if (VARLEN) {
-    const int L = blockIdx.x;
-    const int bh = p.Hq * p.B;
-    mt = L / bh;
-    h = (L % bh) % p.Hq;
-    b = (L % bh) / p.Hq;
+    int row, t;
+    if (!varlen_order(blockIdx.x, p.Hkv * p.B, kFwdPpVarlenRun * p.group, row, t)) return;
+    mt = t / p.group;
+    if (mt >= p.num_m_tiles) return;   // padding of the last run
+    h = (row % p.Hkv) * p.group + (t - mt * p.group);
+    b = row / p.Hkv;
     if (CAUSAL) mt = p.num_m_tiles - 1 - mt;
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -348,7 +346,8 @@ template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(FwdParams p, hipStream_t stream) {
   const int rows = p.Sq;   // dense: Sq; varlen: max query length
   p.num_m_tiles = (rows + BM - 1) / BM;
-  const long nblk = (long)p.num_m_tiles * p.Hq * p.B;
+  const long nblk = VARLEN ? varlen_grid(p.Hkv * p.B, p.num_m_tiles * p.group, kFwdPpVarlenRun * p.group)
+                           : (long)p.num_m_tiles * p.Hq * p.B;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NT), 0, stream, p);

@@ -14,7 +14,8 @@
  *     materialised, arithmetic stays quadratic;
  *   - "Flash Attention and Efficient Transformer Mechanisms": blocks of Q, K
  *     and V are read from high-bandwidth memory into on-chip memory and
- *     partial outputs are computed there, "without approximation";
+ *     partial outputs are computed there, and the result is that of
+ *     standard attention, not an approximation of it;
  *   - Dao-AILab repository overview: online softmax with rescaling, tiled
  *     attention staged through on-chip memory, a dense entry point, a packed
  *     variable-length entry point and a KV-cache (decode) entry point,

@@ -17,8 +17,8 @@
  *        P_ij = exp(s_ij - m_i) / sum_j' exp(s_ij' - m_i)   over allowed j
  *        O_i  = sum_j P_ij v_j,     LSE_i = m_i + ln(sum_j exp(s_ij - m_i))
  *  - "Flash Attention and Efficient Transformer Mechanisms" (article, the
- *    paragraph on block computation): the result is the same as standard
- *    attention "without approximation".
+ *    paragraph on block computation): the blockwise result equals standard
+ *    attention exactly; nothing is approximated.
  *  - The backward is the calculus derivative of that definition (the pages
  *    say only that the backward recomputes attention from saved statistics;
  *    they print no formula):

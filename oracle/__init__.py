@@ -12,11 +12,13 @@ Sources (pages on IO-aware exact attention):
     research record, fields "summary" and "boundary": the method is exact
     attention computed with tiling and recomputation, without the full
     attention matrix; the result is the plain definition.
-  * "Flash Attention and Efficient Transformer Mechanisms": exact, "without
-    approximation".
+  * "Flash Attention and Efficient Transformer Mechanisms": the blockwise
+    result is standard attention, nothing approximated.
   * "Dao-AILab" repository overview: the public surface has dense, packed
     variable-length (varlen) and KV-cache entry points -- the varlen oracle
-    below is the dense oracle run on every packed sequence separately.
+    below is the dense oracle run on every packed sequence separately, and
+    the KV-cache oracle is the dense oracle run on each sequence's keys as
+    read from its cache pages, after the new keys are appended.
 
 Layouts (readings; the pages give none): dense tensors are [B, S, H, d];
 packed varlen tensors are [T, H, d] with cumulative sequence offsets; LSE is
@@ -259,3 +261,82 @@ def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, causal=False
         dv[k0:k1] = dvz[0]
     return o, lse, dq, dk, dv
 
+
+
+def _cache_rows(cache, pages, slots, g):
+    """Rows cache[pages[i], slots[i], g, :] as float64 [n, d]."""
+    if hasattr(cache, "detach"):
+        import torch
+        pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
+        slots = torch.as_tensor(np.asarray(slots, dtype=np.int64))
+    return _f64(cache[pages, slots, g, :])
+
+
+def _seq_pages(b, n, page_size, block_table):
+    """Page and slot of tokens 0..n-1 of sequence b: token j lives in page
+    block_table[b][j // page_size] at slot j % page_size; without a block
+    table, sequence b owns page b of capacity page_size."""
+    j = np.arange(n, dtype=np.int64)
+    if block_table is None:
+        return np.full(n, b, dtype=np.int64), j
+    row = np.asarray(block_table[b], dtype=np.int64)
+    return row[j // page_size], j % page_size
+
+
+def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new, block_table=None):
+    """The cache after the append step of KV-cache attention, as float64
+    copies: row i of k_new[b] / v_new[b] ([B, Snew, Hkv, d]) is written at
+    token position cache_seqlens[b] + i of sequence b (page and slot as in
+    _seq_pages); nothing else changes.  Caches are [pages, page_size, Hkv, d]
+    (without a block table: [B, capacity, Hkv, d])."""
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    kn, vn = _f64(k_new), _f64(v_new)
+    page_size = kc.shape[1]
+    lens = np.asarray(cache_seqlens, dtype=np.int64)
+    for b in range(kn.shape[0]):
+        pages, slots = _seq_pages(b, lens[b] + kn.shape[1], page_size, block_table)
+        for i in range(kn.shape[1]):
+            j = lens[b] + i
+            kc[pages[j], slots[j]] = kn[b, i]
+            vc[pages[j], slots[j]] = vn[b, i]
+    return kc, vc
+
+
+def attention_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=None,
+                      v_new=None, causal=False, scale=None, seqs=None, rows=None):
+    """KV-cache attention (the repository overview's KV-cache entry point).
+
+    Sequence b holds L_b = cache_seqlens[b] + Snew keys: tokens
+    0..cache_seqlens[b]-1 read from its cache pages (see _seq_pages), then
+    the Snew rows of k_new[b] / v_new[b] (the append).  q [B,Sq,Hq,d]
+    attends to them with the causal alignment of the dense path (query row i
+    sees key j iff j <= i + L_b - Sq).  Returns o [B,Sq,Hq,d], lse [B,Hq,Sq].
+    `seqs` restricts the work to some sequences and `rows` (list of query
+    positions) to some rows; rows not computed are left at zero (o) and nan
+    (lse)."""
+    B, Sq, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    page_size = k_cache.shape[1]
+    grp = Hq // Hkv
+    scale = _default_scale(d, scale)
+    lens = np.asarray(cache_seqlens, dtype=np.int64)
+    snew = 0 if k_new is None else k_new.shape[1]
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.full((B, Hq, Sq), np.nan)
+    pos = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    for b in (range(B) if seqs is None else seqs):
+        pages, slots = _seq_pages(b, lens[b], page_size, block_table)
+        L = int(lens[b]) + snew
+        for g in range(Hkv):
+            kk = _cache_rows(k_cache, pages, slots, g)
+            vv = _cache_rows(v_cache, pages, slots, g)
+            if snew:
+                kk = np.concatenate([kk, _f64(k_new[b, :, g, :])])
+                vv = np.concatenate([vv, _f64(v_new[b, :, g, :])])
+            for h in range(g * grp, (g + 1) * grp):
+                qr = _f64(q[b, :, h, :])[pos]
+                ob, lb = head_fwd(qr, pos, kk.reshape(L, d), vv.reshape(L, d), L - Sq,
+                                  causal, scale)
+                o[b, pos, h, :] = ob
+                lse[b, h, pos] = lb
+    return o, lse

@@ -395,3 +395,113 @@ def test_varlen_bwd_matches_block_diagonal_autograd():
         # rows with no visible key: LSE = -inf
         no_key = ~allowed.any(1)
         assert np.all(np.isneginf(lse[:, no_key]))
+
+
+# ---- KV-cache oracle (append + paged cache) ----------------------------------
+
+def paged_case(seed, lens, snew, sq, Hq=4, Hkv=2, d=16, page_size=4, npages=24):
+    """A paged cache whose pages are handed out to the sequences in a
+    shuffled order, plus new rows to append and queries."""
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    per = max(-(-(L + snew) // page_size) for L in lens)
+    assert B * per <= npages
+    phys = rng.permutation(npages)[:B * per].reshape(B, per)
+    kc = rng.standard_normal((npages, page_size, Hkv, d))
+    vc = rng.standard_normal((npages, page_size, Hkv, d))
+    kn = rng.standard_normal((B, snew, Hkv, d))
+    vn = rng.standard_normal((B, snew, Hkv, d))
+    q = rng.standard_normal((B, sq, Hq, d))
+    return q, kc, vc, np.asarray(lens), phys, kn, vn
+
+
+def walk_pages(cache, table_row, n, page_size):
+    """Tokens 0..n-1 of one sequence by concatenating its pages in order."""
+    parts, left, p = [], n, 0
+    while left > 0:
+        take = min(page_size, left)
+        parts.append(cache[table_row[p], :take])
+        left -= take
+        p += 1
+    return np.concatenate(parts) if parts else cache[:0, 0]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_matches_sdpa_on_page_walk(causal):
+    # the append written by hand into a copy of the cache, the sequence read
+    # back page by page, then torch's attention per sequence
+    lens, snew, sq = [5, 0, 13, 8], 3, 3
+    q, kc, vc, lens, bt, kn, vn = paged_case(1, lens, snew, sq)
+    o, lse = oracle.attention_kvcache(q, kc, vc, lens, bt, kn, vn, causal, 0.3)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(len(lens)):
+        for i in range(snew):
+            j = lens[b] + i
+            kc2[bt[b, j // 4], j % 4] = kn[b, i]
+            vc2[bt[b, j // 4], j % 4] = vn[b, i]
+    for b in range(len(lens)):
+        L = lens[b] + snew
+        kk = walk_pages(kc2, bt[b], L, 4)[None]
+        vv = walk_pages(vc2, bt[b], L, 4)[None]
+        o_r, lse_r = sdpa_ref(q[b:b + 1], kk, vv, causal, 0.3)
+        np.testing.assert_allclose(o[b], o_r[0], atol=1e-12)
+        np.testing.assert_allclose(lse[b], lse_r[0], atol=1e-12)
+
+
+def test_kvcache_append_writes_only_the_new_rows():
+    lens, snew = [5, 0, 13], 3
+    q, kc, vc, lens, bt, kn, vn = paged_case(2, lens, snew, 1)
+    kc2, vc2 = oracle.kvcache_append(kc, vc, lens, kn, vn, bt)
+    written = np.zeros(kc.shape[:2], dtype=bool)
+    for b in range(len(lens)):
+        for i in range(snew):
+            j = lens[b] + i
+            p, s = bt[b, j // 4], j % 4
+            assert np.array_equal(kc2[p, s], kn[b, i]) and np.array_equal(vc2[p, s], vn[b, i])
+            written[p, s] = True
+    assert np.array_equal(kc2[~written], kc[~written]) and np.array_equal(vc2[~written], vc[~written])
+
+
+def test_kvcache_invariant_under_page_permutation():
+    # moving the physical pages and rewriting the block table changes nothing
+    q, kc, vc, lens, bt, kn, vn = paged_case(3, [6, 11, 1], 2, 2)
+    perm = np.random.default_rng(9).permutation(kc.shape[0])
+    inv = np.argsort(perm)
+    kcp, vcp = kc[perm], vc[perm]          # new page x holds old page perm[x]
+    btp = inv[bt]
+    o1, l1 = oracle.attention_kvcache(q, kc, vc, lens, bt, kn, vn, True)
+    o2, l2 = oracle.attention_kvcache(q, kcp, vcp, lens, btp, kn, vn, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_kvcache_append_equals_prefilled_cache():
+    # appending Snew rows = a cache that already holds them, with no append
+    q, kc, vc, lens, bt, kn, vn = paged_case(4, [6, 0, 9], 3, 3)
+    o1, l1 = oracle.attention_kvcache(q, kc, vc, lens, bt, kn, vn, True)
+    kc2, vc2 = oracle.kvcache_append(kc, vc, lens, kn, vn, bt)
+    o2, l2 = oracle.attention_kvcache(q, kc2, vc2, lens + 3, bt, None, None, True)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+
+
+def test_kvcache_dense_cache_equals_dense_attention():
+    # without a block table sequence b owns cache row b; a full cache with no
+    # append is the dense forward, and shorter lengths are its prefix
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 4, 16))
+    kc = rng.standard_normal((2, 10, 2, 16))
+    vc = rng.standard_normal((2, 10, 2, 16))
+    o1, l1 = oracle.attention_kvcache(q, kc, vc, [10, 10], None, None, None, True)
+    o2, l2 = oracle.attention_fwd(q, kc, vc, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, l3 = oracle.attention_kvcache(q, kc, vc, [7, 10], None, None, None, False)
+    o4, l4 = oracle.attention_fwd(q[:1], kc[:1, :7], vc[:1, :7], False)
+    assert np.array_equal(o3[:1], o4) and np.array_equal(l3[:1], l4)
+
+
+def test_kvcache_empty_sequence():
+    # no cached tokens and nothing appended: O = 0, LSE = -inf
+    q, kc, vc, lens, bt, kn, vn = paged_case(6, [0, 3], 0, 2)
+    o, lse = oracle.attention_kvcache(q, kc, vc, lens, bt, None, None, False)
+    assert np.all(o[0] == 0) and np.all(lse[0] == -np.inf)
+    assert np.all(np.isfinite(lse[1]))

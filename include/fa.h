@@ -205,6 +205,62 @@ typedef struct {
   size_t workspace_bytes;
 } fa_bwd_varlen_args;
 
+/* KV-cache attention (bf16): the repository overview's KV-cache entry point
+ * (flash_attn_with_kvcache), with a cache that is appended to and may be
+ * paged.  Layouts and rules are readings; the pages give none.
+ *
+ * Cache.  k_cache and v_cache are [num_pages, page_size, Hkv, d] with
+ * element strides *_stride_page, *_stride_s and *_stride_h (d contiguous,
+ * strides multiples of 8).  Token j of sequence b is slot j % page_size of
+ * page block_table[b * block_table_stride + j / page_size]; page_size must be
+ * a power of two and block_table an int32 device array with
+ * max_pages_per_seq used columns per row.  With block_table NULL the cache is
+ * dense: page b is all of sequence b's cache (num_pages >= B, page_size =
+ * the capacity, any value >= 1).  cache_seqlens [B] int32 (device) counts
+ * the tokens each sequence already has in the cache.
+ *
+ * Append.  When Snew > 0, k_new and v_new [B, Snew, Hkv, d] are written
+ * first, at token positions cache_seqlens[b] .. cache_seqlens[b] + Snew - 1
+ * of each sequence (the caller provides those pages in block_table).
+ * cache_seqlens itself is not modified.
+ *
+ * Attention.  q [B, Sq, Hq, d] attends to the L_b = cache_seqlens[b] + Snew
+ * tokens of its sequence, causal alignment bottom-right against L_b (query
+ * row i sees key j iff j <= i + L_b - Sq); o [B, Sq, Hq, d] bf16, lse
+ * [B, Hq, Sq] fp32 contiguous.  Sq may be 0 (append only).
+ *
+ * max_seqlen_k bounds every L_b (0: the capacity, max_pages_per_seq *
+ * page_size, or page_size for a dense cache); it sizes the grid and the
+ * split plan.  When Sq * (Hq / Hkv) <= 32, fa_fwd_kvcache_workspace_size is
+ * nonzero and with that workspace (256-byte aligned) the keys are cut into
+ * chunks that run in parallel and are merged exactly, as in fa_fwd's decode
+ * path; otherwise (or without a workspace) the tiled forward kernels read
+ * the cache pages directly (chunked prefill against a cache).
+ *
+ * Device contents are trusted: every L_b <= max_seqlen_k, and the block
+ * table holds valid page indices for tokens 0 .. L_b - 1.  o and lse must
+ * not overlap the inputs or the cache; k_new / v_new must not overlap the
+ * cache.  Deterministic. */
+typedef struct {
+  fa_dtype dtype;
+  int32_t B, Sq, Hq, Hkv, d, Snew;
+  int32_t causal;
+  float softmax_scale;
+  fa_tensor q, o;
+  float* lse;
+  void* k_cache;
+  void* v_cache;
+  int64_t k_stride_page, k_stride_s, k_stride_h;
+  int64_t v_stride_page, v_stride_s, v_stride_h;
+  int32_t num_pages, page_size, max_pages_per_seq, max_seqlen_k;
+  const int32_t* block_table;
+  int64_t block_table_stride;
+  const int32_t* cache_seqlens;
+  fa_tensor k_new, v_new;
+  void* workspace;
+  size_t workspace_bytes;
+} fa_fwd_kvcache_args;
+
 /* Returns FA_ABI_VERSION. */
 int32_t fa_abi_version(void);
 
@@ -236,6 +292,13 @@ size_t fa_bwd_varlen_workspace_size(const fa_bwd_varlen_args* args);
 
 /* Packed variable-length backward; see fa_bwd_varlen_args. */
 fa_status fa_bwd_varlen(const fa_bwd_varlen_args* args, hipStream_t stream);
+
+/* Workspace bytes the split-KV path of fa_fwd_kvcache uses for these
+ * arguments; 0 when it does not apply. */
+size_t fa_fwd_kvcache_workspace_size(const fa_fwd_kvcache_args* args);
+
+/* KV-cache attention with append; see fa_fwd_kvcache_args. */
+fa_status fa_fwd_kvcache(const fa_fwd_kvcache_args* args, hipStream_t stream);
 
 /* FP8 quantiser (input preparation for the FP8 forward; "FlashAttention-3:
  * Fast and Accurate Attention with Asynchrony and Low-precision", third

@@ -69,17 +69,17 @@ struct DecodePlan {
   size_t o_part_bytes, lse_part_bytes;
 };
 
-DecodePlan decode_plan(const fa_fwd_args* a) {
+DecodePlan split_plan(fa_dtype dtype, int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                      int64_t d) {
   DecodePlan pl = {false, 1, 32, 0, 0};
-  if (a->dtype != FA_BF16 || a->B <= 0 || a->Sq <= 0 || a->Sk < 0 || a->Hkv <= 0 || a->Hq <= 0 ||
-      a->Hq % a->Hkv != 0 || (a->d != 64 && a->d != 128))
+  if (dtype != FA_BF16 || B <= 0 || Sq <= 0 || Sk < 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 ||
+      (d != 64 && d != 128))
     return pl;
-  const int64_t group = a->Hq / a->Hkv;
-  if ((int64_t)a->Sq * group > kDecodeMaxRows) return pl;
+  const int64_t group = Hq / Hkv;
+  if (Sq * group > kDecodeMaxRows) return pl;
   pl.eligible = true;
-  const int64_t Sk = a->Sk;
   if (Sk > 0) {
-    const int64_t pairs = (int64_t)a->B * a->Hkv;
+    const int64_t pairs = B * Hkv;
     int64_t ns = (kDecodeTargetWaves + pairs - 1) / pairs;
     const int64_t by_len = (Sk + kDecodeMinKeysPerSplit - 1) / kDecodeMinKeysPerSplit;
     if (ns > by_len) ns = by_len;
@@ -89,10 +89,14 @@ DecodePlan decode_plan(const fa_fwd_args* a) {
     pl.chunk = (int)chunk;
     pl.nsplit = (int)((Sk + chunk - 1) / chunk);
   }
-  const size_t rows = (size_t)a->B * a->Hq * a->Sq * pl.nsplit;
-  pl.o_part_bytes = align256(rows * a->d * 4);
+  const size_t rows = (size_t)B * Hq * Sq * pl.nsplit;
+  pl.o_part_bytes = align256(rows * d * 4);
   pl.lse_part_bytes = align256(rows * 4);
   return pl;
+}
+
+DecodePlan decode_plan(const fa_fwd_args* a) {
+  return split_plan(a->dtype, a->B, a->Sq, a->Sk, a->Hq, a->Hkv, a->d);
 }
 
 fa_status check_fwd(const fa_fwd_args* a) {
@@ -307,6 +311,97 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
 hipError_t launch_fwd_tiled(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
   if (d == 128) return launch_fwd_bf16_pp(p, d, causal, varlen, stream);
   return launch_fwd_bf16(p, d, causal, varlen, stream);
+}
+
+// ---- KV-cache attention
+int64_t kv_capacity(const fa_fwd_kvcache_args* a) {
+  return a->block_table ? (int64_t)a->max_pages_per_seq * a->page_size : (int64_t)a->page_size;
+}
+
+int64_t kv_max_len(const fa_fwd_kvcache_args* a) {
+  return a->max_seqlen_k > 0 ? (int64_t)a->max_seqlen_k : kv_capacity(a);
+}
+
+DecodePlan kvcache_plan(const fa_fwd_kvcache_args* a) {
+  return split_plan(a->dtype, a->B, a->Sq, kv_max_len(a), a->Hq, a->Hkv, a->d);
+}
+
+bool strides8(int64_t a, int64_t b, int64_t c) {
+  return a >= 0 && b >= 0 && c >= 0 && a % 8 == 0 && b % 8 == 0 && c % 8 == 0;
+}
+
+fa_status check_kvcache(const fa_fwd_kvcache_args* a) {
+  if (!a) return FA_ERR_NULL;
+  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->B < 0 || a->Sq < 0 || a->Snew < 0 || a->Hq < 1 || a->Hkv < 1 || a->num_pages < 0 ||
+      a->page_size < 1 || a->max_seqlen_k < 0)
+    return FA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
+  if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
+  if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
+  const bool paged = a->block_table != nullptr;
+  if (paged) {
+    if ((a->page_size & (a->page_size - 1)) != 0) return FA_ERR_SHAPE;   // a power of two
+    if (a->max_pages_per_seq < 1 || a->block_table_stride < a->max_pages_per_seq) return FA_ERR_SHAPE;
+    if (a->B > 0 && a->num_pages < 1) return FA_ERR_SHAPE;
+    if ((uintptr_t)a->block_table & 3u) return FA_ERR_ALIGN;
+  } else if (a->num_pages < a->B) {
+    return FA_ERR_SHAPE;   // dense cache: page b is sequence b's
+  }
+  const int64_t cap = kv_capacity(a);
+  if (cap > 0x7fffffffLL - 256) return FA_ERR_SHAPE;   // token positions are 32-bit
+  if (a->max_seqlen_k > cap || a->Snew > kv_max_len(a)) return FA_ERR_SHAPE;
+  if (a->B == 0) return FA_OK;
+  if (!a->cache_seqlens || !a->k_cache || !a->v_cache) return FA_ERR_NULL;
+  if (a->Sq > 0 && (!a->q.ptr || !a->o.ptr || !a->lse)) return FA_ERR_NULL;
+  if (a->Snew > 0 && (!a->k_new.ptr || !a->v_new.ptr)) return FA_ERR_NULL;
+  if (!aligned16(a->q.ptr) || !aligned16(a->o.ptr) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
+      !aligned16(a->k_new.ptr) || !aligned16(a->v_new.ptr) || ((uintptr_t)a->lse & 3u) ||
+      ((uintptr_t)a->cache_seqlens & 3u))
+    return FA_ERR_ALIGN;
+  if (!strides_ok(a->q, 8) || !strides_ok(a->o, 8) || !strides_ok(a->k_new, 8) || !strides_ok(a->v_new, 8) ||
+      !strides8(a->k_stride_page, a->k_stride_s, a->k_stride_h) ||
+      !strides8(a->v_stride_page, a->v_stride_s, a->v_stride_h))
+    return FA_ERR_ALIGN;
+  const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
+  if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!fits32(a->Sq, a->q.stride_s, 2) || !fits32(a->Sq, a->o.stride_s, 2)) return FA_ERR_SHAPE;
+  const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
+  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
+  const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2);
+  const Span skn = span4(a->k_new.ptr, a->B, a->Snew, a->Hkv, a->d, a->k_new.stride_b, a->k_new.stride_s,
+                         a->k_new.stride_h, 2);
+  const Span svn = span4(a->v_new.ptr, a->B, a->Snew, a->Hkv, a->d, a->v_new.stride_b, a->v_new.stride_s,
+                         a->v_new.stride_h, 2);
+  const Span skc = span4(a->k_cache, a->num_pages, a->page_size, a->Hkv, a->d, a->k_stride_page, a->k_stride_s,
+                         a->k_stride_h, 2);
+  const Span svc = span4(a->v_cache, a->num_pages, a->page_size, a->Hkv, a->d, a->v_stride_page, a->v_stride_s,
+                         a->v_stride_h, 2);
+  const Span sbt = paged ? Span{(uintptr_t)a->block_table,
+                                (uintptr_t)(a->block_table + ((int64_t)a->B - 1) * a->block_table_stride +
+                                            a->max_pages_per_seq)}
+                         : Span{0, 0};
+  const Span ssl = {(uintptr_t)a->cache_seqlens, (uintptr_t)(a->cache_seqlens + a->B)};
+  // outputs: o, lse, and (when appending) the caches
+  const Span outs[2] = {so, sl};
+  const Span ins[8] = {sq, skn, svn, skc, svc, sbt, ssl, Span{0, 0}};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlap(o, i)) return FA_ERR_ALIAS;
+  if (overlap(so, sl)) return FA_ERR_ALIAS;
+  if (a->Snew > 0) {
+    const Span readers[5] = {sq, skn, svn, sbt, ssl};
+    for (const Span& r : readers)
+      if (overlap(skc, r) || overlap(svc, r)) return FA_ERR_ALIAS;
+  }
+  if (a->workspace && a->workspace_bytes > 0) {
+    if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
+    const Span sw = {(uintptr_t)a->workspace, (uintptr_t)a->workspace + a->workspace_bytes};
+    const Span all[9] = {so, sl, sq, skn, svn, skc, svc, sbt, ssl};
+    for (const Span& x : all)
+      if (overlap(sw, x)) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
 }
 
 }  // namespace
@@ -524,6 +619,84 @@ fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, in
   const Span ss_ = {(uintptr_t)scales, (uintptr_t)scales + (uintptr_t)((int64_t)B * H * nb * 4)};
   if (overlap(sx, sc) || overlap(sx, ss_) || overlap(sc, ss_)) return FA_ERR_ALIAS;
   return hip_status(launch_quantize_fp8(x, sb, ss, sh, B, S, H, d, per_tensor != 0, codes, scales, stream));
+}
+
+size_t fa_fwd_kvcache_workspace_size(const fa_fwd_kvcache_args* a) {
+  if (!a) return 0;
+  const DecodePlan pl = kvcache_plan(a);
+  return pl.eligible ? pl.o_part_bytes + pl.lse_part_bytes : 0;
+}
+
+fa_status fa_fwd_kvcache(const fa_fwd_kvcache_args* a, hipStream_t stream) {
+  const fa_status s = check_kvcache(a);
+  if (s != FA_OK) return s;
+  if (a->B == 0) return FA_OK;
+  KvCacheParams kv = {};
+  kv.seqlens = a->cache_seqlens;
+  kv.block_table = a->block_table;
+  kv.bt_stride = a->block_table_stride;
+  int shift = 0;
+  while (a->block_table && (1 << shift) < a->page_size) ++shift;
+  kv.page_shift = shift;
+  kv.snew = a->Snew;
+  kv.k_sp = a->k_stride_page;
+  kv.v_sp = a->v_stride_page;
+  if (a->Snew > 0) {
+    KvAppendParams ap = {};
+    ap.k_new = a->k_new.ptr;
+    ap.v_new = a->v_new.ptr;
+    ap.kn_sb = a->k_new.stride_b; ap.kn_ss = a->k_new.stride_s; ap.kn_sh = a->k_new.stride_h;
+    ap.vn_sb = a->v_new.stride_b; ap.vn_ss = a->v_new.stride_s; ap.vn_sh = a->v_new.stride_h;
+    ap.k_cache = a->k_cache;
+    ap.v_cache = a->v_cache;
+    ap.k_ss = a->k_stride_s; ap.k_sh = a->k_stride_h;
+    ap.v_ss = a->v_stride_s; ap.v_sh = a->v_stride_h;
+    ap.kv = kv;
+    ap.B = a->B;
+    ap.Hkv = a->Hkv;
+    const hipError_t e = launch_kv_append(ap, a->d, stream);
+    if (e != hipSuccess) return FA_ERR_HIP;
+  }
+  if (a->Sq == 0) return FA_OK;
+  const int64_t maxlen = kv_max_len(a);
+  const float scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  const DecodePlan pl = kvcache_plan(a);
+  if (pl.eligible && a->workspace && a->workspace_bytes >= pl.o_part_bytes + pl.lse_part_bytes) {
+    DecodeParams d = {};
+    d.q = a->q.ptr; d.k = a->k_cache; d.v = a->v_cache; d.o = a->o.ptr; d.lse = a->lse;
+    d.o_part = (float*)a->workspace;
+    d.lse_part = (float*)((char*)a->workspace + pl.o_part_bytes);
+    d.q_sb = a->q.stride_b; d.q_ss = a->q.stride_s; d.q_sh = a->q.stride_h;
+    d.k_ss = a->k_stride_s; d.k_sh = a->k_stride_h;
+    d.v_ss = a->v_stride_s; d.v_sh = a->v_stride_h;
+    d.o_sb = a->o.stride_b; d.o_ss = a->o.stride_s; d.o_sh = a->o.stride_h;
+    d.lse_sb = (int64_t)a->Hq * a->Sq; d.lse_sh = a->Sq;
+    d.B = a->B; d.Sq = a->Sq; d.Sk = (int)maxlen; d.Hq = a->Hq; d.Hkv = a->Hkv; d.group = a->Hq / a->Hkv;
+    d.causal = a->causal != 0;
+    d.nsplit = pl.nsplit;
+    d.chunk = pl.chunk;
+    d.scale = a->softmax_scale;
+    d.scale_log2 = scale_log2;
+    d.kv = kv;
+    return hip_status(launch_decode_bf16_kvcache(d, a->d, stream));
+  }
+  FwdParams p = {};
+  p.q = a->q.ptr; p.k = a->k_cache; p.v = a->v_cache; p.o = a->o.ptr; p.lse = a->lse;
+  p.q_sb = a->q.stride_b; p.q_ss = a->q.stride_s; p.q_sh = a->q.stride_h;
+  p.k_ss = a->k_stride_s; p.k_sh = a->k_stride_h;
+  p.v_ss = a->v_stride_s; p.v_sh = a->v_stride_h;
+  p.o_sb = a->o.stride_b; p.o_ss = a->o.stride_s; p.o_sh = a->o.stride_h;
+  p.lse_sb = (int64_t)a->Hq * a->Sq;
+  p.lse_sh = a->Sq;
+  p.B = a->B; p.Sq = a->Sq; p.Sk = (int)maxlen; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.num_m_tiles = (a->Sq + kBM - 1) / kBM;
+  p.scale = a->softmax_scale;
+  p.scale_log2 = scale_log2;
+  p.kv = kv;
+  const bool causal = a->causal != 0;
+  return hip_status(a->d == 128 ? launch_fwd_bf16_pp_kvcache(p, a->d, causal, stream)
+                                : launch_fwd_bf16_kvcache(p, a->d, causal, stream));
 }
 
 }  // extern "C"

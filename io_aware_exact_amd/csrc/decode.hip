@@ -29,6 +29,11 @@
 //     the LDS transposing read.  The next block's K and V loads are issued
 //     before the current block's MFMAs (32 keys, 16 KB per wave in flight).
 //   * A second kernel combines the partials of every row.
+//   * KV-cache attention (an appended, possibly paged cache) runs the same
+//     kernel with KVC = true: each sequence's length is its cached count plus
+//     the appended rows, and every K/V row is addressed through the block
+//     table (page, slot); rows past the end read the last valid row instead,
+//     and their scores are masked.
 #include "device_common.h"
 #include "fa_internal.h"
 
@@ -59,7 +64,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
+template <int D, bool KVC>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   using T = DecTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Vs[T::BUF];
@@ -71,8 +76,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int Lk = p.Sk;
-  const int diag = p.Sk - p.Sq;
+  const int Lk = KVC ? p.kv.seqlens[b] + p.kv.snew : p.Sk;
+  const int diag = Lk - p.Sq;
   const int nrows = p.Sq * p.group;
 
   const int kbeg = split * p.chunk;
@@ -105,15 +110,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int vcol = (lane % T::CH) * 8;
   bf16x8 kf[T::NC];
   u32x4 vreg[T::NP];
+  // KV cache: the head's base; rows through the block table (Lk >= 1
+  // whenever a block is loaded)
+  const __bf16* kcb = (const __bf16*)p.k + (int64_t)g * p.k_sh;
+  const __bf16* vcb = (const __bf16*)p.v + (int64_t)g * p.v_sh;
   auto gload = [&](int j0) {
-    const uint32_t kr = (uint32_t)(j0 + kp);
+    if constexpr (KVC) {
+      const int jk = min(j0 + kp, Lk - 1);
+      const __bf16* kr = kcb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, jk,
+                                               p.kv.k_sp, p.k_ss);
 #pragma unroll
-    for (int c = 0; c < T::NC; ++c)
-      kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rk, (kr * (uint32_t)p.k_ss + 16 * c + 8 * hh) * 2));
+      for (int c = 0; c < T::NC; ++c) kf[c] = *(const bf16x8*)(kr + 16 * c + 8 * hh);
 #pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      const uint32_t r = (uint32_t)(j0 + vrow + u * T::RPP);
-      vreg[u] = buf_load16(rv, (r * (uint32_t)p.v_ss + vcol) * 2);
+      for (int u = 0; u < T::NP; ++u) {
+        const int jv = min(j0 + vrow + u * T::RPP, Lk - 1);
+        vreg[u] = *(const u32x4*)(vcb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift,
+                                                         b, jv, p.kv.v_sp, p.v_ss) + vcol);
+      }
+    } else {
+      const uint32_t kr = (uint32_t)(j0 + kp);
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c)
+        kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rk, (kr * (uint32_t)p.k_ss + 16 * c + 8 * hh) * 2));
+#pragma unroll
+      for (int u = 0; u < T::NP; ++u) {
+        const uint32_t r = (uint32_t)(j0 + vrow + u * T::RPP);
+        vreg[u] = buf_load16(rv, (r * (uint32_t)p.v_ss + vcol) * 2);
+      }
     }
   };
   const int trG = lane >> 4;
@@ -234,12 +257,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   if (lane == 0) p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qi] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
-template <int D>
+template <int D, bool KVC>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const long nblk = (long)p.B * p.Hkv * p.nsplit;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)nblk), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, KVC>), dim3((unsigned)nblk), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long nrow = (long)p.B * p.Hq * p.Sq;
@@ -250,5 +273,9 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) {
-  return d == 128 ? launch<128>(p, stream) : launch<64>(p, stream);
+  return d == 128 ? launch<128, false>(p, stream) : launch<64, false>(p, stream);
+}
+
+hipError_t launch_decode_bf16_kvcache(const DecodeParams& p, int d, hipStream_t stream) {
+  return d == 128 ? launch<128, true>(p, stream) : launch<64, true>(p, stream);
 }

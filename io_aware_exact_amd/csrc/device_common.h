@@ -122,3 +122,26 @@ __device__ __forceinline__ bool varlen_order(int w, int rows, int run, int& row,
   tile = grp * run + k;
   return row < rows;
 }
+
+// Page and slot of token j of sequence b in a KV cache of pages: page
+// block_table[b * bt_stride + (j >> page_shift)], slot j & (page size - 1);
+// without a block table sequence b owns page b and the slot is j.
+__device__ __forceinline__ void kv_page_slot(const int32_t* block_table, int64_t bt_stride,
+                                             int page_shift, int b, int j, int64_t& page, int& slot) {
+  page = b;
+  slot = j;
+  if (block_table) {
+    page = block_table[(int64_t)b * bt_stride + (j >> page_shift)];
+    slot = j & ((1 << page_shift) - 1);
+  }
+}
+
+// Element offset page * page_stride + slot * token_stride of that token.
+__device__ __forceinline__ int64_t kv_token_offset(const int32_t* block_table, int64_t bt_stride,
+                                                   int page_shift, int b, int j,
+                                                   int64_t page_stride, int64_t token_stride) {
+  int64_t page;
+  int slot;
+  kv_page_slot(block_table, bt_stride, page_shift, b, j, page, slot);
+  return page * page_stride + (int64_t)slot * token_stride;
+}

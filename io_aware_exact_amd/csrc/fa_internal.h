@@ -10,6 +10,20 @@ constexpr int kFwdPpVarlenRun = 2;    // fwd_bf16_pp_kernel (256-row tiles, 1 pe
 constexpr int kDkdvVarlenRun = 8;     // bwd_dkdv_kernel (128 keys, 1 per CU)
 constexpr int kDqVarlenRun = 4;       // bwd_dq_kernel (128 rows, 2 per CU)
 
+// A KV cache read by token position (KV-cache attention).  Token j of
+// sequence b is slot j & (2^page_shift - 1) of page
+// block_table[b * bt_stride + (j >> page_shift)]; with no block table,
+// sequence b owns page b and the slot is j.  The token and head strides are
+// the k_ss/k_sh and v_ss/v_sh of the launch parameters.
+struct KvCacheParams {
+  const int32_t* seqlens;      // [B] tokens cached before the append
+  const int32_t* block_table;  // [B, bt_stride] page indices, or NULL
+  int64_t bt_stride;
+  int page_shift;
+  int snew;                    // tokens appended per sequence (part of every length)
+  int64_t k_sp, v_sp;          // element strides between pages
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -30,6 +44,7 @@ struct FwdParams {
   int num_m_tiles;
   float scale;                // softmax scale
   float scale_log2;           // scale * log2(e)
+  KvCacheParams kv;           // KV-cache kernels only (then Sk bounds every length)
 };
 
 struct BwdParams {
@@ -80,6 +95,20 @@ struct DecodeParams {
   int nsplit, chunk;          // keys [s*chunk, (s+1)*chunk) form split s
   float scale;
   float scale_log2;
+  KvCacheParams kv;           // KV-cache kernels only (then Sk bounds every length)
+};
+
+// Append of new K/V rows into a KV cache: row i of sequence b goes to token
+// position seqlens[b] + i.
+struct KvAppendParams {
+  const void* k_new;
+  const void* v_new;
+  int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;
+  void* k_cache;
+  void* v_cache;
+  int64_t k_ss, k_sh, v_ss, v_sh;
+  KvCacheParams kv;
+  int B, Hkv;
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen,
@@ -92,6 +121,12 @@ hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t s
                                int H, int d, int per_tensor, void* codes, float* scales,
                                hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
+// KV-cache attention: the same kernels reading a paged (or dense) cache with
+// per-sequence lengths seqlens[b] + snew.
+hipError_t launch_decode_bf16_kvcache(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_fwd_bf16_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_bf16_pp_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_kv_append(const KvAppendParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool varlen, int stages,
                            hipStream_t stream);
 // Zero a bf16 [B,S,H,d] tensor with element strides (d contiguous).

@@ -66,7 +66,7 @@ struct FwdTile {
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool KVC>
 __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
@@ -103,13 +103,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
     qtok = qs;
     ktok = ks;
   }
+  if (KVC) Lk = p.kv.seqlens[b] + p.kv.snew;   // cached tokens plus the appended ones
   const int q0 = mt * BM;
   if (q0 >= Lq) return;
   const int diag = Lk - Lq;
 
   const __bf16* qb = (const __bf16*)p.q + (VARLEN ? qtok * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
-  const __bf16* kb = (const __bf16*)p.k + (VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
-  const __bf16* vb = (const __bf16*)p.v + (VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
+  // KV cache: the head's base, rows through the block table
+  const __bf16* kb = (const __bf16*)p.k + (KVC ? 0 : VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (KVC ? 0 : VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
   __bf16* ob = (__bf16*)p.o + (VARLEN ? qtok * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
   float* lseb = p.lse + (VARLEN ? qtok : (int64_t)b * p.lse_sb) + (int64_t)h * p.lse_sh;
 
@@ -153,9 +155,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   auto gload = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) {
-      const uint32_t r = (uint32_t)(j0 + u * T::RPP);
-      kreg[u] = buf_load16(rk, koff + r * (uint32_t)p.k_ss * 2);
-      vreg[u] = buf_load16(rv, voff + r * (uint32_t)p.v_ss * 2);
+      if constexpr (KVC) {
+        // rows past the end read the last row (finite; their scores are masked)
+        const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
+        int64_t page;
+        int slot;
+        kv_page_slot(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, j, page, slot);
+        kreg[u] = *(const u32x4*)(kb + page * p.kv.k_sp + (int64_t)slot * p.k_ss + lcol);
+        vreg[u] = *(const u32x4*)(vb + page * p.kv.v_sp + (int64_t)slot * p.v_ss + lcol);
+      } else {
+        const uint32_t r = (uint32_t)(j0 + u * T::RPP);
+        kreg[u] = buf_load16(rk, koff + r * (uint32_t)p.k_ss * 2);
+        vreg[u] = buf_load16(rv, voff + r * (uint32_t)p.v_ss * 2);
+      }
     }
   };
   auto lstore = [&](int st) {
@@ -290,13 +302,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool KVC = false>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const long nblk = VARLEN ? varlen_grid(p.Hkv * p.B, p.num_m_tiles * p.group, kFwdVarlenRun * p.group)
                            : (long)p.num_m_tiles * p.Hq * p.B;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, KVC>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -309,4 +321,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, 
   }
   if (causal) return varlen ? launch<64, true, true>(p, stream) : launch<64, true, false>(p, stream);
   return varlen ? launch<64, false, true>(p, stream) : launch<64, false, false>(p, stream);
+}
+
+// KV-cache attention with the one-group kernel (d = 64; d = 128 uses the
+// ping-pong kernel).
+hipError_t launch_fwd_bf16_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d != 64) return hipErrorInvalidValue;
+  return causal ? launch<64, true, false, true>(p, stream) : launch<64, false, false, true>(p, stream);
 }

@@ -52,7 +52,7 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool KVC>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   using T = PpTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
@@ -87,13 +87,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     qtok = qs;
     ktok = ks;
   }
+  if (KVC) Lk = p.kv.seqlens[b] + p.kv.snew;   // cached tokens plus the appended ones
   const int q0 = mt * BM;
   if (q0 >= Lq) return;   // workgroup-uniform: no barrier is reached
   const int diag = Lk - Lq;
 
   const __bf16* qb = (const __bf16*)p.q + (VARLEN ? qtok * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
-  const __bf16* kb = (const __bf16*)p.k + (VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
-  const __bf16* vb = (const __bf16*)p.v + (VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
+  // KV cache: the head's base, rows through the block table
+  const __bf16* kb = (const __bf16*)p.k + (KVC ? 0 : VARLEN ? ktok * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.v + (KVC ? 0 : VARLEN ? ktok * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh;
   __bf16* ob = (__bf16*)p.o + (VARLEN ? qtok * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
   float* lseb = p.lse + (VARLEN ? qtok : (int64_t)b * p.lse_sb) + (int64_t)h * p.lse_sh;
 
@@ -131,15 +133,31 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   u32x4 kreg[T::NP], vreg[T::NP];
   auto kstage = [&](int st) { return smem + st * T::KSTAGE; };
   auto vstage = [&](int st) { return smem + 2 * T::KSTAGE + st * T::VSTAGE; };
+  // KV cache: rows past the end read the last row (finite; their scores are
+  // masked)
   auto gload_k = [&](int j0) {
 #pragma unroll
-    for (int u = 0; u < T::NP; ++u)
-      kreg[u] = buf_load16(rk, koff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.k_ss * 2);
+    for (int u = 0; u < T::NP; ++u) {
+      if constexpr (KVC) {
+        const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
+        kreg[u] = *(const u32x4*)(kb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, j,
+                                                        p.kv.k_sp, p.k_ss) + lcol);
+      } else {
+        kreg[u] = buf_load16(rk, koff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.k_ss * 2);
+      }
+    }
   };
   auto gload_v = [&](int j0) {
 #pragma unroll
-    for (int u = 0; u < T::NP; ++u)
-      vreg[u] = buf_load16(rv, voff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.v_ss * 2);
+    for (int u = 0; u < T::NP; ++u) {
+      if constexpr (KVC) {
+        const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
+        vreg[u] = *(const u32x4*)(vb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, j,
+                                                        p.kv.v_sp, p.v_ss) + lcol);
+      } else {
+        vreg[u] = buf_load16(rv, voff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.v_ss * 2);
+      }
+    }
   };
   auto lstore_k = [&](int st) {
     __bf16* Ks = kstage(st);
@@ -342,7 +360,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool KVC = false>
 hipError_t launch(FwdParams p, hipStream_t stream) {
   const int rows = p.Sq;   // dense: Sq; varlen: max query length
   p.num_m_tiles = (rows + BM - 1) / BM;
@@ -350,7 +368,7 @@ hipError_t launch(FwdParams p, hipStream_t stream) {
                            : (long)p.num_m_tiles * p.Hq * p.B;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, VARLEN, KVC>), dim3((unsigned)nblk), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -360,4 +378,11 @@ hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varle
   if (d != 128) return hipErrorInvalidValue;
   if (causal) return varlen ? launch<128, true, true>(p, stream) : launch<128, true, false>(p, stream);
   return varlen ? launch<128, false, true>(p, stream) : launch<128, false, false>(p, stream);
+}
+
+// KV-cache attention (d = 128): the cache pages are read through the block
+// table, each sequence's length is its cached count plus the appended rows.
+hipError_t launch_fwd_bf16_pp_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  return causal ? launch<128, true, false, true>(p, stream) : launch<128, false, false, true>(p, stream);
 }

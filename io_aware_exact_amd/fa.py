@@ -93,13 +93,33 @@ class BwdVarlenArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class FwdKvcacheArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Sq", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("Snew", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float),
+                ("q", FaTensor), ("o", FaTensor), ("lse", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("k_stride_page", ctypes.c_int64), ("k_stride_s", ctypes.c_int64),
+                ("k_stride_h", ctypes.c_int64),
+                ("v_stride_page", ctypes.c_int64), ("v_stride_s", ctypes.c_int64),
+                ("v_stride_h", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
+                ("cache_seqlens", ctypes.c_void_p),
+                ("k_new", FaTensor), ("v_new", FaTensor),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 
 
 # Every symbol include/fa.h declares.
 EXPORTS = ["fa_abi_version", "fa_status_string", "fa_fwd_workspace_size",
            "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
-           "fa_bwd_varlen_workspace_size", "fa_bwd_varlen", "fa_quantize_fp8"]
+           "fa_bwd_varlen_workspace_size", "fa_bwd_varlen", "fa_fwd_kvcache_workspace_size",
+           "fa_fwd_kvcache", "fa_quantize_fp8"]
 
 _lib = None
 
@@ -130,6 +150,10 @@ def lib():
         L.fa_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(BwdVarlenArgs)]
         L.fa_bwd_varlen.restype = ctypes.c_int
         L.fa_bwd_varlen.argtypes = [ctypes.POINTER(BwdVarlenArgs), vp]
+        L.fa_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
+        L.fa_fwd_kvcache_workspace_size.argtypes = [ctypes.POINTER(FwdKvcacheArgs)]
+        L.fa_fwd_kvcache.restype = ctypes.c_int
+        L.fa_fwd_kvcache.argtypes = [ctypes.POINTER(FwdKvcacheArgs), vp]
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         L.fa_quantize_fp8.restype = ctypes.c_int
         L.fa_quantize_fp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
@@ -224,6 +248,61 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                       v.stride(0), v.stride(1), out.stride(0), out.stride(1),
                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), lse.data_ptr())
     _check("fa_fwd_varlen", lib().fa_fwd_varlen(ctypes.byref(a), _stream()))
+    return out, lse
+
+
+def kvcache_args(q, k_cache, v_cache, cache_seqlens, block_table, k_new, v_new, out, lse,
+                 causal, scale, max_seqlen_k=0, workspace=None):
+    """fa_fwd_kvcache_args.  Caches [pages, page_size, Hkv, d] (without a
+    block table: [B, capacity, Hkv, d]); block_table int32 [B, max_pages] or
+    None; cache_seqlens int32 [B]; k_new/v_new [B, Snew, Hkv, d] or None."""
+    B, Sq, Hq, d = q.shape
+    npages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for x in (k_cache, v_cache):
+        assert x.dim() == 4 and x.stride(3) == 1
+    assert cache_seqlens.dtype == torch.int32
+    snew = 0 if k_new is None else k_new.shape[1]
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
+    none4 = FaTensor(None, 0, 0, 0)
+    if block_table is not None:
+        assert block_table.dtype == torch.int32 and block_table.stride(1) == 1
+        bt_ptr, bt_stride, maxp = block_table.data_ptr(), block_table.stride(0), block_table.shape[1]
+    else:
+        bt_ptr, bt_stride, maxp = None, 0, 0
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return FwdKvcacheArgs(dt, B, Sq, Hq, Hkv, d, snew, int(bool(causal)), _scale(d, scale),
+                          _t4(q), _t4(out), lse.data_ptr(),
+                          k_cache.data_ptr(), v_cache.data_ptr(),
+                          k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+                          v_cache.stride(0), v_cache.stride(1), v_cache.stride(2),
+                          npages, page_size, maxp, int(max_seqlen_k), bt_ptr, bt_stride,
+                          cache_seqlens.data_ptr(),
+                          _t4(k_new) if snew else none4, _t4(v_new) if snew else none4,
+                          ws_ptr, ws_bytes)
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=None, v_new=None,
+                causal=False, scale=None, max_seqlen_k=0, out=None, lse=None, workspace=None):
+    """KV-cache attention: appends k_new/v_new ([B,Snew,Hkv,d]) to the cache
+    at positions cache_seqlens[b].., then q [B,Sq,Hq,d] attends to the
+    cache_seqlens[b] + Snew tokens of each sequence (see kvcache_args for the
+    cache layout).  cache_seqlens is not updated.  Returns (o, lse).  When
+    `workspace` is None and the split-KV path applies, one is allocated."""
+    B, Sq, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        a = kvcache_args(q, k_cache, v_cache, cache_seqlens, block_table, k_new, v_new, out, lse,
+                         causal, scale, max_seqlen_k)
+        n = int(lib().fa_fwd_kvcache_workspace_size(ctypes.byref(a)))
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    a = kvcache_args(q, k_cache, v_cache, cache_seqlens, block_table, k_new, v_new, out, lse,
+                     causal, scale, max_seqlen_k, workspace)
+    _check("fa_fwd_kvcache", lib().fa_fwd_kvcache(ctypes.byref(a), _stream()))
     return out, lse
 
 

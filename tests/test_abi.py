@@ -153,3 +153,85 @@ def test_bwd_varlen_null_and_workspace_query():
     assert L.fa_bwd_varlen_workspace_size(None) == 0
     a = bwd_varlen_args(Hq=4, Hkv=2, Tq=1000)
     assert L.fa_bwd_varlen_workspace_size(ctypes.byref(a)) == 4 * 1000 * 4 // 256 * 256 + 256 * (4 * 1000 * 4 % 256 != 0)
+
+
+def kvcache_args(**kw):
+    """fa_fwd_kvcache_args over FAKE pointers: B=2, Sq=1, Hq=4, Hkv=2, d=64,
+    4 pages of 16 tokens, block table [2, 2], Snew=1."""
+    base = dict(dtype=0, B=2, Sq=1, Hq=4, Hkv=2, d=64, Snew=1, causal=1, softmax_scale=0.125,
+                num_pages=4, page_size=16, max_pages_per_seq=2, max_seqlen_k=0,
+                block_table=FAKE + (8 << 24), block_table_stride=2, cache_seqlens=FAKE + (9 << 24),
+                k_stride_page=2048, k_stride_s=128, k_stride_h=64,
+                v_stride_page=2048, v_stride_s=128, v_stride_h=64,
+                k_cache=FAKE + (5 << 24), v_cache=FAKE + (6 << 24), lse=FAKE + (4 << 24),
+                workspace=None, workspace_bytes=0)
+    base.update({k: v for k, v in kw.items() if k in base})
+    q = kw.get("q", fa.FaTensor(FAKE, 256, 256, 64))
+    o = kw.get("o", fa.FaTensor(FAKE + (3 << 24), 256, 256, 64))
+    kn = kw.get("k_new", fa.FaTensor(FAKE + (7 << 24), 128, 128, 64))
+    vn = kw.get("v_new", fa.FaTensor(FAKE + (10 << 24), 128, 128, 64))
+    b = base
+    return fa.FwdKvcacheArgs(b["dtype"], b["B"], b["Sq"], b["Hq"], b["Hkv"], b["d"], b["Snew"],
+                             b["causal"], b["softmax_scale"], q, o, b["lse"], b["k_cache"],
+                             b["v_cache"], b["k_stride_page"], b["k_stride_s"], b["k_stride_h"],
+                             b["v_stride_page"], b["v_stride_s"], b["v_stride_h"], b["num_pages"],
+                             b["page_size"], b["max_pages_per_seq"], b["max_seqlen_k"],
+                             b["block_table"], b["block_table_stride"], b["cache_seqlens"], kn, vn,
+                             b["workspace"], b["workspace_bytes"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 4), (dict(d=96), 3), (dict(Hq=3), 5), (dict(softmax_scale=0.0), 10),
+    (dict(page_size=48), 2),                         # paged: not a power of two
+    (dict(max_pages_per_seq=0), 2), (dict(block_table_stride=1), 2),
+    (dict(block_table=None, num_pages=1), 2),        # dense cache: one page per sequence
+    (dict(max_seqlen_k=33), 2),                      # beyond the capacity 2 x 16
+    (dict(Snew=40), 2), (dict(Sq=-1), 2),
+    (dict(cache_seqlens=None), 1), (dict(k_new=fa.FaTensor(None, 0, 0, 0)), 1),
+    (dict(k_cache=None), 1), (dict(lse=None), 1),
+    (dict(q=fa.FaTensor(FAKE + 8, 256, 256, 64)), 6),
+    (dict(k_stride_s=130), 6), (dict(cache_seqlens=FAKE + (9 << 24) + 2), 6),
+    (dict(workspace=FAKE + (11 << 24) + 16, workspace_bytes=4096), 6),
+    (dict(o=fa.FaTensor(FAKE + 64, 256, 256, 64)), 8),             # o overlaps q
+    (dict(k_new=fa.FaTensor(FAKE + (5 << 24) + 256, 128, 128, 64)), 8),   # k_new in the cache
+    (dict(lse=FAKE + (6 << 24) + 64), 8),                          # lse in the V cache
+])
+def test_kvcache_rejects(kw, status):
+    a = kvcache_args(**kw)
+    assert fa.lib().fa_fwd_kvcache(ctypes.byref(a), None) == status
+
+
+def test_kvcache_noop_and_workspace_query():
+    assert fa.lib().fa_fwd_kvcache(None, None) == 1
+    a = kvcache_args(B=0)
+    assert fa.lib().fa_fwd_kvcache(ctypes.byref(a), None) == 0
+    # decode-shaped (Sq * group = 2 <= 32): a split-KV workspace; prefill-shaped: none
+    assert fa.lib().fa_fwd_kvcache_workspace_size(ctypes.byref(kvcache_args())) > 0
+    big = kvcache_args(Sq=64, q=fa.FaTensor(FAKE, 16384, 256, 64), o=fa.FaTensor(FAKE + (3 << 24), 16384, 256, 64))
+    assert fa.lib().fa_fwd_kvcache_workspace_size(ctypes.byref(big)) == 0
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Every ctypes argument structure has the header's size and field offsets
+    (checked with the host C compiler)."""
+    structs = {"fa_fwd_args": fa.FwdArgs, "fa_fwd_varlen_args": fa.FwdVarlenArgs,
+               "fa_bwd_args": fa.BwdArgs, "fa_bwd_varlen_args": fa.BwdVarlenArgs,
+               "fa_fwd_kvcache_args": fa.FwdKvcacheArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fa.h"', 'int main(void) {']
+    expect = []
+    for cname, cls in structs.items():
+        lines.append(f'  printf("%zu\\n", sizeof({cname}));')
+        expect.append(ctypes.sizeof(cls))
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("%zu\\n", offsetof({cname}, {fname}));')
+            expect.append(getattr(cls, fname).offset)
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == expect

@@ -197,6 +197,51 @@ def leg_varlen(reps):
             "fwd_bwd_tflops_exact_pairs": round(14.0 * Hq * d * pairs / (ms + ms_b) / 1e9, 2)}
 
 
+def leg_kvcache(reps):
+    """KV-cache attention (fa_fwd_kvcache) on a paged cache of 256-token pages
+    handed out in a shuffled order (seed 3201):
+    decode -- B=64, Hq=32, Hkv=8, d=128, 32767 cached tokens plus one
+    appended per sequence (the dense decode's workload, read through the
+    block table; the append is inside the timed call);
+    prefill -- B=4 sequences with 15360 cached tokens and a 1024-token chunk
+    appended and attended causally (Sq = Snew = 1024)."""
+    from io_aware_exact_amd import fa
+    out = {}
+    Hq, Hkv, d, ps = 32, 8, 128, 256
+    for name, B, L, sq in (("decode", 64, 32767, 1), ("prefill", 4, 15360, 1024)):
+        per = (L + sq + ps - 1) // ps
+        g = torch.Generator(device="cuda")
+        g.manual_seed(3200)
+        kc = torch.randn((B * per, ps, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        vc = torch.randn((B * per, ps, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        q = torch.randn((B, sq, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+        kn = torch.randn((B, sq, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        vn = torch.randn((B, sq, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        gc = torch.Generator(device="cpu")
+        gc.manual_seed(3201)
+        bt = torch.randperm(B * per, generator=gc).to(torch.int32).view(B, per).cuda()
+        lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, sq), dtype=torch.float32, device="cuda")
+        a = fa.kvcache_args(q, kc, vc, lens, bt, kn, vn, o, lse, True, None)
+        n = int(fa.lib().fa_fwd_kvcache_workspace_size(ctypes.byref(a)))
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+        ms = time_calls(lambda: fa.fwd_kvcache(q, kc, vc, lens, bt, kn, vn, True, out=o, lse=lse,
+                                               workspace=ws), reps)
+        Lk = L + sq
+        kv_bytes = 2 * B * Lk * Hkv * d * 2
+        io_bytes = kv_bytes + 2 * B * sq * Hq * d * 2 + B * Hq * sq * 4 + 2 * B * sq * Hkv * d * 2
+        pairs = B * sum(min(Lk, i + 1 + Lk - sq) for i in range(sq))
+        out[name] = {"workload": f"paged KV cache B={B} cached={L} new={sq} Hq={Hq} Hkv={Hkv} "
+                                 f"d={d} page={ps} causal",
+                     "ms": round(ms, 4), "gbps": round(io_bytes / ms / 1e6, 1),
+                     "frac_of_hbm": round(io_bytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
+                     "tflops": round(4.0 * Hq * d * pairs / ms / 1e9, 2)}
+        del kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
 def leg_fp8(reps):
     """FP8 (E4M3, per-block scales) forward: B=1, H=16, S=16384, d=128,
     non-causal, inputs N(0,1) + Bernoulli(0.001) N(0,100) (seed 4000).
@@ -259,7 +304,8 @@ def extra_legs(args):
     if args.only in ("fwd", "fwdbwd"):
         return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
     for name, fn, reps in (("causal", leg_causal, 10), ("decode", leg_decode, 20),
-                           ("varlen", leg_varlen, 5), ("fp8", leg_fp8, 10),
+                           ("varlen", leg_varlen, 5), ("kvcache", leg_kvcache, 10),
+                           ("fp8", leg_fp8, 10),
                            ("sweep", leg_sweep, 5)):
         if args.only and args.only != name:
             continue
@@ -276,7 +322,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
-    ap.add_argument("--only", choices=["decode", "varlen", "causal", "fp8", "sweep", "fwd",
+    ap.add_argument("--only", choices=["decode", "varlen", "kvcache", "causal", "fp8", "sweep", "fwd",
                                        "fwdbwd"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -389,7 +435,7 @@ def main():
                      "achieved": round(dk_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dk_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile("bwd_dkdv_b2_h16_s8192_d128", BWD_SOURCES)},
-        "roofline_fwd": {"kernel": "fwd_bf16_pp_kernel<128,false,false>", "bound": "mfma",
+        "roofline_fwd": {"kernel": "fwd_bf16_pp_kernel<128,false,false,false>", "bound": "mfma",
                          "achieved": tf(ff, ms_fwd), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profile("fwd_bf16_b2_h16_s8192_d128", FWD_SOURCES)},

@@ -365,7 +365,11 @@ fa_status check_kvcache(const fa_fwd_kvcache_args* a) {
     return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
   if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (!fits32(a->Sq, a->q.stride_s, 2) || !fits32(a->Sq, a->o.stride_s, 2)) return FA_ERR_SHAPE;
+  // q and o slices, and one page (or a dense cache's rows), are addressed
+  // with 32-bit byte offsets
+  if (!fits32(a->Sq, a->q.stride_s, 2) || !fits32(a->Sq, a->o.stride_s, 2) ||
+      !fits32(a->page_size, a->k_stride_s, 2) || !fits32(a->page_size, a->v_stride_s, 2))
+    return FA_ERR_SHAPE;
   const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
   const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
   const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2);

@@ -110,33 +110,67 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int vcol = (lane % T::CH) * 8;
   bf16x8 kf[T::NC];
   u32x4 vreg[T::NP];
-  // KV cache: the head's base; rows through the block table (Lk >= 1
-  // whenever a block is loaded)
+  // KV cache.  Without a block table the sequence's cache is one dense
+  // region, read exactly like the dense path.  With pages of >= 32 tokens a
+  // block (32 keys from a multiple of 32) lies in one page: its page number
+  // comes from a window of block-table entries held one per lane, and its
+  // rows are read through a buffer resource over the page's rows that hold
+  // tokens (rows past the end read as zero, as in the dense path).  Smaller
+  // pages: every row's page comes from the window by a cross-lane permute,
+  // and rows past the end read the last row (finite; their scores are
+  // masked).  Lk >= 1 whenever a block is loaded.
   const __bf16* kcb = (const __bf16*)p.k + (int64_t)g * p.k_sh;
   const __bf16* vcb = (const __bf16*)p.v + (int64_t)g * p.v_sh;
+  const bool paged = KVC && p.kv.block_table != nullptr;
+  const int shift = p.kv.page_shift;
+  const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
+  const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
+  PageWindow win;
+  __amdgpu_buffer_rsrc_t rkc = rk, rvc = rv;
+  if (KVC && !paged) {
+    rkc = make_rsrc(kcb + (int64_t)b * p.kv.k_sp, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+    rvc = make_rsrc(vcb + (int64_t)b * p.kv.v_sp, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  }
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rkk, const __amdgpu_buffer_rsrc_t& rvv, int r0) {
+    const uint32_t kr = (uint32_t)(r0 + kp);
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c)
+      kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rkk, (kr * (uint32_t)p.k_ss + 16 * c + 8 * hh) * 2));
+#pragma unroll
+    for (int u = 0; u < T::NP; ++u) {
+      const uint32_t r = (uint32_t)(r0 + vrow + u * T::RPP);
+      vreg[u] = buf_load16(rvv, (r * (uint32_t)p.v_ss + vcol) * 2);
+    }
+  };
   auto gload = [&](int j0) {
     if constexpr (KVC) {
-      const int jk = min(j0 + kp, Lk - 1);
-      const __bf16* kr = kcb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, jk,
-                                               p.kv.k_sp, p.k_ss);
+      if (!paged) {
+        load_rows(rkc, rvc, j0);
+      } else if (shift >= 5) {
+        const int pn = j0 >> shift;
+        win.cover(btrow, pn, pn, last_page_no, lane);
+        const int64_t page = win.uniform(pn);
+        const int first_tok = pn << shift;
+        const int rows = min(Lk - first_tok, 1 << shift);
+        const __amdgpu_buffer_rsrc_t rkp = make_rsrc(kcb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2));
+        const __amdgpu_buffer_rsrc_t rvp = make_rsrc(vcb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2));
+        load_rows(rkp, rvp, j0 - first_tok);
+      } else {
+        win.cover(btrow, j0 >> shift, min(j0 + BNK - 1, Lk - 1) >> shift, last_page_no, lane);
+        const int mask = (1 << shift) - 1;
+        const int jk = min(j0 + kp, Lk - 1);
+        const __bf16* kr = kcb + (int64_t)win.per_lane(jk >> shift) * p.kv.k_sp + (int64_t)(jk & mask) * p.k_ss;
 #pragma unroll
-      for (int c = 0; c < T::NC; ++c) kf[c] = *(const bf16x8*)(kr + 16 * c + 8 * hh);
+        for (int c = 0; c < T::NC; ++c) kf[c] = *(const bf16x8*)(kr + 16 * c + 8 * hh);
 #pragma unroll
-      for (int u = 0; u < T::NP; ++u) {
-        const int jv = min(j0 + vrow + u * T::RPP, Lk - 1);
-        vreg[u] = *(const u32x4*)(vcb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift,
-                                                         b, jv, p.kv.v_sp, p.v_ss) + vcol);
+        for (int u = 0; u < T::NP; ++u) {
+          const int jv = min(j0 + vrow + u * T::RPP, Lk - 1);
+          vreg[u] = *(const u32x4*)(vcb + (int64_t)win.per_lane(jv >> shift) * p.kv.v_sp +
+                                    (int64_t)(jv & mask) * p.v_ss + vcol);
+        }
       }
     } else {
-      const uint32_t kr = (uint32_t)(j0 + kp);
-#pragma unroll
-      for (int c = 0; c < T::NC; ++c)
-        kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rk, (kr * (uint32_t)p.k_ss + 16 * c + 8 * hh) * 2));
-#pragma unroll
-      for (int u = 0; u < T::NP; ++u) {
-        const uint32_t r = (uint32_t)(j0 + vrow + u * T::RPP);
-        vreg[u] = buf_load16(rv, (r * (uint32_t)p.v_ss + vcol) * 2);
-      }
+      load_rows(rk, rv, j0);
     }
   };
   const int trG = lane >> 4;

@@ -145,3 +145,28 @@ __device__ __forceinline__ int64_t kv_token_offset(const int32_t* block_table, i
   kv_page_slot(block_table, bt_stride, page_shift, b, j, page, slot);
   return page * page_stride + (int64_t)slot * token_stride;
 }
+
+// A window of up to 64 consecutive page numbers of one sequence's block-table
+// row, one per lane of a wave: lane i holds the page of page number base + i
+// (clamped to the sequence's last page, so no entry past it is read).  A
+// refill is one vector load; lookups are a lane read (same page number across
+// the wave) or a cross-lane permute (per-lane page numbers).
+struct PageWindow {
+  int base = -1;
+  int pages = 0;
+  // make page numbers first..last available (uniform; last - first < 64)
+  __device__ __forceinline__ void cover(const int32_t* row, int first, int last, int max_page_no,
+                                        int lane) {
+    if (base < 0 || first < base || last >= base + 64) {
+      base = first;
+      pages = row[min(first + lane, max_page_no)];
+    }
+  }
+  __device__ __forceinline__ int uniform(int page_no) const {
+    return __builtin_amdgcn_readlane(pages, page_no - base);
+  }
+  // every lane of the wave must take part
+  __device__ __forceinline__ int per_lane(int page_no) const {
+    return __builtin_amdgcn_ds_bpermute((page_no - base) << 2, pages);
+  }
+};

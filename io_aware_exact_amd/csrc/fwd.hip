@@ -152,22 +152,56 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
   const uint32_t koff = (uint32_t)(lrow * p.k_ss + lcol) * 2;
   const uint32_t voff = (uint32_t)(lrow * p.v_ss + lcol) * 2;
   u32x4 kreg[T::NP], vreg[T::NP];
-  auto gload = [&](int j0) {
+  // KV cache.  Without a block table the sequence's cache is one dense
+  // region, read like the dense path.  With pages of >= 64 tokens a tile (64
+  // keys from a multiple of 64) lies in one page, found in a window of
+  // block-table entries held one per lane and read through a buffer resource
+  // over the page's rows that hold tokens (rows past the end read as zero).
+  // Smaller pages: each row's page comes from the window by a cross-lane
+  // permute, and rows past the end read the last row (finite; masked).
+  const bool paged = KVC && p.kv.block_table != nullptr;
+  const int shift = p.kv.page_shift;
+  const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
+  const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
+  PageWindow win;
+  __amdgpu_buffer_rsrc_t rkc = rk, rvc = rv;
+  if (KVC && !paged) {
+    rkc = make_rsrc(kb + (int64_t)b * p.kv.k_sp, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+    rvc = make_rsrc(vb + (int64_t)b * p.kv.v_sp, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  }
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rkk, const __amdgpu_buffer_rsrc_t& rvv, int r0) {
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) {
-      if constexpr (KVC) {
-        // rows past the end read the last row (finite; their scores are masked)
-        const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
-        int64_t page;
-        int slot;
-        kv_page_slot(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, j, page, slot);
-        kreg[u] = *(const u32x4*)(kb + page * p.kv.k_sp + (int64_t)slot * p.k_ss + lcol);
-        vreg[u] = *(const u32x4*)(vb + page * p.kv.v_sp + (int64_t)slot * p.v_ss + lcol);
+      const uint32_t r = (uint32_t)(r0 + u * T::RPP);
+      kreg[u] = buf_load16(rkk, koff + r * (uint32_t)p.k_ss * 2);
+      vreg[u] = buf_load16(rvv, voff + r * (uint32_t)p.v_ss * 2);
+    }
+  };
+  auto gload = [&](int j0) {
+    if constexpr (KVC) {
+      if (!paged) {
+        load_rows(rkc, rvc, j0);
+      } else if (shift >= 6) {
+        const int pn = j0 >> shift;
+        win.cover(btrow, pn, pn, last_page_no, lane);
+        const int64_t page = win.uniform(pn);
+        const int first_tok = pn << shift;
+        const int rows = min(Lk - first_tok, 1 << shift);
+        load_rows(make_rsrc(kb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2)),
+                  make_rsrc(vb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2)), j0 - first_tok);
       } else {
-        const uint32_t r = (uint32_t)(j0 + u * T::RPP);
-        kreg[u] = buf_load16(rk, koff + r * (uint32_t)p.k_ss * 2);
-        vreg[u] = buf_load16(rv, voff + r * (uint32_t)p.v_ss * 2);
+        win.cover(btrow, j0 >> shift, min(j0 + BN - 1, Lk - 1) >> shift, last_page_no, lane);
+        const int mask = (1 << shift) - 1;
+#pragma unroll
+        for (int u = 0; u < T::NP; ++u) {
+          const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
+          const int64_t page = win.per_lane(j >> shift);
+          kreg[u] = *(const u32x4*)(kb + page * p.kv.k_sp + (int64_t)(j & mask) * p.k_ss + lcol);
+          vreg[u] = *(const u32x4*)(vb + page * p.kv.v_sp + (int64_t)(j & mask) * p.v_ss + lcol);
+        }
       }
+    } else {
+      load_rows(rk, rv, j0);
     }
   };
   auto lstore = [&](int st) {

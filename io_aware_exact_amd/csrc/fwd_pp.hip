@@ -133,32 +133,56 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   u32x4 kreg[T::NP], vreg[T::NP];
   auto kstage = [&](int st) { return smem + st * T::KSTAGE; };
   auto vstage = [&](int st) { return smem + 2 * T::KSTAGE + st * T::VSTAGE; };
-  // KV cache: rows past the end read the last row (finite; their scores are
-  // masked)
-  auto gload_k = [&](int j0) {
+  // KV cache.  Without a block table the sequence's cache is one dense
+  // region, read like the dense path.  With pages of >= 64 tokens a tile (64
+  // keys from a multiple of 64) lies in one page, found in a window of
+  // block-table entries held one per lane and read through a buffer resource
+  // over the page's rows that hold tokens (rows past the end read as zero).
+  // Smaller pages: each row's page comes from the window by a cross-lane
+  // permute, and rows past the end read the last row (finite; masked).
+  const bool paged = KVC && p.kv.block_table != nullptr;
+  const int shift = p.kv.page_shift;
+  const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
+  const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
+  PageWindow win;
+  __amdgpu_buffer_rsrc_t rkc = rk, rvc = rv;
+  if (KVC && !paged) {
+    rkc = make_rsrc(kb + (int64_t)b * p.kv.k_sp, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+    rvc = make_rsrc(vb + (int64_t)b * p.kv.v_sp, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  }
+  // one operand (K or V) of the tile at key j0
+  auto gload_one = [&](u32x4 (&regs)[T::NP], const __amdgpu_buffer_rsrc_t& rd, uint32_t off,
+                       const __bf16* base, int64_t sp, int64_t ss, int j0) {
+    if constexpr (KVC) {
+      if (!paged) {
 #pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      if constexpr (KVC) {
-        const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
-        kreg[u] = *(const u32x4*)(kb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, j,
-                                                        p.kv.k_sp, p.k_ss) + lcol);
+        for (int u = 0; u < T::NP; ++u) regs[u] = buf_load16(rd, off + (uint32_t)(j0 + u * T::RPP) * (uint32_t)ss * 2);
+      } else if (shift >= 6) {
+        const int pn = j0 >> shift;
+        win.cover(btrow, pn, pn, last_page_no, lane);
+        const int64_t page = win.uniform(pn);
+        const int first_tok = pn << shift;
+        const int rows = min(Lk - first_tok, 1 << shift);
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(base + page * sp, (uint32_t)(rows * ss * 2));
+#pragma unroll
+        for (int u = 0; u < T::NP; ++u)
+          regs[u] = buf_load16(rp, off + (uint32_t)(j0 - first_tok + u * T::RPP) * (uint32_t)ss * 2);
       } else {
-        kreg[u] = buf_load16(rk, koff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.k_ss * 2);
+        win.cover(btrow, j0 >> shift, min(j0 + BN - 1, Lk - 1) >> shift, last_page_no, lane);
+        const int mask = (1 << shift) - 1;
+#pragma unroll
+        for (int u = 0; u < T::NP; ++u) {
+          const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
+          regs[u] = *(const u32x4*)(base + (int64_t)win.per_lane(j >> shift) * sp + (int64_t)(j & mask) * ss + lcol);
+        }
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < T::NP; ++u) regs[u] = buf_load16(rd, off + (uint32_t)(j0 + u * T::RPP) * (uint32_t)ss * 2);
     }
   };
-  auto gload_v = [&](int j0) {
-#pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      if constexpr (KVC) {
-        const int j = min(j0 + lrow + u * T::RPP, Lk - 1);
-        vreg[u] = *(const u32x4*)(vb + kv_token_offset(p.kv.block_table, p.kv.bt_stride, p.kv.page_shift, b, j,
-                                                        p.kv.v_sp, p.v_ss) + lcol);
-      } else {
-        vreg[u] = buf_load16(rv, voff + (uint32_t)(j0 + u * T::RPP) * (uint32_t)p.v_ss * 2);
-      }
-    }
-  };
+  auto gload_k = [&](int j0) { gload_one(kreg, KVC ? rkc : rk, koff, kb, p.kv.k_sp, p.k_ss, j0); };
+  auto gload_v = [&](int j0) { gload_one(vreg, KVC ? rvc : rv, voff, vb, p.kv.v_sp, p.v_ss, j0); };
   auto lstore_k = [&](int st) {
     __bf16* Ks = kstage(st);
 #pragma unroll

@@ -101,3 +101,67 @@ def dequantize_blocks(codes, scales, block=128):
     B, S, H, d = codes.shape
     tok_scale = np.repeat(np.asarray(scales, np.float64), block, axis=2)[:, :, :S]
     return decode_e4m3(codes) * tok_scale.transpose(0, 2, 1)[..., None]
+
+
+# ---- MX (OCP microscaling) FP8 ------------------------------------------------
+# Native block scaling of gfx950's scaled FP8 matrix instruction: E4M3
+# elements, one E8M0 scale (a power of two, byte = exponent + 127) per block
+# of 32 consecutive elements along the reduction dimension.  Readings (the
+# pages fix no format):
+#   * the shared exponent is floor(log2(amax)) - 8, 8 being the exponent of
+#     E4M3's largest normal, so the block maximum lands in E4M3's top binade;
+#   * elements are x / 2^e (fp32) encoded as above (nearest, ties to even,
+#     saturating to +-448);
+#   * a block of zeros gets exponent 0; exponents are clamped to [-127, 127];
+#   * Q and K blocks run along d (scales [B, S, H, d/32]); V blocks run along
+#     the tokens, the reduction dimension of P V (scales [B, H, ceil(S/32), d];
+#     the last block may be partial).
+MX_BLOCK = 32
+E4M3_EMAX = 8
+
+
+def mx_exponent(amax):
+    """Shared exponents floor(log2(amax)) - 8 of blocks with maxima amax
+    (0 for a zero block), clamped to [-127, 127]."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, k = np.frexp(amax)                 # amax = f 2^k with f in [0.5, 1)
+    e = np.where(amax > 0, (k - 1) - E4M3_EMAX, 0)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_mx(x, axis):
+    """x [B,S,H,d] fp32.  axis "d": blocks of 32 along d -> (codes [B,S,H,d],
+    scale bytes uint8 [B,S,H,d/32]).  axis "s": blocks of 32 tokens for each
+    (batch, head, d) -> (codes, scale bytes uint8 [B,H,ceil(S/32),d])."""
+    x = np.asarray(x, dtype=np.float32)
+    B, S, H, d = x.shape
+    if axis == "d":
+        assert d % MX_BLOCK == 0
+        blk = np.abs(x).reshape(B, S, H, d // MX_BLOCK, MX_BLOCK).max(axis=4)
+        e = mx_exponent(blk)                                   # [B,S,H,d/32]
+        e_el = np.repeat(e, MX_BLOCK, axis=3)                   # [B,S,H,d]
+        scales = (e + 127).astype(np.uint8)
+    elif axis == "s":
+        nb = (S + MX_BLOCK - 1) // MX_BLOCK
+        e = np.zeros((B, H, nb, d), dtype=np.int64)
+        for t in range(nb):
+            amax = np.abs(x[:, t * MX_BLOCK:(t + 1) * MX_BLOCK]).max(axis=1)   # [B,H,d]
+            e[:, :, t, :] = mx_exponent(amax)
+        e_el = np.repeat(e, MX_BLOCK, axis=2)[:, :, :S, :].transpose(0, 2, 1, 3)   # [B,S,H,d]
+        scales = (e + 127).astype(np.uint8)
+    else:
+        raise ValueError(axis)
+    y = (x / np.exp2(e_el).astype(np.float32)).astype(np.float32)
+    return encode_e4m3(y), scales
+
+
+def dequantize_mx(codes, scales, axis):
+    """Inverse of quantize_mx: E4M3 value times 2^(byte - 127), float64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    B, S, H, d = codes.shape
+    e = np.asarray(scales, dtype=np.int64) - 127
+    if axis == "d":
+        e_el = np.repeat(e, MX_BLOCK, axis=3)
+    else:
+        e_el = np.repeat(e, MX_BLOCK, axis=2)[:, :, :S, :].transpose(0, 2, 1, 3)
+    return decode_e4m3(codes) * np.exp2(e_el.astype(np.float64))

@@ -56,3 +56,61 @@ def test_block_scales_and_roundtrip():
     assert (err <= bound + 1e-12).all()
     # every block's largest element maps to +-448 exactly
     assert np.abs(codes[0, :128, 0].astype(np.int32) & 0x7F).max() == 0x7E
+
+
+# ---- MX (microscaling) FP8 pins ----------------------------------------------
+
+def mx_case(seed, shape):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g) * torch.exp(torch.randn(*shape, generator=g) * 2)
+    return x.numpy().astype(np.float32)
+
+
+def test_mx_exponent_closed_form():
+    # the block maximum's binade maps onto E4M3's top binade [256, 512)
+    amax = np.array([1.0, 1.5, 0.75, 448.0, 512.0, 2.0 ** -100, 3.0e38, 0.0])
+    e = fp8.mx_exponent(amax)
+    assert list(e) == [-8, -8, -9, 0, 1, -108, 119, 0]
+    nz = amax > 0
+    r = amax[nz] / np.exp2(e[nz].astype(np.float64))
+    assert ((r >= 256) & (r < 512)).all()
+    assert fp8.mx_exponent(np.array([2.0 ** -130]))[0] == -127   # clamped
+
+
+def test_mx_codes_match_torch_cast():
+    # codes are torch's own e4m3fn cast of x / 2^e (clamped to the finite range)
+    x = mx_case(2, (2, 40, 3, 64))
+    codes, sc = fp8.quantize_mx(x, "d")
+    assert sc.shape == (2, 40, 3, 2) and sc.dtype == np.uint8
+    e = np.repeat(sc.astype(np.int64) - 127, 32, axis=3)
+    y = torch.from_numpy((x / np.exp2(e).astype(np.float32)).astype(np.float32)).clamp(-448, 448)
+    ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (codes == ref).all()
+    amax = np.abs(x).reshape(2, 40, 3, 2, 32).max(axis=4)
+    assert (sc == (np.floor(np.log2(amax)) - 8 + 127).astype(np.uint8)).all()
+
+
+def test_mx_token_blocks_and_roundtrip():
+    # V: blocks of 32 tokens per (batch, head, d), a partial last block, a zero block
+    x = mx_case(3, (1, 70, 2, 64))
+    x[0, 32:64, 1, 5] = 0.0
+    codes, sc = fp8.quantize_mx(x, "s")
+    assert sc.shape == (1, 2, 3, 64)
+    assert sc[0, 1, 1, 5] == 127 and (codes[0, 32:64, 1, 5] & 0x7F == 0).all()
+    amax_tail = np.abs(x[0, 64:70, 0, 7]).max()
+    assert sc[0, 0, 2, 7] == int(np.floor(np.log2(amax_tail))) - 8 + 127
+    xd = fp8.dequantize_mx(codes, sc, "s")
+    e_el = np.repeat(sc.astype(np.int64) - 127, 32, axis=2)[:, :, :70].transpose(0, 2, 1, 3)
+    step = np.exp2(e_el.astype(np.float64))
+    # below E4M3's top binade the rounding error is at most half a step of
+    # 3 mantissa bits (2^-4 relative) or half the subnormal spacing 2^-10;
+    # the top binade saturates at 448, an error below 64 steps
+    err = np.abs(xd - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, step * 2.0 ** -10)
+    sat = np.abs(x) / step > 448
+    assert (err[~sat] <= bound[~sat] + 1e-300).all()
+    assert (err[sat] <= 64 * step[sat]).all()
+    # every nonzero block's largest element decodes into E4M3's top binade
+    top = np.abs(codes[0, :32, 0, 0].astype(np.int32) & 0x7F).max()
+    assert (top >> 3) == 15
+

@@ -261,6 +261,29 @@ typedef struct {
   size_t workspace_bytes;
 } fa_fwd_kvcache_args;
 
+/* MX FP8 forward: gfx950's native block scaling (OCP microscaling).  q, k
+ * and v hold OCP E4M3 codes (fa_tensor strides in bytes, 16-byte rows); each
+ * block of 32 consecutive elements along a product's reduction dimension
+ * carries one E8M0 scale byte (real value 2^(byte - 127); 255 is not
+ * allowed):
+ *   q_scale [B, Sq, Hq, d/32] and k_scale [B, Sk, Hkv, d/32]: blocks along d;
+ *   v_scale [B, Hkv, ceil(Sk/32), d]: blocks of 32 keys for each d column;
+ * all uint8, contiguous, 4-byte aligned (fa_quantize_mxfp8 writes them).
+ * Both products run on the scaled MFMA with these per-block scales; the
+ * probabilities are rounded to E4M3 after a 2^8 prescale, as in fa_fwd's
+ * FP8 path.  o [B,Sq,Hq,d] bf16, lse [B,Hq,Sq] fp32.  d is 64 or 128; the
+ * other rules and errors are fa_fwd's. */
+typedef struct {
+  int32_t B, Sq, Sk, Hq, Hkv, d;
+  int32_t causal;
+  float softmax_scale;
+  fa_tensor q, k, v, o;
+  float* lse;
+  const uint8_t* q_scale;
+  const uint8_t* k_scale;
+  const uint8_t* v_scale;
+} fa_fwd_mxfp8_args;
+
 /* Returns FA_ABI_VERSION. */
 int32_t fa_abi_version(void);
 
@@ -317,6 +340,25 @@ fa_status fa_quantize_fp8(const float* x, int64_t stride_b, int64_t stride_s,
                           int64_t stride_h, int32_t B, int32_t S, int32_t H,
                           int32_t d, int32_t per_tensor, void* codes,
                           float* scales, hipStream_t stream);
+
+/* MX FP8 forward; see fa_fwd_mxfp8_args. */
+fa_status fa_fwd_mxfp8(const fa_fwd_mxfp8_args* args, hipStream_t stream);
+
+/* MX FP8 quantiser (input preparation for fa_fwd_mxfp8).  x [B,S,H,d] fp32
+ * with element strides (d contiguous, 4-byte aligned) -> codes [B,S,H,d] e4m3
+ * contiguous (16-byte aligned) and E8M0 scale bytes (4-byte aligned):
+ *   axis 0: blocks of 32 along d (for q and k), scales [B,S,H,d/32];
+ *   axis 1: blocks of 32 tokens along S for each (b, h, d column) (for v),
+ *           scales [B,H,ceil(S/32),d]; the last block may be partial.
+ * Per block, e = floor(log2(amax)) - 8 (8: the exponent of E4M3's largest
+ * normal), clamped to [-127, 127], and 0 for an all-zero block; the scale
+ * byte is e + 127 and the codes are the nearest e4m3 values of x * 2^-e,
+ * ties to the even code, saturating to +-448.  d is a multiple of 32, at most
+ * 256.  x, codes and scales must not overlap.  Deterministic. */
+fa_status fa_quantize_mxfp8(const float* x, int64_t stride_b, int64_t stride_s,
+                            int64_t stride_h, int32_t B, int32_t S, int32_t H,
+                            int32_t d, int32_t axis, void* codes,
+                            uint8_t* scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -625,6 +625,68 @@ fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, in
   return hip_status(launch_quantize_fp8(x, sb, ss, sh, B, S, H, d, per_tensor != 0, codes, scales, stream));
 }
 
+fa_status fa_fwd_mxfp8(const fa_fwd_mxfp8_args* a, hipStream_t stream) {
+  if (!a) return FA_ERR_NULL;
+  // the dense FP8 rules (shapes, strides in bytes, alignment, aliasing)
+  fa_fwd_args f = {};
+  f.dtype = FA_FP8_E4M3;
+  f.B = a->B; f.Sq = a->Sq; f.Sk = a->Sk; f.Hq = a->Hq; f.Hkv = a->Hkv; f.d = a->d;
+  f.causal = a->causal;
+  f.softmax_scale = a->softmax_scale;
+  f.q = a->q; f.k = a->k; f.v = a->v; f.o = a->o;
+  f.lse = a->lse;
+  f.q_descale = (const float*)a->q_scale;
+  f.k_descale = (const float*)a->k_scale;
+  f.v_descale = (const float*)a->v_scale;
+  const fa_status s = check_fwd(&f);
+  if (s != FA_OK) return s;
+  if (a->B == 0 || a->Sq == 0) return FA_OK;
+  const int64_t nb = a->d / 32;
+  const Span sqs = {(uintptr_t)a->q_scale, (uintptr_t)(a->q_scale + (int64_t)a->B * a->Sq * a->Hq * nb)};
+  const Span sks = {(uintptr_t)a->k_scale, (uintptr_t)(a->k_scale + (int64_t)a->B * a->Sk * a->Hkv * nb)};
+  const Span svs = {(uintptr_t)a->v_scale,
+                    (uintptr_t)(a->v_scale + (int64_t)a->B * a->Hkv * ((a->Sk + 31) / 32) * a->d)};
+  const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
+  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
+  const Span sc[3] = {sqs, sks, svs};
+  for (const Span& x : sc)
+    if (overlap(x, so) || overlap(x, sl)) return FA_ERR_ALIAS;
+  FwdParams p = {};
+  p.q = a->q.ptr; p.k = a->k.ptr; p.v = a->v.ptr; p.o = a->o.ptr; p.lse = a->lse;
+  p.q_sb = a->q.stride_b; p.q_ss = a->q.stride_s; p.q_sh = a->q.stride_h;
+  p.k_sb = a->k.stride_b; p.k_ss = a->k.stride_s; p.k_sh = a->k.stride_h;
+  p.v_sb = a->v.stride_b; p.v_ss = a->v.stride_s; p.v_sh = a->v.stride_h;
+  p.o_sb = a->o.stride_b; p.o_ss = a->o.stride_s; p.o_sh = a->o.stride_h;
+  p.lse_sb = (int64_t)a->Hq * a->Sq;
+  p.lse_sh = a->Sq;
+  p.B = a->B; p.Sq = a->Sq; p.Sk = a->Sk; p.Hq = a->Hq; p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.num_m_tiles = (a->Sq + kBM - 1) / kBM;
+  p.scale = a->softmax_scale;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.q_e8m0 = a->q_scale;
+  p.k_e8m0 = a->k_scale;
+  p.v_e8m0 = a->v_scale;
+  return hip_status(launch_fwd_mxfp8(p, a->d, a->causal != 0, stream));
+}
+
+fa_status fa_quantize_mxfp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int32_t B, int32_t S,
+                            int32_t H, int32_t d, int32_t axis, void* codes, uint8_t* scales,
+                            hipStream_t stream) {
+  if (!x || !codes || !scales) return FA_ERR_NULL;
+  if (B < 0 || S < 0 || H < 1 || (axis != 0 && axis != 1)) return FA_ERR_SHAPE;
+  if (d < 32 || d > 256 || d % 32 != 0) return FA_ERR_HEADDIM;
+  if (sb < 0 || ss < 0 || sh < 0) return FA_ERR_SHAPE;
+  if (((uintptr_t)x & 3u) || ((uintptr_t)codes & 15u) || ((uintptr_t)scales & 3u)) return FA_ERR_ALIGN;
+  if (B == 0 || S == 0) return FA_OK;
+  const int64_t nsc = axis == 0 ? (int64_t)B * S * H * (d / 32) : (int64_t)B * H * ((S + 31) / 32) * d;
+  const Span sx = span4(x, B, S, H, d, sb, ss, sh, 4);
+  const Span sc = {(uintptr_t)codes, (uintptr_t)codes + (uintptr_t)((int64_t)B * S * H * d)};
+  const Span ss_ = {(uintptr_t)scales, (uintptr_t)scales + (uintptr_t)nsc};
+  if (overlap(sx, sc) || overlap(sx, ss_) || overlap(sc, ss_)) return FA_ERR_ALIAS;
+  return hip_status(launch_quantize_mxfp8(x, sb, ss, sh, B, S, H, d, axis, codes, scales, stream));
+}
+
 size_t fa_fwd_kvcache_workspace_size(const fa_fwd_kvcache_args* a) {
   if (!a) return 0;
   const DecodePlan pl = kvcache_plan(a);

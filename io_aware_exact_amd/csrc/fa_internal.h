@@ -40,6 +40,9 @@ struct FwdParams {
   const float* q_descale;     // fp8 only
   const float* k_descale;
   const float* v_descale;
+  const uint8_t* q_e8m0;      // MX fp8 only: [B,Sq,Hq,d/32], [B,Sk,Hkv,d/32], [B,Hkv,ceil(Sk/32),d]
+  const uint8_t* k_e8m0;
+  const uint8_t* v_e8m0;
   int B, Sq, Sk, Hq, Hkv, group;   // varlen: B = nseq, Sq/Sk = max lengths
   int num_m_tiles;
   float scale;                // softmax scale
@@ -117,6 +120,11 @@ hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varle
                               hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_mxfp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
+// MX fp8 quantiser: axis 0 blocks of 32 along d, axis 1 blocks of 32 tokens.
+hipError_t launch_quantize_mxfp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int B, int S,
+                                 int H, int d, int axis, void* codes, uint8_t* scales,
+                                 hipStream_t stream);
 hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int B, int S,
                                int H, int d, int per_tensor, void* codes, float* scales,
                                hipStream_t stream);

@@ -34,6 +34,22 @@
 //     read from the row-major V tile with the 8-bit LDS transposing read
 //     (ds_read_b64_tr_b8: within 16 lanes, lane i gets byte i % 8 of the
 //     rows addressed by lanes i / 8 + 2 e, e = 0..7).
+//
+// MX variant (MX = true): the scales are gfx950's native block scales, one
+// E8M0 power of two per 32 elements along each product's reduction
+// dimension (Q and K: along d; V: along the keys), passed per lane to the
+// scaled MFMA.  The scores and P V come out in true units, so no scale
+// enters the softmax or the rescale.  The instruction's two 32-element
+// scale blocks (checked with an in-bounds probe) are bytes 0-15 of both lane
+// halves (scale from the half-0 lane of the row) and bytes 16-31 of both
+// halves (scale from the half-1 lane).  Hence:
+//   * P V: with the key order above, bytes 0-15 of the two halves are keys
+//     0-31 of the tile and bytes 16-31 keys 32-63, so the V scale of lane
+//     half hh is that of key block 2 t + hh, with no change of layout;
+//   * S^T: Q and K fragments are loaded so that bytes 0-15 of half hh hold
+//     d = 64 c + 16 hh + i and bytes 16-31 hold d = 64 c + 32 + 16 hh + i,
+//     which makes the blocks d = 64 c .. 64 c + 31 (scale of d block 2 c,
+//     from half 0) and 64 c + 32 .. 64 c + 63 (d block 2 c + 1, half 1).
 #include "device_common.h"
 #include "fa_internal.h"
 
@@ -51,6 +67,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// With per-lane E8M0 scales (low byte of sa for A's block, of sb for B's).
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
@@ -75,7 +96,7 @@ struct Fp8Tile {
   static constexpr int STAGE = 2 * BN * STR;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MX>
 __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   using T = Fp8Tile<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
@@ -97,9 +118,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   __bf16* ob = (__bf16*)p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
   float* lseb = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
   const int nqb = (Lq + QBLK - 1) / QBLK, nkb = (Lk + QBLK - 1) / QBLK;
-  const float sq = p.q_descale[((int64_t)b * p.Hq + h) * nqb + q0 / QBLK];
-  const float* ksc = p.k_descale + ((int64_t)b * p.Hkv + g) * nkb;
-  const float* vsc = p.v_descale + ((int64_t)b * p.Hkv + g) * nkb;
+  const float sq = MX ? 1.f : p.q_descale[((int64_t)b * p.Hq + h) * nqb + q0 / QBLK];
+  const float* ksc = MX ? nullptr : p.k_descale + ((int64_t)b * p.Hkv + g) * nkb;
+  const float* vsc = MX ? nullptr : p.v_descale + ((int64_t)b * p.Hkv + g) * nkb;
+  constexpr int NB32 = D / 32;   // MX blocks per row along d
 
   int kend = Lk;
   if (CAUSAL) kend = min(Lk, q0 + BM + diag);
@@ -117,10 +139,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   i32x8 qf[T::NC];
 #pragma unroll
   for (int c = 0; c < T::NC; ++c) {
-    const uint32_t off = (uint32_t)(qrow * p.q_ss + 64 * c + 32 * hh);
-    const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
+    const uint32_t off = (uint32_t)(qrow * p.q_ss + 64 * c);
+    const u32x4 lo = buf_load16(rq, off + (MX ? 16 * hh : 32 * hh)),
+                hi = buf_load16(rq, off + (MX ? 32 + 16 * hh : 32 * hh + 16));
     qf[c] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  // MX: E8M0 scales of this lane's Q^T blocks (row qrow, d block 2c + hh)
+  int qsc[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) qsc[c] = 127;
+  if (MX && qrow < Lq) {
+    const uint8_t* qs = p.q_e8m0 + (((int64_t)b * Lq + qrow) * p.Hq + h) * NB32;
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) qsc[c] = qs[2 * c + hh];
   }
 
   const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
@@ -128,18 +161,38 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   const int G = lane >> 4, u = lane & 15;
   const int tr_row = 8 * (G >> 1) + (u >> 1);
   const int tr_col = 16 * (G & 1) + 8 * (u & 1);
+  // byte offsets within a 64-wide d chunk of this lane's two 16-byte halves
+  const int dlo = MX ? 16 * hh : 32 * hh, dhi = MX ? 32 + 16 * hh : 32 * hh + 16;
 
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss));
   const int lrow = tid / T::CH;
   const int lcol = (tid % T::CH) * 16;
   u32x4 kreg[T::NP], vreg[T::NP];
+  // MX: scales of the next tile, loaded with it.  K: the d-block scales of
+  // this lane's A row in score blocks 0 and 1 (one word for d = 128, a
+  // half-word for d = 64); V: the key-block-hh scale of d row 32 db + l32.
+  // Indices past the sequence end are clamped (their codes read as zero).
+  uint32_t ksn[2] = {0u, 0u}, vsn[T::ND];
+  const int nkb32 = (Lk + 31) / 32;
   auto gload = [&](int j0) {
 #pragma unroll
     for (int w = 0; w < T::NP; ++w) {
       const uint32_t r = (uint32_t)(j0 + lrow + w * T::RPP);
       kreg[w] = buf_load16(rk, r * (uint32_t)p.k_ss + lcol);
       vreg[w] = buf_load16(rv, r * (uint32_t)p.v_ss + lcol);
+    }
+    if constexpr (MX) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int tok = min(j0 + 32 * kb2 + kperm, Lk - 1);
+        const uint8_t* ks = p.k_e8m0 + (((int64_t)b * Lk + tok) * p.Hkv + g) * NB32;
+        ksn[kb2] = NB32 == 4 ? *(const uint32_t*)ks : (uint32_t)*(const uint16_t*)ks;
+      }
+      const int kblk = min((j0 >> 5) + hh, nkb32 - 1);
+      const uint8_t* vs = p.v_e8m0 + (((int64_t)b * p.Hkv + g) * nkb32 + kblk) * D + l32;
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) vsn[db] = vs[32 * db];
     }
   };
   auto lstore = [&](int st) {
@@ -149,6 +202,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
     for (int w = 0; w < T::NP; ++w) {
       *(u32x4*)(Ks + (lrow + w * T::RPP) * T::STR + lcol) = kreg[w];
       *(u32x4*)(Vs + (lrow + w * T::RPP) * T::STR + lcol) = vreg[w];
+    }
+  };
+  uint32_t ksc_t[2] = {0u, 0u}, vsc_t[T::ND];   // MX scales of the tile in LDS
+  auto take_scales = [&]() {
+    if constexpr (MX) {
+      ksc_t[0] = ksn[0];
+      ksc_t[1] = ksn[1];
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) vsc_t[db] = vsn[db];
     }
   };
 
@@ -163,6 +225,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   if (ntiles > 0) {
     gload(0);
     lstore(0);
+    take_scales();
   }
   wait_vmem();
   __syncthreads();
@@ -177,19 +240,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
     if (wave_active) {
       const uint8_t* Ks = smem + st * T::STAGE;
       const uint8_t* Vs = Ks + BN * T::STR;
-      const float c2 = cq * ksc[j0 / QBLK];
-      const float sv = vsc[j0 / QBLK];
-      const uint8_t* kbase = Ks + kperm * T::STR + 32 * hh;
+      const float c2 = MX ? p.scale_log2 : cq * ksc[j0 / QBLK];
+      const float sv = MX ? 1.f : vsc[j0 / QBLK];
+      const uint8_t* kbase = Ks + kperm * T::STR;
       f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
       for (int c = 0; c < T::NC; ++c)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
           const uint8_t* kp = kbase + 32 * kb2 * T::STR + 64 * c;
-          const u32x4 lo = *(const u32x4*)kp, hi = *(const u32x4*)(kp + 16);
+          const u32x4 lo = *(const u32x4*)(kp + dlo), hi = *(const u32x4*)(kp + dhi);
           const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          sacc[kb2] = mfma_fp8(kf, qf[c], sacc[kb2]);
+          if constexpr (MX)
+            sacc[kb2] = mfma_mx(kf, qf[c], sacc[kb2], (int)(ksc_t[kb2] >> (8 * (2 * c + hh))), qsc[c]);
+          else
+            sacc[kb2] = mfma_fp8(kf, qf[c], sacc[kb2]);
         }
       const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > q0 + wave * 32 + diag);
       if (need_mask) {
@@ -247,10 +313,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
           vf[2 * r] = x[0];
           vf[2 * r + 1] = x[1];
         }
-        oacc[db] = mfma_fp8(vf, pf, oacc[db]);
+        if constexpr (MX)
+          oacc[db] = mfma_mx(vf, pf, oacc[db], (int)vsc_t[db], 127);
+        else
+          oacc[db] = mfma_fp8(vf, pf, oacc[db]);
       }
     }
-    if (more) lstore(st ^ 1);
+    if (more) {
+      lstore(st ^ 1);
+      take_scales();
+    }
     __syncthreads();
   }
 
@@ -367,12 +439,94 @@ __global__ __launch_bounds__(256) void quant_encode_kernel(QuantParams p) {
   *(u32x4*)(p.codes + (((int64_t)b * p.S + s) * p.H + h) * p.d + 16 * c16) = out;
 }
 
-template <int D, bool CAUSAL>
+// ---------------------------------------------------------------------------
+// MX quantiser: E4M3 codes with one E8M0 scale per 32 consecutive elements.
+// The shared exponent is floor(log2(amax)) - 8 (8: the exponent of E4M3's
+// largest normal), clamped to [-127, 127], 0 for a zero block; the codes
+// encode x * 2^-e, exact in fp32 outside subnormal results.
+
+// Shared exponent from the bit pattern of amax = max |x| (an integer max of
+// the magnitude bits orders finite values the same way, subnormals included).
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0u) return 0;
+  const int E = (int)(amax_bits >> 23);
+  const int fl = E > 0 ? E - 127                                          // normal
+                       : (31 - __builtin_clz(amax_bits & 0x7FFFFFu)) - 149;   // subnormal
+  return min(127, max(-127, fl - 8));
+}
+
+struct MxQuantParams {
+  const float* x;
+  int64_t sb, ss, sh;
+  uint8_t* codes;
+  uint8_t* scales;
+  int B, S, H, d, nb;   // nb: token blocks (axis 1)
+};
+
+// Blocks along d: one thread per (b, s, h, 32-element block).
+__global__ __launch_bounds__(256) void quant_mx_d_kernel(MxQuantParams p) {
+  const int nbd = p.d / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.S * p.H * nbd;
+  if (idx >= total) return;
+  const int blk = (int)(idx % nbd);
+  int64_t r = idx / nbd;
+  const int h = (int)(r % p.H);
+  r /= p.H;
+  const int s = (int)(r % p.S);
+  const int b = (int)(r / p.S);
+  const float* xr = p.x + (int64_t)b * p.sb + (int64_t)s * p.ss + (int64_t)h * p.sh + 32 * blk;
+  float v[32];
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = xr[i];
+    amax = max(amax, __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu);
+  }
+  const int e = mx_exponent(amax);
+  uint8_t* out = p.codes + (((int64_t)b * p.S + s) * p.H + h) * p.d + 32 * blk;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    u32x4 q;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) word |= encode_e4m3(ldexpf(v[16 * w + 4 * j + c], -e)) << (8 * c);
+      q[j] = word;
+    }
+    *(u32x4*)(out + 16 * w) = q;
+  }
+  p.scales[idx] = (uint8_t)(e + 127);   // [B,S,H,d/32]
+}
+
+// Blocks along the tokens: one thread per (b, h, token block, d column).
+__global__ __launch_bounds__(256) void quant_mx_s_kernel(MxQuantParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.H * p.nb * p.d;
+  if (idx >= total) return;
+  const int c = (int)(idx % p.d);
+  int64_t r = idx / p.d;
+  const int blk = (int)(r % p.nb);
+  r /= p.nb;
+  const int h = (int)(r % p.H);
+  const int b = (int)(r / p.H);
+  const int s0 = 32 * blk, s1 = min(p.S, s0 + 32);
+  const float* xc = p.x + (int64_t)b * p.sb + (int64_t)h * p.sh + c;
+  uint32_t amax = 0u;
+  for (int s = s0; s < s1; ++s) amax = max(amax, __builtin_bit_cast(uint32_t, xc[(int64_t)s * p.ss]) & 0x7FFFFFFFu);
+  const int e = mx_exponent(amax);
+  for (int s = s0; s < s1; ++s)
+    p.codes[(((int64_t)b * p.S + s) * p.H + h) * p.d + c] = (uint8_t)encode_e4m3(ldexpf(xc[(int64_t)s * p.ss], -e));
+  p.scales[idx] = (uint8_t)(e + 127);   // [B,H,nb,d]
+}
+
+template <int D, bool CAUSAL, bool MX = false>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const long nblk = (long)p.num_m_tiles * p.Hq * p.B;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, MX>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -402,5 +556,25 @@ hipError_t launch_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t s
   const long grid = (n16 + 255) / 256;
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mxfp8(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch<128, true, true>(p, stream) : launch<128, false, true>(p, stream);
+  return causal ? launch<64, true, true>(p, stream) : launch<64, false, true>(p, stream);
+}
+
+hipError_t launch_quantize_mxfp8(const float* x, int64_t sb, int64_t ss, int64_t sh, int B, int S,
+                                 int H, int d, int axis, void* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  MxQuantParams p = {x, sb, ss, sh, (uint8_t*)codes, scales, B, S, H, d, (S + 31) / 32};
+  const long n = axis == 0 ? (long)B * S * H * (d / 32) : (long)B * H * p.nb * d;
+  if (n <= 0) return hipSuccess;
+  const long grid = (n + 255) / 256;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  if (axis == 0)
+    hipLaunchKernelGGL(quant_mx_d_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(quant_mx_s_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

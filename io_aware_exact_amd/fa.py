@@ -112,6 +112,15 @@ class FwdKvcacheArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class FwdMxfp8Args(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("q", FaTensor), ("k", FaTensor), ("v", FaTensor), ("o", FaTensor),
+                ("lse", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
 FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 
 
@@ -119,7 +128,7 @@ FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 EXPORTS = ["fa_abi_version", "fa_status_string", "fa_fwd_workspace_size",
            "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
            "fa_bwd_varlen_workspace_size", "fa_bwd_varlen", "fa_fwd_kvcache_workspace_size",
-           "fa_fwd_kvcache", "fa_quantize_fp8"]
+           "fa_fwd_kvcache", "fa_quantize_fp8", "fa_fwd_mxfp8", "fa_quantize_mxfp8"]
 
 _lib = None
 
@@ -157,6 +166,10 @@ def lib():
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         L.fa_quantize_fp8.restype = ctypes.c_int
         L.fa_quantize_fp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.fa_fwd_mxfp8.restype = ctypes.c_int
+        L.fa_fwd_mxfp8.argtypes = [ctypes.POINTER(FwdMxfp8Args), vp]
+        L.fa_quantize_mxfp8.restype = ctypes.c_int
+        L.fa_quantize_mxfp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -428,6 +441,44 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=Non
                 _t4(q8), _t4(k8), _t4(v8), _t4(out), lse.data_ptr(), q_descale.data_ptr(),
                 k_descale.data_ptr(), v_descale.data_ptr(), None, 0)
     _check("fa_fwd", lib().fa_fwd(ctypes.byref(a), _stream()))
+    return out, lse
+
+
+def quantize_mxfp8(x, axis):
+    """MX quantisation of x [B,S,H,d] fp32 on the GPU (d contiguous): codes
+    uint8 [B,S,H,d] OCP E4M3 and E8M0 scale bytes, one per 32 elements --
+    axis 0 (q, k): along d, scales [B,S,H,d/32]; axis 1 (v): along the
+    tokens, scales [B,H,ceil(S/32),d]."""
+    assert x.dtype == torch.float32 and x.dim() == 4 and x.stride(3) == 1
+    B, S, H, d = x.shape
+    codes = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
+    shape = (B, S, H, d // 32) if axis == 0 else (B, H, (S + 31) // 32, d)
+    scales = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    _check("fa_quantize_mxfp8", lib().fa_quantize_mxfp8(
+        x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, S, H, d, int(axis),
+        codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def fwd_mxfp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None, out=None,
+              lse=None):
+    """MX FP8 forward: E4M3 codes q8 [B,Sq,Hq,d], k8/v8 [B,Sk,Hkv,d] with the
+    E8M0 scale bytes of quantize_mxfp8 (q, k: axis 0; v: axis 1).  Returns
+    (o bf16, lse)."""
+    B, Sq, Hq, d = q8.shape
+    Sk, Hkv = k8.shape[1], k8.shape[2]
+    for t in (q8, k8, v8):
+        assert t.element_size() == 1
+    for t in (q_scale, k_scale, v_scale):
+        assert t.dtype == torch.uint8 and t.is_contiguous()
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    a = FwdMxfp8Args(B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
+                     _t4(q8), _t4(k8), _t4(v8), _t4(out), lse.data_ptr(), q_scale.data_ptr(),
+                     k_scale.data_ptr(), v_scale.data_ptr())
+    _check("fa_fwd_mxfp8", lib().fa_fwd_mxfp8(ctypes.byref(a), _stream()))
     return out, lse
 
 

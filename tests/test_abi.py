@@ -216,7 +216,7 @@ def test_struct_layouts_match_header(tmp_path):
     (checked with the host C compiler)."""
     structs = {"fa_fwd_args": fa.FwdArgs, "fa_fwd_varlen_args": fa.FwdVarlenArgs,
                "fa_bwd_args": fa.BwdArgs, "fa_bwd_varlen_args": fa.BwdVarlenArgs,
-               "fa_fwd_kvcache_args": fa.FwdKvcacheArgs}
+               "fa_fwd_kvcache_args": fa.FwdKvcacheArgs, "fa_fwd_mxfp8_args": fa.FwdMxfp8Args}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fa.h"', 'int main(void) {']
     expect = []
     for cname, cls in structs.items():
@@ -235,3 +235,37 @@ def test_struct_layouts_match_header(tmp_path):
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
     assert got == expect
+
+
+def mx_args(**kw):
+    base = dict(B=1, Sq=16, Sk=16, Hq=2, Hkv=2, d=64, causal=0, softmax_scale=0.125)
+    base.update({k: v for k, v in kw.items() if k in base})
+    t = fa.FaTensor(FAKE, 2048, 128, 64)
+    return fa.FwdMxfp8Args(base["B"], base["Sq"], base["Sk"], base["Hq"], base["Hkv"], base["d"],
+                           base["causal"], base["softmax_scale"], kw.get("q", t),
+                           fa.FaTensor(FAKE + (1 << 24), 2048, 128, 64),
+                           fa.FaTensor(FAKE + (2 << 24), 2048, 128, 64),
+                           kw.get("o", fa.FaTensor(FAKE + (3 << 24), 2048, 128, 64)),
+                           FAKE + (4 << 24), kw.get("q_scale", FAKE + (5 << 24)),
+                           FAKE + (6 << 24), kw.get("v_scale", FAKE + (7 << 24)))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 3), (dict(Hq=3), 5), (dict(softmax_scale=0.0), 10), (dict(Sq=-1), 2),
+    (dict(q_scale=None), 1), (dict(q_scale=FAKE + (5 << 24) + 2), 6),
+    (dict(q=fa.FaTensor(FAKE + 8, 2048, 128, 64)), 6),
+    (dict(o=fa.FaTensor(FAKE + (7 << 24), 2048, 128, 64)), 8),   # o over the V scales
+])
+def test_mxfp8_rejects(kw, status):
+    a = mx_args(**kw)
+    assert fa.lib().fa_fwd_mxfp8(ctypes.byref(a), None) == status
+
+
+def test_quantize_mxfp8_rejects():
+    L = fa.lib()
+    assert L.fa_quantize_mxfp8(None, 0, 0, 0, 1, 1, 1, 64, 0, FAKE, FAKE, None) == 1
+    assert L.fa_quantize_mxfp8(FAKE, 0, 0, 0, 1, 1, 1, 48, 0, FAKE + (1 << 24), FAKE + (2 << 24), None) == 3
+    assert L.fa_quantize_mxfp8(FAKE, 0, 0, 0, 1, 1, 1, 64, 2, FAKE + (1 << 24), FAKE + (2 << 24), None) == 2
+    assert L.fa_quantize_mxfp8(FAKE, 0, 0, 0, 1, 1, 1, 64, 0, FAKE + (1 << 24) + 4, FAKE + (2 << 24), None) == 6
+    assert L.fa_quantize_mxfp8(FAKE, 64, 64, 64, 1, 4, 1, 64, 1, FAKE + 16, FAKE + (2 << 24), None) == 8
+    assert L.fa_quantize_mxfp8(FAKE, 0, 0, 0, 0, 1, 1, 64, 0, FAKE + (1 << 24), FAKE + (2 << 24), None) == 0

@@ -256,9 +256,17 @@ def leg_fp8(reps):
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
     ms = time_calls(lambda: fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse), reps)
     ff = fwd_flops(B, S, S, H, d, False)
+    X = [inputs.outlier_normal((B, S, H, d), 4000 + i, device="cuda") for i in range(3)]
+    mx = [fa.quantize_mxfp8(X[0], 0), fa.quantize_mxfp8(X[1], 0), fa.quantize_mxfp8(X[2], 1)]
+    del X
+    ms_mx = time_calls(lambda: fa.fwd_mxfp8(*[c for c, _ in mx], *[s for _, s in mx], False,
+                                            out=o, lse=lse), reps)
     return {"workload": "fp8 e4m3 fwd B=1 H=16 S=16384 d=128 non-causal, per-block scales",
             "ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2),
-            "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
+            "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "mx": {"workload": "MX fp8 (E8M0 scale per 32 elements) fwd, same shape and inputs",
+                   "ms": round(ms_mx, 4), "tflops": round(ff / ms_mx / 1e9, 2),
+                   "frac_of_fp8_peak": round(ff / ms_mx / 1e9 / PEAK_FP8_TFLOPS, 4)}}
 
 
 def leg_sweep(reps):

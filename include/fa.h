@@ -350,10 +350,10 @@ fa_status fa_fwd_mxfp8(const fa_fwd_mxfp8_args* args, hipStream_t stream);
  *   axis 0: blocks of 32 along d (for q and k), scales [B,S,H,d/32];
  *   axis 1: blocks of 32 tokens along S for each (b, h, d column) (for v),
  *           scales [B,H,ceil(S/32),d]; the last block may be partial.
- * Per block, e = floor(log2(amax)) - 8 (8: the exponent of E4M3's largest
- * normal), clamped to [-127, 127], and 0 for an all-zero block; the scale
- * byte is e + 127 and the codes are the nearest e4m3 values of x * 2^-e,
- * ties to the even code, saturating to +-448.  d is a multiple of 32, at most
+ * Per block, e is the smallest exponent with amax <= 448 * 2^e (so no
+ * element saturates), clamped to [-127, 127], and 0 for an all-zero block;
+ * the scale byte is e + 127 and the codes are the nearest e4m3 values of
+ * x * 2^-e, ties to the even code.  d is a multiple of 32, at most
  * 256.  x, codes and scales must not overlap.  Deterministic. */
 fa_status fa_quantize_mxfp8(const float* x, int64_t stride_b, int64_t stride_s,
                             int64_t stride_h, int32_t B, int32_t S, int32_t H,

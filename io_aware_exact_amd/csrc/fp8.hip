@@ -441,8 +441,9 @@ __global__ __launch_bounds__(256) void quant_encode_kernel(QuantParams p) {
 
 // ---------------------------------------------------------------------------
 // MX quantiser: E4M3 codes with one E8M0 scale per 32 consecutive elements.
-// The shared exponent is floor(log2(amax)) - 8 (8: the exponent of E4M3's
-// largest normal), clamped to [-127, 127], 0 for a zero block; the codes
+// The shared exponent is the smallest e with amax <= 448 * 2^e, i.e.
+// floor(log2(amax)) - 8 plus one when amax's significand exceeds 1.75, so no
+// element saturates; clamped to [-127, 127], 0 for a zero block.  The codes
 // encode x * 2^-e, exact in fp32 outside subnormal results.
 
 // Shared exponent from the bit pattern of amax = max |x| (an integer max of
@@ -452,7 +453,9 @@ __device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
   const int E = (int)(amax_bits >> 23);
   const int fl = E > 0 ? E - 127                                          // normal
                        : (31 - __builtin_clz(amax_bits & 0x7FFFFFu)) - 149;   // subnormal
-  return min(127, max(-127, fl - 8));
+  // significand above 1.75 = 448 / 2^8: one more (subnormals are clamped anyway)
+  const int up = (E > 0 && (amax_bits & 0x7FFFFFu) > 0x600000u) ? 1 : 0;
+  return min(127, max(-127, fl - 8 + up));
 }
 
 struct MxQuantParams {

@@ -108,10 +108,14 @@ def dequantize_blocks(codes, scales, block=128):
 # elements, one E8M0 scale (a power of two, byte = exponent + 127) per block
 # of 32 consecutive elements along the reduction dimension.  Readings (the
 # pages fix no format):
-#   * the shared exponent is floor(log2(amax)) - 8, 8 being the exponent of
-#     E4M3's largest normal, so the block maximum lands in E4M3's top binade;
-#   * elements are x / 2^e (fp32) encoded as above (nearest, ties to even,
-#     saturating to +-448);
+#   * the shared exponent e is the smallest for which the block maximum fits
+#     E4M3's range, amax <= 448 * 2^e: floor(log2(amax)) - 8, plus one when
+#     amax's significand exceeds 1.75.  (The OCP rule floor(log2(amax)) - 8
+#     alone clips block maxima in [448, 512) * 2^e to 448; on the outlier
+#     workload that more than doubled the RMS error of the attention output
+#     against the 128-token per-block scaling, so the non-clipping exponent
+#     is used.)  The block maximum lands in (224, 448] * 2^e;
+#   * elements are x / 2^e (fp32) encoded as above (nearest, ties to even);
 #   * a block of zeros gets exponent 0; exponents are clamped to [-127, 127];
 #   * Q and K blocks run along d (scales [B, S, H, d/32]); V blocks run along
 #     the tokens, the reduction dimension of P V (scales [B, H, ceil(S/32), d];
@@ -121,11 +125,12 @@ E4M3_EMAX = 8
 
 
 def mx_exponent(amax):
-    """Shared exponents floor(log2(amax)) - 8 of blocks with maxima amax
-    (0 for a zero block), clamped to [-127, 127]."""
+    """Shared exponents of blocks with maxima amax: the smallest e with
+    amax <= 448 * 2^e (0 for a zero block), clamped to [-127, 127]."""
     amax = np.asarray(amax, dtype=np.float64)
-    _, k = np.frexp(amax)                 # amax = f 2^k with f in [0.5, 1)
-    e = np.where(amax > 0, (k - 1) - E4M3_EMAX, 0)
+    m, k = np.frexp(amax)                 # amax = m 2^k with m in [0.5, 1)
+    e = (k - 1) - E4M3_EMAX + (m > 0.875)  # significand 2m > 1.75
+    e = np.where(amax > 0, e, 0)
     return np.clip(e, -127, 127).astype(np.int64)
 
 

@@ -126,7 +126,10 @@ def test_mx_full_size():
     check_lse_fp8(l_mx[bi, hi, ii].cpu().numpy(), l_ref_m, absdot)
     assert rel <= FP8_O_REL_L2
     o_ref, _ = oracle.attention_fwd_rows(*[x.cpu() for x in X], bi, hi, ii, False)
-    rms = {}
+    deq_b = [ofp8.dequantize_blocks(c.cpu().numpy(), s.cpu().numpy()) for c, s in blk]
+    o_deq_b, _ = oracle.attention_fwd_rows(*deq_b, bi, hi, ii, False)
+    rms = {"exact_on_mx_inputs": float(np.sqrt(np.mean((o_ref_m - o_ref) ** 2))),
+           "exact_on_block128_inputs": float(np.sqrt(np.mean((o_deq_b - o_ref) ** 2)))}
     for name, o in (("mxfp8", o_mx), ("fp8_block128", o_blk)):
         v = o[bi, ii, hi].float().cpu().numpy()
         rms[name] = float(np.sqrt(np.mean((v - o_ref) ** 2)))

@@ -66,14 +66,25 @@ def mx_case(seed, shape):
     return x.numpy().astype(np.float32)
 
 
+def smallest_fitting_exponent(amax):
+    """The least e with amax <= 448 * 2^e, by search (exact in float64)."""
+    if amax == 0:
+        return 0
+    e = int(np.floor(np.log2(amax))) - 10
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    return max(-127, min(127, e))
+
+
 def test_mx_exponent_closed_form():
-    # the block maximum's binade maps onto E4M3's top binade [256, 512)
-    amax = np.array([1.0, 1.5, 0.75, 448.0, 512.0, 2.0 ** -100, 3.0e38, 0.0])
+    amax = np.array([1.0, 1.5, 0.75, 448.0, 449.0, 512.0, 1.76, 2.0 ** -100, 3.0e38, 0.0])
     e = fp8.mx_exponent(amax)
-    assert list(e) == [-8, -8, -9, 0, 1, -108, 119, 0]
+    assert list(e) == [-8, -8, -9, 0, 1, 1, -7, -108, 120, 0]
+    assert list(e) == [smallest_fitting_exponent(a) for a in amax]
+    # the block maximum lands in (224, 448] * 2^e: no clipping, top two binades
     nz = amax > 0
     r = amax[nz] / np.exp2(e[nz].astype(np.float64))
-    assert ((r >= 256) & (r < 512)).all()
+    assert ((r > 224) & (r <= 448)).all()
     assert fp8.mx_exponent(np.array([2.0 ** -130]))[0] == -127   # clamped
 
 
@@ -87,7 +98,8 @@ def test_mx_codes_match_torch_cast():
     ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert (codes == ref).all()
     amax = np.abs(x).reshape(2, 40, 3, 2, 32).max(axis=4)
-    assert (sc == (np.floor(np.log2(amax)) - 8 + 127).astype(np.uint8)).all()
+    want = np.vectorize(smallest_fitting_exponent)(amax.astype(np.float64)) + 127
+    assert (sc == want.astype(np.uint8)).all()
 
 
 def test_mx_token_blocks_and_roundtrip():
@@ -98,19 +110,17 @@ def test_mx_token_blocks_and_roundtrip():
     assert sc.shape == (1, 2, 3, 64)
     assert sc[0, 1, 1, 5] == 127 and (codes[0, 32:64, 1, 5] & 0x7F == 0).all()
     amax_tail = np.abs(x[0, 64:70, 0, 7]).max()
-    assert sc[0, 0, 2, 7] == int(np.floor(np.log2(amax_tail))) - 8 + 127
+    assert sc[0, 0, 2, 7] == smallest_fitting_exponent(float(amax_tail)) + 127
     xd = fp8.dequantize_mx(codes, sc, "s")
     e_el = np.repeat(sc.astype(np.int64) - 127, 32, axis=2)[:, :, :70].transpose(0, 2, 1, 3)
     step = np.exp2(e_el.astype(np.float64))
-    # below E4M3's top binade the rounding error is at most half a step of
-    # 3 mantissa bits (2^-4 relative) or half the subnormal spacing 2^-10;
-    # the top binade saturates at 448, an error below 64 steps
+    # nothing saturates: the rounding error is at most half a step of 3
+    # mantissa bits (2^-4 relative) or half the subnormal spacing 2^-10
     err = np.abs(xd - x)
     bound = np.maximum(np.abs(x) * 2.0 ** -4, step * 2.0 ** -10)
-    sat = np.abs(x) / step > 448
-    assert (err[~sat] <= bound[~sat] + 1e-300).all()
-    assert (err[sat] <= 64 * step[sat]).all()
-    # every nonzero block's largest element decodes into E4M3's top binade
+    assert (np.abs(x) / step <= 448).all()
+    assert (err <= bound + 1e-300).all()
+    # every nonzero block's largest element decodes into E4M3's top two binades
     top = np.abs(codes[0, :32, 0, 0].astype(np.int32) & 0x7F).max()
-    assert (top >> 3) == 15
+    assert (top >> 3) >= 14
 

@@ -213,7 +213,7 @@ typedef struct {
  * element strides *_stride_page, *_stride_s and *_stride_h (d contiguous,
  * strides multiples of 8).  Token j of sequence b is slot j % page_size of
  * page block_table[b * block_table_stride + j / page_size]; page_size must be
- * a power of two and block_table an int32 device array with
+ * a power of two of at least 16 and block_table an int32 device array with
  * max_pages_per_seq used columns per row.  With block_table NULL the cache is
  * dense: page b is all of sequence b's cache (num_pages >= B, page_size =
  * the capacity, any value >= 1).  cache_seqlens [B] int32 (device) counts

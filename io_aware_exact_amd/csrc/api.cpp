@@ -341,7 +341,9 @@ fa_status check_kvcache(const fa_fwd_kvcache_args* a) {
   if (!scale_ok(a->softmax_scale)) return FA_ERR_SCALE;
   const bool paged = a->block_table != nullptr;
   if (paged) {
-    if ((a->page_size & (a->page_size - 1)) != 0) return FA_ERR_SHAPE;   // a power of two
+    // a power of two, at least 16 (the decode kernel's DMAs cover up to 8
+    // consecutive rows, which must lie in one page)
+    if ((a->page_size & (a->page_size - 1)) != 0 || a->page_size < 16) return FA_ERR_SHAPE;
     if (a->max_pages_per_seq < 1 || a->block_table_stride < a->max_pages_per_seq) return FA_ERR_SHAPE;
     if (a->B > 0 && a->num_pages < 1) return FA_ERR_SHAPE;
     if ((uintptr_t)a->block_table & 3u) return FA_ERR_ALIGN;

@@ -20,20 +20,23 @@
 //     M = Sq * group query rows of the kv head (all query heads of the group,
 //     all query positions) form the 32 columns of S^T = K Q^T, so K and V are
 //     read once for the whole group; unused columns are zero.
-//   * K rows are loaded straight from HBM into the A operand of the 32x32x16
-//     bf16 MFMA (16 bytes per lane per load), in the permuted row order that
-//     makes accumulator registers 0..7 / 8..15 hold 8 consecutive keys, so
-//     the probabilities are directly the B operand of O^T += V^T P^T.
-//   * V rows go HBM -> registers -> a wave-private LDS tile (coalesced
-//     16-byte loads, whole rows per 16 lanes) and come back as V^T through
-//     the LDS transposing read.  The next block's K and V loads are issued
-//     before the current block's MFMAs (32 keys, 16 KB per wave in flight).
+//   * K and V tiles of 32 keys go from HBM straight into a 2-stage,
+//     wave-private LDS ring by DMA (buffer_load ... lds), stored swizzled so
+//     that the K A-operand reads (16 consecutive rows per 16 lanes, in the
+//     permuted row order that makes accumulator registers 0..7 / 8..15 hold
+//     8 consecutive keys, so the probabilities are directly the B operand of
+//     O^T += V^T P^T) and the V^T transposing reads are free of bank
+//     conflicts.  While one block is consumed the next is in flight, with no
+//     registers held for it; explicit vmcnt waits let the younger block's
+//     DMA stay outstanding.
 //   * A second kernel combines the partials of every row.
 //   * KV-cache attention (an appended, possibly paged cache) runs the same
 //     kernel with KVC = true: each sequence's length is its cached count plus
-//     the appended rows, and every K/V row is addressed through the block
-//     table (page, slot); rows past the end read the last valid row instead,
-//     and their scores are masked.
+//     the appended rows; each DMA covers a few consecutive rows inside one
+//     page (pages hold at least 16 tokens) and reads them through that page's
+//     buffer resource, found in a window of block-table entries.
+#include <type_traits>
+
 #include "device_common.h"
 #include "fa_internal.h"
 
@@ -43,14 +46,8 @@ constexpr int BNK = 32;   // keys per iteration (one MFMA block)
 
 template <int D>
 struct DecTile {
-  static constexpr int VSTR = D + 32;        // V row stride in LDS (elements): 4 rows of
-                                             // a transposing read fall on disjoint banks
   static constexpr int NC = D / 16;          // 16-wide d chunks (K^T Q)
   static constexpr int ND = D / 32;          // 32-row d blocks of O^T
-  static constexpr int CH = D / 8;           // 16-byte chunks per row
-  static constexpr int RPP = 64 / CH;        // V rows per wave load pass
-  static constexpr int NP = BNK / RPP;       // V load passes per block
-  static constexpr int BUF = BNK * VSTR;     // elements of one V buffer
 };
 
 __device__ __forceinline__ int row_perm(int l32) {
@@ -64,15 +61,39 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool KVC>
+// s_waitcnt immediate waiting until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+#define VMCNT_IMM(n) ((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
+
+// ---------------------------------------------------------------------------
+// Split-KV decode.  K and V tiles of 32 keys go from HBM straight into an
+// NST-stage wave-private LDS ring (buffer_load ... lds, no staging
+// registers), so NST - 1 blocks are in flight while one is consumed.  Tiles
+// are stored swizzled (swz): the K A-operand reads (16 consecutive rows per
+// 16 lanes) and the V transposing reads are both free of bank conflicts.
+// Each lane of a 1 KB DMA fetches the logical chunk that belongs at its
+// physical slot.  KV cache: a DMA covers RPI consecutive rows, inside one
+// page for pages of >= 16 tokens, so each DMA takes the page's buffer
+// resource (rows past the sequence end read as zero).
+template <int D, bool KVC, int NST>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   using T = DecTile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[T::BUF];
+  constexpr int TILE = BNK * D;            // elements of one K or V tile
+  constexpr int RPI = 512 / D;             // rows per 1 KB DMA
+  constexpr int NLD = BNK / RPI;           // DMAs per tile
+  // one array per stage, so that the compiler can tell a stage being read
+  // from the stages whose DMA is still in flight
+  __shared__ __attribute__((aligned(16))) __bf16 smem0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 smem1[2 * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 smem2[NST > 2 ? 2 * TILE : 8];
+  static_assert(NST == 2 || NST == 3, "stages");
 
-  const int split = blockIdx.x % p.nsplit;
-  const int rest = blockIdx.x / p.nsplit;
-  const int g = rest % p.Hkv;
-  const int b = rest / p.Hkv;
+  // uniform indices, kept scalar: a buffer resource built from a value the
+  // compiler takes as per-lane would put every load in a waterfall loop
+  const int split = __builtin_amdgcn_readfirstlane(blockIdx.x % p.nsplit);
+  const int rest = __builtin_amdgcn_readfirstlane(blockIdx.x / p.nsplit);
+  const int g = __builtin_amdgcn_readfirstlane(rest % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(rest / p.Hkv);
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -99,83 +120,74 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   }
   const int lim = (p.causal ? min(Lk - 1, qi + diag) : Lk - 1);
 
-  // ---- K (direct to MFMA operands) and V (via LDS) streaming; keys past the
-  // end of the cache read as zero and are masked
-  const __bf16* kb = (const __bf16*)p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
-  const __bf16* vb = (const __bf16*)p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)Lk * p.k_ss * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)Lk * p.v_ss * 2));
-  const int kp = row_perm(l32);
-  const int vrow = lane / T::CH;
-  const int vcol = (lane % T::CH) * 8;
-  bf16x8 kf[T::NC];
-  u32x4 vreg[T::NP];
-  // KV cache.  Without a block table the sequence's cache is one dense
-  // region, read exactly like the dense path.  With pages of >= 32 tokens a
-  // block (32 keys from a multiple of 32) lies in one page: its page number
-  // comes from a window of block-table entries held one per lane, and its
-  // rows are read through a buffer resource over the page's rows that hold
-  // tokens (rows past the end read as zero, as in the dense path).  Smaller
-  // pages: every row's page comes from the window by a cross-lane permute,
-  // and rows past the end read the last row (finite; their scores are
-  // masked).  Lk >= 1 whenever a block is loaded.
-  const __bf16* kcb = (const __bf16*)p.k + (int64_t)g * p.k_sh;
-  const __bf16* vcb = (const __bf16*)p.v + (int64_t)g * p.v_sh;
+  // ---- DMA addressing: lane's row within a 1 KB group and its logical column
+  const int lrow_in = lane / (64 / RPI);
+  const int lpc = lane % (64 / RPI);
+  uint32_t koff[NLD], voff[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int row = RPI * u + lrow_in;
+    const int col = swz<D>(row, 8 * lpc) - row * D;
+    koff[u] = (uint32_t)(row * p.k_ss + col) * 2;
+    voff[u] = (uint32_t)(row * p.v_ss + col) * 2;
+  }
   const bool paged = KVC && p.kv.block_table != nullptr;
   const int shift = p.kv.page_shift;
   const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
   const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
   PageWindow win;
-  __amdgpu_buffer_rsrc_t rkc = rk, rvc = rv;
-  if (KVC && !paged) {
-    rkc = make_rsrc(kcb + (int64_t)b * p.kv.k_sp, (uint32_t)((int64_t)Lk * p.k_ss * 2));
-    rvc = make_rsrc(vcb + (int64_t)b * p.kv.v_sp, (uint32_t)((int64_t)Lk * p.v_ss * 2));
-  }
-  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rkk, const __amdgpu_buffer_rsrc_t& rvv, int r0) {
-    const uint32_t kr = (uint32_t)(r0 + kp);
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c)
-      kf[c] = __builtin_bit_cast(bf16x8, buf_load16(rkk, (kr * (uint32_t)p.k_ss + 16 * c + 8 * hh) * 2));
-#pragma unroll
-    for (int u = 0; u < T::NP; ++u) {
-      const uint32_t r = (uint32_t)(r0 + vrow + u * T::RPP);
-      vreg[u] = buf_load16(rvv, (r * (uint32_t)p.v_ss + vcol) * 2);
-    }
+  const __bf16* kseq = (const __bf16*)uniform_ptr(
+      (const __bf16*)p.k + (KVC ? (int64_t)b * p.kv.k_sp : (int64_t)b * p.k_sb) + (int64_t)g * p.k_sh);
+  const __bf16* vseq = (const __bf16*)uniform_ptr(
+      (const __bf16*)p.v + (KVC ? (int64_t)b * p.kv.v_sp : (int64_t)b * p.v_sb) + (int64_t)g * p.v_sh);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kseq, (uint32_t)((int64_t)Lk * p.k_ss * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vseq, (uint32_t)((int64_t)Lk * p.v_ss * 2));
+  const __bf16* kcb = (const __bf16*)p.k + (int64_t)g * p.k_sh;   // paged: page bases
+  const __bf16* vcb = (const __bf16*)p.v + (int64_t)g * p.v_sh;
+  auto kstage = [&](auto st_c) -> __bf16* {
+    constexpr int ST = decltype(st_c)::value;
+    return ST == 0 ? smem0 : ST == 1 ? smem1 : smem2;
   };
-  auto gload = [&](int j0) {
-    if constexpr (KVC) {
-      if (!paged) {
-        load_rows(rkc, rvc, j0);
-      } else if (shift >= 5) {
-        const int pn = j0 >> shift;
-        win.cover(btrow, pn, pn, last_page_no, lane);
+  auto vstage = [&](auto st_c) -> __bf16* { return kstage(st_c) + TILE; };
+  auto issue = [&](auto st, int j0) {
+    if (paged) {
+      win.cover(btrow, j0 >> shift, min(j0 + BNK - 1, Lk - 1) >> shift, last_page_no, lane);
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const int pn = min(j0 + RPI * u, Lk - 1) >> shift;
         const int64_t page = win.uniform(pn);
         const int first_tok = pn << shift;
-        const int rows = min(Lk - first_tok, 1 << shift);
-        const __amdgpu_buffer_rsrc_t rkp = make_rsrc(kcb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2));
-        const __amdgpu_buffer_rsrc_t rvp = make_rsrc(vcb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2));
-        load_rows(rkp, rvp, j0 - first_tok);
-      } else {
-        win.cover(btrow, j0 >> shift, min(j0 + BNK - 1, Lk - 1) >> shift, last_page_no, lane);
-        const int mask = (1 << shift) - 1;
-        const int jk = min(j0 + kp, Lk - 1);
-        const __bf16* kr = kcb + (int64_t)win.per_lane(jk >> shift) * p.kv.k_sp + (int64_t)(jk & mask) * p.k_ss;
-#pragma unroll
-        for (int c = 0; c < T::NC; ++c) kf[c] = *(const bf16x8*)(kr + 16 * c + 8 * hh);
-#pragma unroll
-        for (int u = 0; u < T::NP; ++u) {
-          const int jv = min(j0 + vrow + u * T::RPP, Lk - 1);
-          vreg[u] = *(const u32x4*)(vcb + (int64_t)win.per_lane(jv >> shift) * p.kv.v_sp +
-                                    (int64_t)(jv & mask) * p.v_ss + vcol);
-        }
+        const int rows = max(0, min(Lk - first_tok, 1 << shift));
+        const uint32_t rel = (uint32_t)(j0 - first_tok);
+        buf_load16_lds(make_rsrc(kcb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2)),
+                       rel * (uint32_t)p.k_ss * 2 + koff[u], kstage(st) + RPI * u * D);
+        buf_load16_lds(make_rsrc(vcb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2)),
+                       rel * (uint32_t)p.v_ss * 2 + voff[u], vstage(st) + RPI * u * D);
       }
     } else {
-      load_rows(rk, rv, j0);
+      const uint32_t kb0 = (uint32_t)j0 * (uint32_t)p.k_ss * 2, vb0 = (uint32_t)j0 * (uint32_t)p.v_ss * 2;
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        buf_load16_lds(rk, kb0 + koff[u], kstage(st) + RPI * u * D);
+        buf_load16_lds(rv, vb0 + voff[u], vstage(st) + RPI * u * D);
+      }
     }
   };
+
+  // ---- operand addresses within a stage (swizzled; see device_common.h)
+  const int kp = row_perm(l32);
+  int aoff[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) aoff[c] = swz<D>(kp, 16 * c + 8 * hh);
   const int trG = lane >> 4;
   const int tr_row = 8 * (trG >> 1) + ((lane >> 2) & 3);
   const int tr_col = 16 * (trG & 1) + 4 * (lane & 3);
+  int toff[2][T::ND];
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db) {
+    toff[0][db] = swz<D>(tr_row, 32 * db + tr_col);
+    toff[1][db] = swz<D>(tr_row + 4, 32 * db + tr_col);
+  }
 
   f32x16 oacc[T::ND];
 #pragma unroll
@@ -183,18 +195,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = p.scale_log2;
 
-  if (nblk > 0) gload(kbeg);
-  for (int t = 0; t < nblk; ++t) {
+  if (nblk > 0) issue(std::integral_constant<int, 0>{}, kbeg);
+  if (nblk > 1) issue(std::integral_constant<int, 1>{}, kbeg + BNK);
+  if (NST > 2 && nblk > 2) issue(std::integral_constant<int, NST - 1>{}, kbeg + 2 * BNK);
+  // block t in stage ST = t mod NST
+  auto block = [&](auto st_c, int t) {
     const int j0 = kbeg + t * BNK;
-    // stage this block's V rows and consume its K operands, then issue the
-    // next block's loads into the same registers
-#pragma unroll
-    for (int u = 0; u < T::NP; ++u) *(u32x4*)(Vs + (vrow + u * T::RPP) * T::VSTR + vcol) = vreg[u];
+    // block t has landed once at most the younger blocks' DMAs are pending
+    const int younger = min(NST - 1, nblk - 1 - t);
+    if (NST == 3 && younger == 2) __builtin_amdgcn_s_waitcnt(VMCNT_IMM(4 * NLD));
+    else if (younger >= 1) __builtin_amdgcn_s_waitcnt(VMCNT_IMM(2 * NLD));
+    else __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+    wave_lds_sync();
+    const __bf16* Ks = kstage(st_c);
+    const __bf16* Vs = vstage(st_c);
     f32x16 s = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < T::NC; ++c) s = mfma32(kf[c], qf[c], s);
-    if (t + 1 < nblk) gload(j0 + BNK);
-    wave_lds_sync();
+    for (int c = 0; c < T::NC; ++c) s = mfma32(*(const bf16x8*)(Ks + aoff[c]), qf[c], s);
     // register i holds key j0 + 16 (i / 8) + 8 hh + i % 8; keys past the
     // chunk belong to the next chunk, keys past lim are masked or missing
 #pragma unroll
@@ -224,17 +241,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     m_run = m_new;
 #pragma unroll
     for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
-    const __bf16* vbase = Vs + tr_row * T::VSTR + tr_col;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) {
-        const __bf16* vp = vbase + 16 * c * T::VSTR + 32 * db;
-        const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
+        const bf16x8 vf = cat_bf16(lds_read_tr16(Vs + toff[0][db] + 16 * c * D),
+                                   lds_read_tr16(Vs + toff[1][db] + 16 * c * D));
         oacc[db] = mfma32(vf, pf[c], oacc[db]);
       }
-    // the next iteration's writes come after these reads
+    // this stage's reads are done before the DMA refills it
     wave_lds_sync();
+    if (t + NST < nblk) issue(st_c, j0 + NST * BNK);
+  };
+  // Unrolled by 2 NST: the compiler's own wait before a stage's first LDS
+  // read is exact except at the loop head, where merging the entry and
+  // back-edge paths makes it wait for every DMA in flight.
+  for (int t = 0; t < nblk; t += 2 * NST) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int tr = t + r * NST;
+      if (tr < nblk) block(std::integral_constant<int, 0>{}, tr);
+      if (tr + 1 < nblk) block(std::integral_constant<int, 1>{}, tr + 1);
+      if (NST > 2 && tr + 2 < nblk) block(std::integral_constant<int, NST - 1>{}, tr + 2);
+    }
   }
 
   // ---- partial result of this chunk: O_p = O / l (fp32), LSE_p
@@ -291,12 +320,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   if (lane == 0) p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qi] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
+constexpr int kDecodeStages = 2;   // DMA stages per wave (3 measured slower)
+
 template <int D, bool KVC>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const long nblk = (long)p.B * p.Hkv * p.nsplit;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_split_kernel<D, KVC>), dim3((unsigned)nblk), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, KVC, kDecodeStages>), dim3((unsigned)nblk), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long nrow = (long)p.B * p.Hq * p.Sq;

@@ -43,6 +43,16 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// A wave-uniform pointer made explicitly scalar.  64-bit products of uniform
+// values may be computed on the vector unit; a buffer resource built from
+// such a value would make the compiler wrap every load in a waterfall loop.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
 // Raw buffer resource over [base, base + bytes).  Loads past the end return
 // zero and stores past the end are dropped (the bounds check covers the
 // per-lane offset), which is how tile tails are handled without clamping.

@@ -183,6 +183,7 @@ def kvcache_args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), 4), (dict(d=96), 3), (dict(Hq=3), 5), (dict(softmax_scale=0.0), 10),
     (dict(page_size=48), 2),                         # paged: not a power of two
+    (dict(page_size=8, max_pages_per_seq=4, block_table_stride=4), 2),   # paged: below 16
     (dict(max_pages_per_seq=0), 2), (dict(block_table_stride=1), 2),
     (dict(block_table=None, num_pages=1), 2),        # dense cache: one page per sequence
     (dict(max_seqlen_k=33), 2),                      # beyond the capacity 2 x 16

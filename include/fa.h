@@ -284,6 +284,25 @@ typedef struct {
   const uint8_t* v_scale;
 } fa_fwd_mxfp8_args;
 
+/* Exact merge of partial attention results over disjoint key sets: the
+ * per-shard step of sequence-parallel attention, where part p is the forward
+ * of the same queries over shard p of the keys (e.g. fa_fwd on that shard).
+ * o_parts [nparts, B, S, H, d] (dtype FA_BF16 or FA_FP32) and lse_parts
+ * [nparts, B, H, S] fp32 are contiguous; o [B, S, H, d] bf16 (strides as
+ * fa_tensor), lse [B, H, S] fp32 contiguous.  With M = max_p LSE_p and
+ * w_p = exp(LSE_p - M): LSE = M + ln sum_p w_p, O = sum_p w_p O_p / sum_p w_p;
+ * a part with LSE_p = -inf has weight 0 and a row where every part has
+ * LSE_p = -inf gets O = 0, LSE = -inf.  d is 64 or 128; outputs must not
+ * overlap the parts.  Deterministic (parts are summed in order). */
+typedef struct {
+  fa_dtype dtype;
+  int32_t nparts, B, S, H, d;
+  const void* o_parts;
+  const float* lse_parts;
+  fa_tensor o;
+  float* lse;
+} fa_merge_args;
+
 /* Returns FA_ABI_VERSION. */
 int32_t fa_abi_version(void);
 
@@ -340,6 +359,9 @@ fa_status fa_quantize_fp8(const float* x, int64_t stride_b, int64_t stride_s,
                           int64_t stride_h, int32_t B, int32_t S, int32_t H,
                           int32_t d, int32_t per_tensor, void* codes,
                           float* scales, hipStream_t stream);
+
+/* Merge of partial results over key shards; see fa_merge_args. */
+fa_status fa_merge(const fa_merge_args* args, hipStream_t stream);
 
 /* MX FP8 forward; see fa_fwd_mxfp8_args. */
 fa_status fa_fwd_mxfp8(const fa_fwd_mxfp8_args* args, hipStream_t stream);

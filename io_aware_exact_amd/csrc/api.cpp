@@ -627,6 +627,36 @@ fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, in
   return hip_status(launch_quantize_fp8(x, sb, ss, sh, B, S, H, d, per_tensor != 0, codes, scales, stream));
 }
 
+fa_status fa_merge(const fa_merge_args* a, hipStream_t stream) {
+  if (!a) return FA_ERR_NULL;
+  if (a->dtype != FA_BF16 && a->dtype != FA_FP32) return FA_ERR_DTYPE;
+  if (a->nparts < 1 || a->B < 0 || a->S < 0 || a->H < 1) return FA_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
+  const int64_t rows = (int64_t)a->B * a->S * a->H;
+  if (rows == 0) return FA_OK;
+  if (!a->o_parts || !a->lse_parts || !a->o.ptr || !a->lse) return FA_ERR_NULL;
+  const int64_t es = a->dtype == FA_FP32 ? 4 : 2;
+  if (((uintptr_t)a->o_parts & (uintptr_t)(es - 1)) || ((uintptr_t)a->lse_parts & 3u) ||
+      ((uintptr_t)a->lse & 3u) || ((uintptr_t)a->o.ptr & 1u))
+    return FA_ERR_ALIGN;
+  if (a->o.stride_b < 0 || a->o.stride_s < 0 || a->o.stride_h < 0) return FA_ERR_SHAPE;
+  if ((rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const Span sop = {(uintptr_t)a->o_parts, (uintptr_t)a->o_parts + (uintptr_t)(a->nparts * rows * a->d * es)};
+  const Span slp = {(uintptr_t)a->lse_parts, (uintptr_t)(a->lse_parts + a->nparts * rows)};
+  const Span so = span4(a->o.ptr, a->B, a->S, a->H, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
+  const Span sl = {(uintptr_t)a->lse, (uintptr_t)(a->lse + rows)};
+  if (overlap(so, sop) || overlap(so, slp) || overlap(sl, sop) || overlap(sl, slp) || overlap(so, sl))
+    return FA_ERR_ALIAS;
+  MergeParams p = {};
+  p.o_parts = a->o_parts;
+  p.lse_parts = a->lse_parts;
+  p.o = a->o.ptr;
+  p.lse = a->lse;
+  p.o_sb = a->o.stride_b; p.o_ss = a->o.stride_s; p.o_sh = a->o.stride_h;
+  p.nparts = a->nparts; p.B = a->B; p.S = a->S; p.H = a->H;
+  return hip_status(launch_merge(p, a->d, a->dtype == FA_FP32, stream));
+}
+
 fa_status fa_fwd_mxfp8(const fa_fwd_mxfp8_args* a, hipStream_t stream) {
   if (!a) return FA_ERR_NULL;
   // the dense FP8 rules (shapes, strides in bytes, alignment, aliasing)

@@ -114,6 +114,18 @@ struct KvAppendParams {
   int B, Hkv;
 };
 
+// Merge of partial results over key shards: parts [nparts, B, S, H, d]
+// (bf16 or fp32, contiguous) and [nparts, B, H, S] fp32.
+struct MergeParams {
+  const void* o_parts;
+  const float* lse_parts;
+  void* o;
+  float* lse;                 // [B, H, S] contiguous
+  int64_t o_sb, o_ss, o_sh;
+  int nparts, B, S, H;
+};
+hipError_t launch_merge(const MergeParams& p, int d, bool f32, hipStream_t stream);
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen,
                            hipStream_t stream);
 hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varlen,

@@ -121,6 +121,13 @@ class FwdMxfp8Args(ctypes.Structure):
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
+class MergeArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("nparts", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("o_parts", ctypes.c_void_p), ("lse_parts", ctypes.c_void_p), ("o", FaTensor),
+                ("lse", ctypes.c_void_p)]
+
+
 FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 
 
@@ -128,7 +135,8 @@ FA_BWD_ALL, FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2, 4
 EXPORTS = ["fa_abi_version", "fa_status_string", "fa_fwd_workspace_size",
            "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
            "fa_bwd_varlen_workspace_size", "fa_bwd_varlen", "fa_fwd_kvcache_workspace_size",
-           "fa_fwd_kvcache", "fa_quantize_fp8", "fa_fwd_mxfp8", "fa_quantize_mxfp8"]
+           "fa_fwd_kvcache", "fa_quantize_fp8", "fa_fwd_mxfp8", "fa_quantize_mxfp8",
+           "fa_merge"]
 
 _lib = None
 
@@ -168,6 +176,8 @@ def lib():
         L.fa_quantize_fp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
         L.fa_fwd_mxfp8.restype = ctypes.c_int
         L.fa_fwd_mxfp8.argtypes = [ctypes.POINTER(FwdMxfp8Args), vp]
+        L.fa_merge.restype = ctypes.c_int
+        L.fa_merge.argtypes = [ctypes.POINTER(MergeArgs), vp]
         L.fa_quantize_mxfp8.restype = ctypes.c_int
         L.fa_quantize_mxfp8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
         _lib = L
@@ -441,6 +451,24 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=Non
                 _t4(q8), _t4(k8), _t4(v8), _t4(out), lse.data_ptr(), q_descale.data_ptr(),
                 k_descale.data_ptr(), v_descale.data_ptr(), None, 0)
     _check("fa_fwd", lib().fa_fwd(ctypes.byref(a), _stream()))
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out=None, lse=None):
+    """Exact merge of partial results over disjoint key shards: o_parts
+    [P,B,S,H,d] (bf16 or fp32) and lse_parts [P,B,H,S] fp32, contiguous ->
+    (o [B,S,H,d] bf16, lse [B,H,S] fp32)."""
+    P, B, S, H, d = o_parts.shape
+    assert o_parts.is_contiguous() and lse_parts.is_contiguous()
+    assert lse_parts.shape == (P, B, H, S) and lse_parts.dtype == torch.float32
+    if out is None:
+        out = torch.empty((B, S, H, d), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    dt = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}.get(o_parts.dtype, -1)
+    a = MergeArgs(dt, P, B, S, H, d, o_parts.data_ptr(), lse_parts.data_ptr(), _t4(out),
+                  lse.data_ptr())
+    _check("fa_merge", lib().fa_merge(ctypes.byref(a), _stream()))
     return out, lse
 
 

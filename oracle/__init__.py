@@ -340,3 +340,24 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, k_ne
                 o[b, pos, h, :] = ob
                 lse[b, h, pos] = lb
     return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Exact merge of partial attention results over disjoint key sets
+    (sequence-parallel attention; the same identity merges the split-KV
+    decode chunks): o_parts [P,B,S,H,d], lse_parts [P,B,H,S] ->
+    o [B,S,H,d], lse [B,H,S], with M = max_p LSE_p, w_p = exp(LSE_p - M),
+    LSE = M + ln sum_p w_p and O = sum_p w_p O_p / sum_p w_p.  Rows where
+    every part has LSE_p = -inf get O = 0, LSE = -inf."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    M = lse_parts.max(axis=0)                                   # [B,H,S]
+    fin = np.isfinite(M)
+    Ms = np.where(fin, M, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - Ms[None]), 0.0)   # [P,B,H,S]
+    wsum = w.sum(axis=0)
+    wt = w.transpose(0, 1, 3, 2)[..., None]                     # [P,B,S,H,1]
+    o = (wt * o_parts).sum(axis=0)
+    ws = wsum.transpose(0, 2, 1)[..., None]
+    o = np.where(ws > 0, o / np.where(ws > 0, ws, 1.0), 0.0)
+    lse = np.where(wsum > 0, Ms + np.log(np.where(wsum > 0, wsum, 1.0)), -np.inf)
+    return o, lse

@@ -217,7 +217,8 @@ def test_struct_layouts_match_header(tmp_path):
     (checked with the host C compiler)."""
     structs = {"fa_fwd_args": fa.FwdArgs, "fa_fwd_varlen_args": fa.FwdVarlenArgs,
                "fa_bwd_args": fa.BwdArgs, "fa_bwd_varlen_args": fa.BwdVarlenArgs,
-               "fa_fwd_kvcache_args": fa.FwdKvcacheArgs, "fa_fwd_mxfp8_args": fa.FwdMxfp8Args}
+               "fa_fwd_kvcache_args": fa.FwdKvcacheArgs, "fa_fwd_mxfp8_args": fa.FwdMxfp8Args,
+               "fa_merge_args": fa.MergeArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fa.h"', 'int main(void) {']
     expect = []
     for cname, cls in structs.items():
@@ -270,3 +271,20 @@ def test_quantize_mxfp8_rejects():
     assert L.fa_quantize_mxfp8(FAKE, 0, 0, 0, 1, 1, 1, 64, 0, FAKE + (1 << 24) + 4, FAKE + (2 << 24), None) == 6
     assert L.fa_quantize_mxfp8(FAKE, 64, 64, 64, 1, 4, 1, 64, 1, FAKE + 16, FAKE + (2 << 24), None) == 8
     assert L.fa_quantize_mxfp8(FAKE, 0, 0, 0, 0, 1, 1, 64, 0, FAKE + (1 << 24), FAKE + (2 << 24), None) == 0
+
+
+def test_merge_rejects():
+    L = fa.lib()
+    def m(**kw):
+        base = dict(dtype=0, nparts=2, B=1, S=4, H=2, d=64)
+        base.update({k: v for k, v in kw.items() if k in base})
+        return fa.MergeArgs(base["dtype"], base["nparts"], base["B"], base["S"], base["H"], base["d"],
+                            kw.get("o_parts", FAKE), kw.get("lse_parts", FAKE + (1 << 24)),
+                            kw.get("o", fa.FaTensor(FAKE + (2 << 24), 512, 128, 64)),
+                            kw.get("lse", FAKE + (3 << 24)))
+    assert L.fa_merge(None, None) == 1
+    for kw, st in ((dict(dtype=2), 4), (dict(nparts=0), 2), (dict(d=96), 3), (dict(lse=None), 1),
+                   (dict(lse_parts=FAKE + (1 << 24) + 2), 6),
+                   (dict(o=fa.FaTensor(FAKE + 256, 512, 128, 64)), 8)):
+        assert L.fa_merge(ctypes.byref(m(**kw)), None) == st, kw
+    assert L.fa_merge(ctypes.byref(m(S=0)), None) == 0

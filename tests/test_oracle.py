@@ -505,3 +505,31 @@ def test_kvcache_empty_sequence():
     o, lse = oracle.attention_kvcache(q, kc, vc, lens, bt, None, None, False)
     assert np.all(o[0] == 0) and np.all(lse[0] == -np.inf)
     assert np.all(np.isfinite(lse[1]))
+
+
+def test_merge_of_key_shards_is_full_attention():
+    # attention over all keys equals the merge of attention over key shards
+    # (computed directly, no merge involved on the reference side)
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((2, 9, 4, 16))
+    k = rng.standard_normal((2, 23, 2, 16))
+    v = rng.standard_normal((2, 23, 2, 16))
+    o, lse = oracle.attention_fwd(q, k, v, False, 0.4)
+    cuts = [0, 5, 6, 17, 23]
+    parts = [oracle.attention_fwd(q, k[:, a:b], v[:, a:b], False, 0.4) for a, b in zip(cuts, cuts[1:])]
+    om, lm = oracle.merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, lse, atol=1e-13)
+
+
+def test_merge_with_empty_parts():
+    # a part that sees no key (LSE = -inf) has no weight; a row no part sees
+    # is O = 0, LSE = -inf
+    rng = np.random.default_rng(13)
+    o_parts = rng.standard_normal((3, 1, 2, 1, 8))
+    lse = np.array([[[[0.5, -np.inf]]], [[[-np.inf, -np.inf]]], [[[1.5, -np.inf]]]])   # [3,1,1,2]
+    o, l = oracle.merge_partials(o_parts, lse)
+    w = np.exp(np.array([0.5, 1.5]) - 1.5)
+    np.testing.assert_allclose(o[0, 0, 0], (w[0] * o_parts[0, 0, 0, 0] + w[1] * o_parts[2, 0, 0, 0]) / w.sum())
+    assert l[0, 0, 0] == 1.5 + np.log(w.sum())
+    assert np.all(o[0, 1, 0] == 0) and l[0, 0, 1] == -np.inf

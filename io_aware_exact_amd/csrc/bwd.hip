@@ -305,6 +305,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
         s2[0] = mfma32(a0, bf[c], s2[0]);
         s2[1] = mfma32(a1, bf[c], s2[1]);
       }
+      // keep the operand reads four MFMAs ahead of the products (left to
+      // itself the compiler issues them two ahead and waits on each pair)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * T::NC - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // ---- B operands of the second product: P (P-wave) or dS (dS-wave)
       bf16x8 ob[2][2];
       if (pwave) {
@@ -580,11 +589,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
+        if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < T::NC; ++c) {
           const int off = aoff[c] + 32 * kb2 * D;
           s = mfma32(*(const bf16x8*)(Ks + off), qf[c], s);
           dp = mfma32(*(const bf16x8*)(Vs + off), of[c], dp);
+        }
+        if constexpr (D == 128) {
+          // d=128: fence the 16 products and keep their operand reads four
+          // MFMAs ahead (left to itself the compiler waits on each read; at
+          // d=64 its own schedule is faster)
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * T::NC - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         // Keys past lim (sequence end, causal diagonal) get P = 0.  Register
         // i of this lane holds key j0 + 32 kb2 + 8 hh + r_i with r_i a

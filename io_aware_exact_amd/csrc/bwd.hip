@@ -218,25 +218,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       buf_load16_lds(rq, qbase + qoff[u], Qs + (8 * (wave & 7) + RPI * u) * D);
       buf_load16_lds(rdo, dobase + dooff[u], Os + (8 * (wave & 7) + RPI * u) * D);
     }
-    // threads 0..63 fetch LSE (as log2 values), threads 64..127 fetch D
+    // threads 0..63 fetch LSE, threads 64..127 fetch D (used only when the
+    // stage is completed, so no wait here)
     if (tid < 2 * T::BQ) {
       const int r = q0 + (tid & (T::BQ - 1));
-      if (tid < T::BQ) {
-        const float v = r < Lq ? lse_h[r] : INFINITY;
-        // no visible key (LSE = -inf) or padding: probabilities are zero
-        sval = (v == -INFINITY) ? INFINITY : v * LOG2E;
-      } else {
-        sval = r < Lq ? del_h[r] : 0.f;
-      }
+      if (tid < T::BQ) sval = r < Lq ? lse_h[r] : INFINITY;
+      else sval = r < Lq ? del_h[r] : 0.f;
     }
     if (++ld_qt == per_head) {
       ld_qt = 0;
       if (++ld_h < p.group) set_head(ld_h);
     }
   };
+  // LSE is stored as a log2 value; no visible key (LSE = -inf) or padding
+  // (+inf) makes the probabilities zero
   auto lstore_stats = [&](int st) {
     float* stats = (float*)(stage(st) + 2 * T::TILE);
-    if (tid < 2 * T::BQ) stats[tid] = sval;
+    if (tid < T::BQ) stats[tid] = (sval == -INFINITY) ? INFINITY : sval * LOG2E;
+    else if (tid < 2 * T::BQ) stats[tid] = sval;
   };
   // bf16 P of key group kgrp, query block qb, in P-exchange slot sl, stored
   // lane-interleaved (16 consecutive lanes write 256 contiguous bytes)
@@ -577,10 +576,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * T::BN;
+    // The K^T reads of tile t - 1 are issued before the DMA of tile t + 1:
+    // the compiler cannot tell the transposing reads from a read of the
+    // stage being filled, and would wait for the whole DMA first.
+    if (t >= 1 && t - 1 < nt_w) dq_product(t - 1);
     // tile t + 1 goes to K stage (t+1)%3 and V stage (t+1)&1, last read in
     // iteration t - 1
     if (t + 1 < ntiles) dma(t + 1);
-    if (t >= 1 && t - 1 < nt_w) dq_product(t - 1);
     if (t < nt_w) {
       const __bf16* Ks = kstage(t % 3);
       const __bf16* Vs = vstage(t & 1);

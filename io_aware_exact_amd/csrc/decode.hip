@@ -159,17 +159,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
         const int first_tok = pn << shift;
         const int rows = max(0, min(Lk - first_tok, 1 << shift));
         const uint32_t rel = (uint32_t)(j0 - first_tok);
-        buf_load16_lds(make_rsrc(kcb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2)),
-                       rel * (uint32_t)p.k_ss * 2 + koff[u], kstage(st) + RPI * u * D);
-        buf_load16_lds(make_rsrc(vcb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2)),
-                       rel * (uint32_t)p.v_ss * 2 + voff[u], vstage(st) + RPI * u * D);
+        buf_load16_lds_stream(make_rsrc(kcb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2)),
+                              rel * (uint32_t)p.k_ss * 2 + koff[u], kstage(st) + RPI * u * D);
+        buf_load16_lds_stream(make_rsrc(vcb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2)),
+                              rel * (uint32_t)p.v_ss * 2 + voff[u], vstage(st) + RPI * u * D);
       }
     } else {
       const uint32_t kb0 = (uint32_t)j0 * (uint32_t)p.k_ss * 2, vb0 = (uint32_t)j0 * (uint32_t)p.v_ss * 2;
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        buf_load16_lds(rk, kb0 + koff[u], kstage(st) + RPI * u * D);
-        buf_load16_lds(rv, vb0 + voff[u], vstage(st) + RPI * u * D);
+        buf_load16_lds_stream(rk, kb0 + koff[u], kstage(st) + RPI * u * D);
+        buf_load16_lds_stream(rv, vb0 + voff[u], vstage(st) + RPI * u * D);
       }
     }
   };

@@ -67,7 +67,9 @@ struct FwdTile {
 };
 
 template <int D, bool CAUSAL, bool VARLEN, bool KVC>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
+// d=64: three workgroups per CU fit in LDS; the bound keeps every instance
+// within the registers of three waves per SIMD
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
 
@@ -272,34 +274,53 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(FwdParams p) {
       // grew by more than 2^8 in exp2 units (probabilities then stay <= 256,
       // fine for fp32 sums and bf16 operands); after the first tiles this
       // almost never happens and the 64 O_acc multiplies are skipped.
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const bool grow = mx > m_run + lazy_margin;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.f;
-        if (grow) m_run = mx;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
-      }
-      const float nb = (m_run == -INFINITY) ? 0.f : -m_run * c2;
+      // Causal: once every row of the wave has an m, the exponentials are
+      // first taken against it without forming the tile max; if every lane's
+      // partial row sum is still at most 2^8, no probability exceeds 2^8 and
+      // the tile is done.  Only otherwise is the tile max formed and the
+      // exponentials redone.  (Without the causal mask the extra code costs
+      // registers: the non-causal instances would spill at three waves per
+      // SIMD, and run slower at two.)
       float rs = 0.f;
       bf16x8 pf[4];
+      auto exponentials = [&](float nb) {
+        rs = 0.f;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+          for (int half = 0; half < 2; ++half) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = fast_exp2(__builtin_fmaf(sacc[kb2][8 * half + e], c2, nb));
-            rs += pv;
-            pf[2 * kb2 + half][e] = (__bf16)pv;
+            for (int e = 0; e < 8; ++e) {
+              const float pv = fast_exp2(__builtin_fmaf(sacc[kb2][8 * half + e], c2, nb));
+              rs += pv;
+              pf[2 * kb2 + half][e] = (__bf16)pv;
+            }
           }
+      };
+      bool exact = true;
+      if constexpr (CAUSAL) {
+        if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+          exponentials(-m_run * c2);
+          exact = __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0;
         }
+      }
+      if (exact) {
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const bool grow = mx > m_run + lazy_margin;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.f;
+          if (grow) m_run = mx;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+        }
+        exponentials((m_run == -INFINITY) ? 0.f : -m_run * c2);
+      }
       l_run += rs;
       // ---- O^T += V^T P^T
       const __bf16* vbase = Vs + tr_row * T::VSTR + tr_col;

@@ -266,33 +266,48 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
           if (kj > lim) sacc[kb2][i] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const bool grow = mx > m_run + lazy_margin;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.f;
-      if (grow) m_run = mx;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
-    }
-    const float nb = (m_run == -INFINITY) ? 0.f : -m_run * c2;
     float rs = 0.f;
+    auto exponentials = [&](float nb) {
+      rs = 0.f;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = fast_exp2(__builtin_fmaf(sacc[kb2][8 * half + e], c2, nb));
-          rs += pv;
-          pf[2 * kb2 + half][e] = (__bf16)pv;
+          for (int e = 0; e < 8; ++e) {
+            const float pv = fast_exp2(__builtin_fmaf(sacc[kb2][8 * half + e], c2, nb));
+            rs += pv;
+            pf[2 * kb2 + half][e] = (__bf16)pv;
+          }
         }
+    };
+    // Once every row of the wave has an m, the exponentials are first taken
+    // against it without forming the tile max: if every lane's partial row
+    // sum is still at most 2^8, no probability exceeds 2^8 and the tile is
+    // done.  Only otherwise is the tile max formed, m, l and O_acc rescaled
+    // (lazily, as above) and the exponentials redone.
+    bool exact = true;
+    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+      exponentials(-m_run * c2);
+      exact = __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0;
+    }
+    if (exact) {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const bool grow = mx > m_run + lazy_margin;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.f;
+        if (grow) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
       }
+      exponentials((m_run == -INFINITY) ? 0.f : -m_run * c2);
+    }
     l_run += rs;
     __asm__ volatile("" : "+v"(l_run));   // the row sum belongs to this phase
   };

@@ -105,6 +105,50 @@ def test_varlen_equals_dense_per_sequence():
         assert torch.equal(od[0], o[qs:qe]) and torch.equal(ld[0], lse[:, qs:qe])
 
 
+def check_against_oracle(q, k, v, causal):
+    o, lse = fa.fwd(q, k, v, causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, causal)
+    check_o("O", o.float().cpu().numpy(), o_ref)
+    seen = np.isfinite(lse_ref)
+    check_lse("LSE", lse.cpu().numpy()[seen], lse_ref[seen])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores(d, causal):
+    """Keys whose norm grows along the sequence (x1 to x4), so later key
+    tiles hold much larger scores than the first ones: the running max has
+    to move while the tiles stream, which the first tiles alone never ask."""
+    print(f"growing scores d={d} causal={causal}", flush=True)
+    q, k, v = inputs.qkv(1, 1000, 1000, 4, 2, d, 71 + d, device="cuda")
+    ramp = torch.linspace(1.0, 4.0, 1000, device="cuda").view(1, 1000, 1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    check_against_oracle(q, k, v, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_steps(d, causal):
+    """Every query row is the all-ones vector and key j is beta_j times it,
+    so every score of key j is exactly scale * d * beta_j.  The key blocks
+    step through: 0 (the first 100 keys), +6 in exp2 units (probabilities of
+    64 against the first max: partial row sums far above 2^8 while no single
+    probability passes 2^8), -40 (probabilities that underflow), +12 (a max
+    that grows past 2^8) and +6 again."""
+    print(f"score steps d={d} causal={causal}", flush=True)
+    S = 1000
+    log2e = 1.0 / math.log(2.0)
+    unit = (1.0 / math.sqrt(d)) * d * log2e          # exp2 units per unit of beta
+    beta = torch.zeros(S)
+    for lo, hi, e2 in [(100, 300, 6.0), (300, 450, -40.0), (450, 700, 12.0), (700, S, 6.0)]:
+        beta[lo:hi] = e2 / unit
+    q = torch.ones((1, S, 2, d), dtype=torch.bfloat16, device="cuda")
+    k = (beta.view(1, S, 1, 1) * torch.ones((1, S, 1, d))).to(torch.bfloat16).cuda()
+    _, _, v = inputs.qkv(1, S, S, 2, 1, d, 81 + d, device="cuda")
+    check_against_oracle(q, k, v, causal)
+
+
 @pytest.mark.parametrize("decode", [False, True])
 def test_no_keys(decode):
     """Sk = 0: every row sees no key, so O = 0 and LSE = -inf (no NaN); the

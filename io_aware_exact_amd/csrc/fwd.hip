@@ -369,11 +369,9 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
+// d = 64 (d = 128 runs the ping-pong kernel)
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
-  if (d == 128) {
-    if (causal) return varlen ? launch<128, true, true>(p, stream) : launch<128, true, false>(p, stream);
-    return varlen ? launch<128, false, true>(p, stream) : launch<128, false, false>(p, stream);
-  }
+  if (d != 64) return hipErrorInvalidValue;
   if (causal) return varlen ? launch<64, true, true>(p, stream) : launch<64, true, false>(p, stream);
   return varlen ? launch<64, false, true>(p, stream) : launch<64, false, false>(p, stream);
 }

@@ -613,15 +613,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
         }
         // Keys past lim (sequence end, causal diagonal) get P = 0.  Register
         // i of this lane holds key j0 + 32 kb2 + 8 hh + r_i with r_i a
-        // constant, so the test is r_i > thr for one per-lane threshold (set
-        // out of reach on tiles that need no mask): one compare and one
-        // select per element, with no per-element index arithmetic.
-        const int thr = need_mask ? lim - j0 - 32 * kb2 - 8 * hh : 0x7fffffff;
+        // constant, so the test is r_i > thr for one per-lane threshold: one
+        // compare and one select per element, with no per-element index
+        // arithmetic, and only on tiles that need a mask.
+        // need_mask is wave-uniform; saying so gives a real branch (the
+        // compiler would otherwise select on every element of every tile)
+        if (__builtin_amdgcn_readfirstlane((int)need_mask) != 0) {
+          const int thr = lim - j0 - 32 * kb2 - 8 * hh;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(__builtin_fmaf(s[i], c2, -lse2));
-          if (perm_row_of_reg(i, 0) > thr) pv = 0.f;
-          dsb[2 * kb2 + (i >> 3)][i & 7] = (__bf16)(pv * (dp[i] - dlt));
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(__builtin_fmaf(s[i], c2, -lse2));
+            if (perm_row_of_reg(i, 0) > thr) pv = 0.f;
+            dsb[2 * kb2 + (i >> 3)][i & 7] = (__bf16)(pv * (dp[i] - dlt));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = fast_exp2(__builtin_fmaf(s[i], c2, -lse2));
+            dsb[2 * kb2 + (i >> 3)][i & 7] = (__bf16)(pv * (dp[i] - dlt));
+          }
         }
       }
     }

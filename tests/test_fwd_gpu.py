@@ -149,6 +149,24 @@ def test_score_steps(d, causal):
     check_against_oracle(q, k, v, causal)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_growing_scores(d, causal):
+    """Packed sequences whose keys grow along each sequence (x1 to x4), so the
+    running max moves mid-sequence in every sequence of the pack."""
+    lens = [700, 65, 300, 1000]
+    print(f"varlen growing scores lens={lens} d={d} causal={causal}", flush=True)
+    q, k, v = inputs.packed_qkv(lens, lens, 4, 2, d, 91 + d, device="cuda")
+    ramp = torch.cat([torch.linspace(1.0, 4.0, n) for n in lens]).view(-1, 1, 1).cuda()
+    k = (k.float() * ramp).to(torch.bfloat16)
+    cu = inputs.cu_seqlens(lens, device="cuda")
+    o, lse = fa.fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_varlen(q, k, v, cu.cpu(), cu.cpu(), causal)
+    check_o("O", o.float().cpu().numpy(), o_ref)
+    check_lse("LSE", lse.cpu().numpy(), lse_ref)
+
+
 @pytest.mark.parametrize("decode", [False, True])
 def test_no_keys(decode):
     """Sk = 0: every row sees no key, so O = 0 and LSE = -inf (no NaN); the

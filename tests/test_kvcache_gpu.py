@@ -26,10 +26,12 @@ def same_cache(got, ref):
                 torch.equal(got[~nan].view(torch.int16), ref[~nan].view(torch.int16)))
 
 
-def build_case(lens, snew, sq, Hq, Hkv, d, page_size, paged, seed, spare=3):
+def build_case(lens, snew, sq, Hq, Hkv, d, page_size, paged, seed, spare=3, ramp=False):
     """Cache, block table and inputs.  Paged: each sequence gets
     ceil((len + snew) / page_size) pages, handed out in a shuffled order
-    from a pool with `spare` unused pages.  Dense: a [B, capacity] cache."""
+    from a pool with `spare` unused pages.  Dense: a [B, capacity] cache.
+    ramp: the key at position j of a sequence of total length n is scaled
+    by 1 + 3 j / n, so later keys give larger scores."""
     B = len(lens)
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
@@ -48,12 +50,16 @@ def build_case(lens, snew, sq, Hq, Hkv, d, page_size, paged, seed, spare=3):
         npages, bt, cap = B, None, max(L + snew for L in lens) + 5
     kc = torch.full((npages, cap, Hkv, d), float("nan"))
     vc = torch.full((npages, cap, Hkv, d), float("nan"))
+    grow = lambda j, b: (1.0 + 3.0 * j / (lens[b] + snew)) if ramp else 1.0
     for b, L in enumerate(lens):
         for j in range(L):
             p, s = (int(bt[b, j // page_size]), j % page_size) if paged else (b, j)
-            kc[p, s] = torch.randn((Hkv, d), generator=g)
+            kc[p, s] = torch.randn((Hkv, d), generator=g) * grow(j, b)
             vc[p, s] = torch.randn((Hkv, d), generator=g)
     kn = torch.randn((B, snew, Hkv, d), generator=g)
+    for b, L in enumerate(lens):
+        for i in range(snew):
+            kn[b, i] *= grow(L + i, b)
     vn = torch.randn((B, snew, Hkv, d), generator=g)
     q = torch.randn((B, sq, Hq, d), generator=g)
     bf = lambda x: x.to(torch.bfloat16)
@@ -61,10 +67,11 @@ def build_case(lens, snew, sq, Hq, Hkv, d, page_size, paged, seed, spare=3):
 
 
 def run_kvcache(lens, snew, sq, Hq, Hkv, d, page_size, paged, causal, seed,
-                use_workspace=True, scale=None):
+                use_workspace=True, scale=None, ramp=False):
     print(f"kvcache lens={lens} snew={snew} sq={sq} Hq={Hq} Hkv={Hkv} d={d} page={page_size} "
-          f"paged={paged} causal={causal} ws={use_workspace} seed={seed}", flush=True)
-    q, kc, vc, lens_t, bt, kn, vn = build_case(lens, snew, sq, Hq, Hkv, d, page_size, paged, seed)
+          f"paged={paged} causal={causal} ws={use_workspace} seed={seed} ramp={ramp}", flush=True)
+    q, kc, vc, lens_t, bt, kn, vn = build_case(lens, snew, sq, Hq, Hkv, d, page_size, paged, seed,
+                                               ramp=ramp)
     dq, dkc, dvc = q.cuda(), kc.cuda(), vc.cuda()
     dlens = lens_t.cuda()
     dbt = bt.cuda() if bt is not None else None
@@ -119,6 +126,14 @@ def test_decode_without_append():
 def test_chunked_prefill(d, page_size, causal):
     # Sq = Snew = 200 new tokens appended after 0, 100 and 513 cached ones
     run_kvcache([0, 100, 513], 200, 200, 4, 1, d, page_size, True, causal, seed=41)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunked_prefill_growing_scores(d, causal):
+    # keys grow along each sequence, so the running max moves while the
+    # cached and the appended keys stream
+    run_kvcache([0, 100, 513], 200, 200, 4, 1, d, 64, True, causal, seed=43, ramp=True)
 
 
 def test_decode_shape_without_workspace_takes_tiled_path():

@@ -280,7 +280,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
       l_run *= alpha;
       // O_hat <- O_hat alpha sv_prev / sv; skipped when that factor is 1 in
       // every lane (same V block, no row max grew)
-      const float resc = alpha * (sv_prev / sv);
+      // (sv changes every other tile; the hardware reciprocal's last-bit
+      // error only changes the units O_hat is kept in)
+      const float resc = sv == sv_prev ? alpha : alpha * (sv_prev * __builtin_amdgcn_rcpf(sv));
       if (__builtin_amdgcn_ballot_w64(resc != 1.f) != 0) {
 #pragma unroll
         for (int i = 0; i < T::ND; ++i) oacc[i] *= resc;

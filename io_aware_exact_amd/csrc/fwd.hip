@@ -238,7 +238,10 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
     const bool more = t + 1 < ntiles;
     if (more) gload(j0 + BN);
 
-    const bool wave_active = !CAUSAL || j0 <= wave_last_row + diag;
+    // Non-causal: always true, but kept opaque to the compiler, which
+    // otherwise schedules the loop into more registers than three waves per
+    // SIMD allow once the softmax has its two paths.
+    const bool wave_active = CAUSAL ? j0 <= wave_last_row + diag : __builtin_amdgcn_readfirstlane(ntiles) > 0;
     if (wave_active) {
       const __bf16* Ks = smem + st * T::STAGE;
       const __bf16* Vs = Ks + BN * T::KSTR;
@@ -274,13 +277,11 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
       // grew by more than 2^8 in exp2 units (probabilities then stay <= 256,
       // fine for fp32 sums and bf16 operands); after the first tiles this
       // almost never happens and the 64 O_acc multiplies are skipped.
-      // Causal: once every row of the wave has an m, the exponentials are
-      // first taken against it without forming the tile max; if every lane's
+      // Once every row of the wave has an m, the exponentials are first
+      // taken against it without forming the tile max; if every lane's
       // partial row sum is still at most 2^8, no probability exceeds 2^8 and
       // the tile is done.  Only otherwise is the tile max formed and the
-      // exponentials redone.  (Without the causal mask the extra code costs
-      // registers: the non-causal instances would spill at three waves per
-      // SIMD, and run slower at two.)
+      // exponentials redone.
       float rs = 0.f;
       bf16x8 pf[4];
       auto exponentials = [&](float nb) {
@@ -298,11 +299,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
           }
       };
       bool exact = true;
-      if constexpr (CAUSAL) {
-        if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
-          exponentials(-m_run * c2);
-          exact = __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0;
-        }
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+        exponentials(-m_run * c2);
+        exact = __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0;
       }
       if (exact) {
         float mx = sacc[0][0];

@@ -378,6 +378,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
           }
         }
       }
+      // the transposing reads two MFMAs ahead of the products (the
+      // compiler's own schedule issues nearly all of them first)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * T::ND - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // gload filled stage (it + 1) % 3, last read by the dS-wave in
     // iteration it - 1; P slot it % 2 is read in iteration it + 1; both are

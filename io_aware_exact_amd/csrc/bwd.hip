@@ -577,6 +577,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(BwdParams p) {
                                    lds_read_tr16(Ks + toff[1][dbk] + 16 * c * D));
         dq[dbk] = mfma32(ka, dsb[c], dq[dbk]);
       }
+    // the transposing reads two MFMAs ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * T::ND - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
   if (ntiles > 0) dma(0);

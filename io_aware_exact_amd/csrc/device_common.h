@@ -178,6 +178,10 @@ struct PageWindow {
     if (base < 0 || first < base || last >= base + 64) {
       base = first;
       pages = row[min(first + lane, max_page_no)];
+      // Wait here, on this rare path: otherwise the compiler waits before
+      // every later read of the window, for all loads then in flight (the
+      // tile loads just issued included).
+      wait_vmem();
     }
   }
   __device__ __forceinline__ int uniform(int page_no) const {

@@ -443,7 +443,7 @@ def main():
                      "achieved": round(dk_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dk_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile("bwd_dkdv_b2_h16_s8192_d128", BWD_SOURCES)},
-        "roofline_fwd": {"kernel": "fwd_bf16_pp_kernel<128,false,false,false>", "bound": "mfma",
+        "roofline_fwd": {"kernel": "fwd_bf16_pp_kernel<128,false,false,0>", "bound": "mfma",
                          "achieved": tf(ff, ms_fwd), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profile("fwd_bf16_b2_h16_s8192_d128", FWD_SOURCES)},

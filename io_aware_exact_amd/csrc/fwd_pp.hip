@@ -52,7 +52,10 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KVC>
+// KVC: 0 the dense or packed tensors; a KV cache of 1 one region per
+// sequence (no block table), 2 pages of at least 64 tokens, 3 smaller pages
+// (each layout its own instance, which folds away the paths it cannot take)
+template <int D, bool CAUSAL, bool VARLEN, int KVC>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   using T = PpTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   // over the page's rows that hold tokens (rows past the end read as zero).
   // Smaller pages: each row's page comes from the window by a cross-lane
   // permute, and rows past the end read the last row (finite; masked).
-  const bool paged = KVC && p.kv.block_table != nullptr;
+  constexpr bool paged = KVC >= 2;
   const int shift = p.kv.page_shift;
   const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
   const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       if (!paged) {
 #pragma unroll
         for (int u = 0; u < T::NP; ++u) regs[u] = buf_load16(rd, off + (uint32_t)(j0 + u * T::RPP) * (uint32_t)ss * 2);
-      } else if (shift >= 6) {
+      } else if (KVC == 2) {
         const int pn = j0 >> shift;
         win.cover(btrow, pn, pn, last_page_no, lane);
         const int64_t page = win.uniform(pn);
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KVC = false>
+template <int D, bool CAUSAL, bool VARLEN, int KVC = 0>
 hipError_t launch(FwdParams p, hipStream_t stream) {
   const int rows = p.Sq;   // dense: Sq; varlen: max query length
   p.num_m_tiles = (rows + BM - 1) / BM;
@@ -423,5 +426,7 @@ hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varle
 // table, each sequence's length is its cached count plus the appended rows.
 hipError_t launch_fwd_bf16_pp_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream) {
   if (d != 128) return hipErrorInvalidValue;
-  return causal ? launch<128, true, false, true>(p, stream) : launch<128, false, false, true>(p, stream);
+  if (!p.kv.block_table) return causal ? launch<128, true, false, 1>(p, stream) : launch<128, false, false, 1>(p, stream);
+  if (p.kv.page_shift >= 6) return causal ? launch<128, true, false, 2>(p, stream) : launch<128, false, false, 2>(p, stream);
+  return causal ? launch<128, true, false, 3>(p, stream) : launch<128, false, false, 3>(p, stream);
 }

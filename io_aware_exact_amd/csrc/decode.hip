@@ -31,7 +31,7 @@
 //     DMA stay outstanding.
 //   * A second kernel combines the partials of every row.
 //   * KV-cache attention (an appended, possibly paged cache) runs the same
-//     kernel with KVC = true: each sequence's length is its cached count plus
+//     kernel with KVC = 1 or 2: each sequence's length is its cached count plus
 //     the appended rows; each DMA covers a few consecutive rows inside one
 //     page (pages hold at least 16 tokens) and reads them through that page's
 //     buffer resource, found in a window of block-table entries.
@@ -75,7 +75,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // physical slot.  KV cache: a DMA covers RPI consecutive rows, inside one
 // page for pages of >= 16 tokens, so each DMA takes the page's buffer
 // resource (rows past the sequence end read as zero).
-template <int D, bool KVC, int NST>
+// KVC: 0 the dense tensors; a KV cache of 1 one region per sequence (no
+// block table) or 2 pages (each its own instance, which folds away the
+// other's load path).
+template <int D, int KVC, int NST>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   using T = DecTile<D>;
   constexpr int TILE = BNK * D;            // elements of one K or V tile
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     koff[u] = (uint32_t)(row * p.k_ss + col) * 2;
     voff[u] = (uint32_t)(row * p.v_ss + col) * 2;
   }
-  const bool paged = KVC && p.kv.block_table != nullptr;
+  constexpr bool paged = KVC == 2;
   const int shift = p.kv.page_shift;
   const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
   const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 
 constexpr int kDecodeStages = 2;   // DMA stages per wave (3 measured slower)
 
-template <int D, bool KVC>
+template <int D, int KVC>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const long nblk = (long)p.B * p.Hkv * p.nsplit;
   if (nblk <= 0) return hipSuccess;
@@ -338,9 +341,10 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) {
-  return d == 128 ? launch<128, false>(p, stream) : launch<64, false>(p, stream);
+  return d == 128 ? launch<128, 0>(p, stream) : launch<64, 0>(p, stream);
 }
 
 hipError_t launch_decode_bf16_kvcache(const DecodeParams& p, int d, hipStream_t stream) {
-  return d == 128 ? launch<128, true>(p, stream) : launch<64, true>(p, stream);
+  if (!p.kv.block_table) return d == 128 ? launch<128, 1>(p, stream) : launch<64, 1>(p, stream);
+  return d == 128 ? launch<128, 2>(p, stream) : launch<64, 2>(p, stream);
 }

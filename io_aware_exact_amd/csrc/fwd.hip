@@ -66,9 +66,12 @@ struct FwdTile {
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
-template <int D, bool CAUSAL, bool VARLEN, bool KVC>
+// KVC: 0 the dense or packed tensors; a KV cache of 1 one region per
+// sequence (no block table), 2 pages of at least 64 tokens, 3 smaller pages
+// (each layout its own instance, which folds away the paths it cannot take).
 // d=64: three workgroups per CU fit in LDS; the bound keeps every instance
-// within the registers of three waves per SIMD
+// within the registers of three waves per SIMD.
+template <int D, bool CAUSAL, bool VARLEN, int KVC>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
   // over the page's rows that hold tokens (rows past the end read as zero).
   // Smaller pages: each row's page comes from the window by a cross-lane
   // permute, and rows past the end read the last row (finite; masked).
-  const bool paged = KVC && p.kv.block_table != nullptr;
+  constexpr bool paged = KVC >= 2;
   const int shift = p.kv.page_shift;
   const int32_t* btrow = paged ? p.kv.block_table + (int64_t)b * p.kv.bt_stride : nullptr;
   const int last_page_no = paged && Lk > 0 ? (Lk - 1) >> shift : 0;
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
     if constexpr (KVC) {
       if (!paged) {
         load_rows(rkc, rvc, j0);
-      } else if (shift >= 6) {
+      } else if (KVC == 2) {
         const int pn = j0 >> shift;
         win.cover(btrow, pn, pn, last_page_no, lane);
         const int64_t page = win.uniform(pn);
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool KVC = false>
+template <int D, bool CAUSAL, bool VARLEN, int KVC = 0>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const long nblk = VARLEN ? varlen_grid(p.Hkv * p.B, p.num_m_tiles * p.group, kFwdVarlenRun * p.group)
                            : (long)p.num_m_tiles * p.Hq * p.B;
@@ -379,5 +382,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, 
 // ping-pong kernel).
 hipError_t launch_fwd_bf16_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream) {
   if (d != 64) return hipErrorInvalidValue;
-  return causal ? launch<64, true, false, true>(p, stream) : launch<64, false, false, true>(p, stream);
+  if (!p.kv.block_table) return causal ? launch<64, true, false, 1>(p, stream) : launch<64, false, false, 1>(p, stream);
+  if (p.kv.page_shift >= 6) return causal ? launch<64, true, false, 2>(p, stream) : launch<64, false, false, 2>(p, stream);
+  return causal ? launch<64, true, false, 3>(p, stream) : launch<64, false, false, 3>(p, stream);
 }

@@ -124,3 +124,68 @@ def test_mx_token_blocks_and_roundtrip():
     top = np.abs(codes[0, :32, 0, 0].astype(np.int32) & 0x7F).max()
     assert (top >> 3) >= 14
 
+
+# ---- per-tensor quantisation and the MX decoder along d ----------------------
+
+def test_quantize_tensor_pins():
+    """Per-tensor quantisation, pinned independently of the oracle's code:
+    the scale is the tensor's amax / 448 in fp32 (computed here with torch),
+    the largest magnitude encodes to 0x7E (448), every code is torch's own
+    e4m3fn cast of the fp32 quotient x / scale, and a zero tensor gets
+    scale 1 with all-zero codes."""
+    g = torch.Generator().manual_seed(11)
+    xt = torch.randn(2, 70, 3, 32, generator=g) * torch.exp(torch.randn(2, 70, 3, 32, generator=g))
+    xt[1, 5, 2, 7] = -37.5                       # a unique largest magnitude, negative
+    xt = xt.clamp(-30.0, 30.0)
+    xt[1, 5, 2, 7] = -37.5
+    codes, s = fp8.quantize_tensor(xt.numpy())
+    s_want = (xt.abs().max() / torch.tensor(448.0)).item()
+    assert np.float32(s) == np.float32(s_want)
+    assert codes[1, 5, 2, 7] == 0xFE             # -448
+    assert ((codes & 0x7F) <= 0x7E).all()
+    # only the largest element (up to ties) reaches the top code
+    assert int(((codes & 0x7F) == 0x7E).sum()) == 1
+    y = (xt / torch.tensor(np.float32(s))).to(torch.float32)
+    ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (codes == ref).all()
+    # the decoded tensor is within E4M3's rounding of x
+    xd = fp8.decode_e4m3(codes) * np.float64(s)
+    x = xt.numpy().astype(np.float64)
+    assert (np.abs(xd - x) <= np.maximum(np.abs(x) * 2.0 ** -4, float(s) * 2.0 ** -10) + 1e-12).all()
+    z_codes, z_s = fp8.quantize_tensor(np.zeros((1, 3, 2, 16), np.float32))
+    assert np.float32(z_s) == 1.0 and (z_codes == 0).all()
+
+
+def test_quantize_blocks_codes_match_torch_cast():
+    """Per-block codes are torch's e4m3fn cast of x / (its block's scale)."""
+    g = torch.Generator().manual_seed(12)
+    x = (torch.randn(1, 260, 2, 64, generator=g) * 3).numpy()
+    codes, sc = fp8.quantize_blocks(x, 128)
+    tok = np.repeat(sc, 128, axis=2)[:, :, :260].transpose(0, 2, 1)[..., None]
+    y = torch.from_numpy((x / tok.astype(np.float32)).astype(np.float32))
+    ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (codes == ref).all()
+
+
+def test_mx_d_roundtrip():
+    """dequantize_mx along d inverts quantize_mx within E4M3's rounding, with
+    each 32-element block's step taken from the shared exponent computed here
+    by exact search; a zero block decodes to zeros."""
+    x = mx_case(4, (2, 9, 3, 96))
+    x[1, 4, 2, 32:64] = 0.0
+    codes, sc = fp8.quantize_mx(x, "d")
+    xd = fp8.dequantize_mx(codes, sc, "d")
+    assert xd.shape == x.shape and xd.dtype == np.float64
+    amax = np.abs(x).reshape(2, 9, 3, 3, 32).max(axis=4).astype(np.float64)
+    e = np.vectorize(smallest_fitting_exponent)(amax)
+    step = np.exp2(np.repeat(e, 32, axis=3).astype(np.float64))
+    err = np.abs(xd - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, step * 2.0 ** -10)
+    assert (err <= bound + 1e-300).all()
+    assert (xd[1, 4, 2, 32:64] == 0.0).all()
+    # decoding with a scale byte one higher doubles every value of that block
+    sc2 = sc.copy()
+    sc2[0, 0, 0, 1] += 1
+    xd2 = fp8.dequantize_mx(codes, sc2, "d")
+    assert np.array_equal(xd2[0, 0, 0, 32:64], 2.0 * xd[0, 0, 0, 32:64])
+    assert np.array_equal(xd2[0, 0, 0, :32], xd[0, 0, 0, :32])

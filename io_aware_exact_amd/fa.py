@@ -195,7 +195,7 @@ def _stream():
 
 def _t4(x):
     """fa_tensor of a [B,S,H,d] tensor (d contiguous)."""
-    assert x.dim() == 4 and x.stride(3) == 1, "last dimension must be contiguous"
+    _need(x.dim() == 4 and x.stride(3) == 1, "a [B,S,H,d] tensor with d contiguous is required")
     return FaTensor(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
 
 
@@ -203,8 +203,79 @@ def _scale(d, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+# ---- argument checks ---------------------------------------------------------
+# The C ABI takes one dtype and raw element strides for every tensor of a call,
+# so a tensor of the wrong dtype, shape or device would be read or written out
+# of bounds on the GPU.  The wrappers check every tensor against q before any
+# library call and raise ValueError.
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_device(dev, **ts):
+    """Every named tensor (None allowed) is a GPU tensor on device `dev`."""
+    for name, t in ts.items():
+        if t is None:
+            continue
+        _need(t.device.type == "cuda" and t.device == dev,
+              f"{name} must be a GPU tensor on {dev} (got {t.device})")
+
+
+def _shape(name, t, shape, dtype=None):
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _lse(name, t, shape):
+    _shape(name, t, shape, torch.float32)
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _workspace(ws):
+    if ws is not None:
+        _need(ws.dtype == torch.uint8 and ws.is_contiguous(), "workspace must be a contiguous uint8 tensor")
+
+
+def _check_dense(q, k, v, dtypes):
+    """q [B,Sq,Hq,d], k and v [B,Sk,Hkv,d] of one dtype in `dtypes`."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t.dim() == 4, f"{name} must be [B,S,H,d]")
+    _need(q.dtype in dtypes, f"q dtype {q.dtype} is not supported here")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share one dtype")
+    _need(tuple(k.shape) == tuple(v.shape), "k and v must have the same shape")
+    _need(k.shape[0] == q.shape[0] and k.shape[3] == q.shape[3],
+          "k and v must have q's batch size and head dimension")
+
+
+def _check_packed(q, k, v, dtypes):
+    """q [Tq,Hq,d], k and v [Tk,Hkv,d] of one dtype in `dtypes`."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t.dim() == 3, f"{name} must be [T,H,d]")
+    _need(q.dtype in dtypes, f"q dtype {q.dtype} is not supported here")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share one dtype")
+    _need(tuple(k.shape) == tuple(v.shape), "k and v must have the same shape")
+    _need(k.shape[2] == q.shape[2], "k and v must have q's head dimension")
+
+
+def _check_cu(cu_q, cu_k, dev):
+    for name, t in (("cu_seqlens_q", cu_q), ("cu_seqlens_k", cu_k)):
+        _need(t.dtype == torch.int32 and t.dim() == 1 and t.is_contiguous(),
+              f"{name} must be a contiguous int32 vector")
+    _need(cu_q.numel() == cu_k.numel() and cu_q.numel() >= 1,
+          "cu_seqlens_q and cu_seqlens_k must both have nseq + 1 entries")
+    _on_device(dev, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+
+
 def fwd_args(q, k, v, out, lse, causal, scale, workspace=None):
+    _check_dense(q, k, v, (torch.bfloat16, torch.float32))
     B, Sq, Hq, d = q.shape
+    _shape("out", out, q.shape, torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
+    _lse("lse", lse, (B, Hq, Sq))
+    _workspace(workspace)
+    _on_device(q.device, q=q, k=k, v=v, out=out, lse=lse, workspace=workspace)
     Sk, Hkv = k.shape[1], k.shape[2]
     dt = _DTYPES.get(q.dtype, -1)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -216,6 +287,7 @@ def fwd_args(q, k, v, out, lse, causal, scale, workspace=None):
 
 def fwd_workspace_bytes(q, k, v, causal=False, scale=None):
     """Bytes of workspace the split-KV decode path wants (0: not applicable)."""
+    _check_dense(q, k, v, (torch.bfloat16, torch.float32))
     B, Sq, Hq, d = q.shape
     dummy = torch.empty(0)
     a = FwdArgs(FA_BF16, B, Sq, k.shape[1], Hq, k.shape[2], d, int(bool(causal)),
@@ -230,6 +302,7 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None):
     fp32).  With a `workspace`
     (uint8 device tensor of fwd_workspace_bytes) decode-shaped calls take the
     split-KV path."""
+    _check_dense(q, k, v, (torch.bfloat16, torch.float32))
     B, Sq, Hq, d = q.shape
     if out is None:
         odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
@@ -253,16 +326,21 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                causal=False, scale=None, out=None, lse=None):
     """Packed forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16; cu_seqlens_* int32
     [nseq+1] on the GPU.  Returns (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32)."""
+    _check_packed(q, k, v, (torch.bfloat16,))
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
     for x in (q, k, v):
-        assert x.stride(2) == 1
-    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32
+        _need(x.stride(2) == 1, "the last dimension must be contiguous")
     nseq = cu_seqlens_q.numel() - 1
     if out is None:
         out = torch.empty((Tq, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    _shape("out", out, q.shape, torch.bfloat16)
+    _need(out.stride(2) == 1, "out: the last dimension must be contiguous")
+    _lse("lse", lse, (Hq, Tq))
+    _check_cu(cu_seqlens_q, cu_seqlens_k, q.device)
+    _on_device(q.device, q=q, k=k, v=v, out=out, lse=lse)
     dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
     a = FwdVarlenArgs(dt, nseq, Hq, Hkv, d, int(max_seqlen_q), int(max_seqlen_k), Tq, Tk,
                       int(bool(causal)), _scale(d, scale),
@@ -279,16 +357,34 @@ def kvcache_args(q, k_cache, v_cache, cache_seqlens, block_table, k_new, v_new, 
     """fa_fwd_kvcache_args.  Caches [pages, page_size, Hkv, d] (without a
     block table: [B, capacity, Hkv, d]); block_table int32 [B, max_pages] or
     None; cache_seqlens int32 [B]; k_new/v_new [B, Snew, Hkv, d] or None."""
+    _need(q.dim() == 4 and q.dtype == torch.bfloat16, "q must be a bf16 [B,Sq,Hq,d] tensor")
     B, Sq, Hq, d = q.shape
+    for name, x in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(x.dim() == 4 and x.stride(3) == 1 and x.dtype == torch.bfloat16,
+              f"{name} must be a bf16 [pages, page_size, Hkv, d] tensor, d contiguous")
+    _need(tuple(k_cache.shape) == tuple(v_cache.shape) and k_cache.shape[3] == d,
+          "k_cache and v_cache must have the same shape and q's head dimension")
     npages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
-    for x in (k_cache, v_cache):
-        assert x.dim() == 4 and x.stride(3) == 1
-    assert cache_seqlens.dtype == torch.int32
+    _need(cache_seqlens.dtype == torch.int32 and tuple(cache_seqlens.shape) == (B,)
+          and cache_seqlens.is_contiguous(), "cache_seqlens must be a contiguous int32 [B] tensor")
+    _need((k_new is None) == (v_new is None), "k_new and v_new go together")
+    if k_new is not None:
+        _shape("k_new", k_new, (B, k_new.shape[1], Hkv, d), torch.bfloat16)
+        _shape("v_new", v_new, k_new.shape, torch.bfloat16)
+    if block_table is not None:
+        _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_pages]")
+    _shape("out", out, q.shape, torch.bfloat16)
+    _lse("lse", lse, (B, Hq, Sq))
+    _workspace(workspace)
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, cache_seqlens=cache_seqlens,
+               block_table=block_table, k_new=k_new, v_new=v_new, out=out, lse=lse,
+               workspace=workspace)
     snew = 0 if k_new is None else k_new.shape[1]
     dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
     none4 = FaTensor(None, 0, 0, 0)
     if block_table is not None:
-        assert block_table.dtype == torch.int32 and block_table.stride(1) == 1
+        _need(block_table.dtype == torch.int32 and block_table.stride(1) == 1,
+              "block_table must be int32 with contiguous rows")
         bt_ptr, bt_stride, maxp = block_table.data_ptr(), block_table.stride(0), block_table.shape[1]
     else:
         bt_ptr, bt_stride, maxp = None, 0, 0
@@ -330,8 +426,15 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=None
 
 
 def bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace=None, stages=0):
+    _check_dense(q, k, v, (torch.bfloat16,))
     B, Sq, Hq, d = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
+    for name, t, like in (("o", o, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _shape(name, t, like.shape, torch.bfloat16)
+    _lse("lse", lse, (B, Hq, Sq))
+    _workspace(workspace)
+    _on_device(q.device, q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv,
+               workspace=workspace)
     dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -360,11 +463,18 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, out=None, workspace=Non
 
 def bwd_varlen_args(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
                     max_seqlen_q, max_seqlen_k, causal, scale, workspace=None):
+    _check_packed(q, k, v, (torch.bfloat16,))
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
+    for name, t, like in (("o", o, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _shape(name, t, like.shape, torch.bfloat16)
     for x in (q, k, v, o, dout, dq, dk, dv):
-        assert x.dim() == 3 and x.stride(2) == 1, "packed [T,H,d] with d contiguous"
-    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32
+        _need(x.stride(2) == 1, "packed [T,H,d] tensors need a contiguous last dimension")
+    _lse("lse", lse, (Hq, Tq))
+    _check_cu(cu_seqlens_q, cu_seqlens_k, q.device)
+    _workspace(workspace)
+    _on_device(q.device, q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv,
+               workspace=workspace)
     dt = FA_BF16 if q.dtype == torch.bfloat16 else -1
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -423,7 +533,9 @@ def quantize_fp8(x, per_tensor=False):
     """x [B,S,H,d] fp32 on the GPU (d contiguous) -> (codes uint8 [B,S,H,d]
     OCP E4M3, scales fp32 [B,H,ceil(S/128)]).  Per-block: one scale per
     (batch, head, 128 tokens); per-tensor: one scale written to every entry."""
-    assert x.dtype == torch.float32 and x.dim() == 4 and x.stride(3) == 1
+    _need(x.dtype == torch.float32 and x.dim() == 4 and x.stride(3) == 1,
+          "x must be fp32 [B,S,H,d] with d contiguous")
+    _on_device(x.device, x=x)
     B, S, H, d = x.shape
     codes = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
     scales = torch.empty((B, H, (S + 127) // 128), dtype=torch.float32, device=x.device)
@@ -433,20 +545,33 @@ def quantize_fp8(x, per_tensor=False):
     return codes, scales
 
 
+def _check_fp8_codes(q8, k8, v8):
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _need(t.dim() == 4 and t.dtype in (torch.uint8, torch.float8_e4m3fn),
+              f"{name} must be E4M3 codes (uint8 or float8_e4m3fn) [B,S,H,d]")
+    _need(tuple(k8.shape) == tuple(v8.shape), "k8 and v8 must have the same shape")
+    _need(k8.shape[0] == q8.shape[0] and k8.shape[3] == q8.shape[3],
+          "k8 and v8 must have q8's batch size and head dimension")
+
+
 def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=None,
             out=None, lse=None):
     """FP8 forward: q8 [B,Sq,Hq,d], k8/v8 [B,Sk,Hkv,d] E4M3 codes (uint8 or
     float8_e4m3fn) with fp32 scales [B,H,ceil(S/128)].  Returns (o bf16, lse)."""
+    _check_fp8_codes(q8, k8, v8)
     B, Sq, Hq, d = q8.shape
     Sk, Hkv = k8.shape[1], k8.shape[2]
-    for t in (q8, k8, v8):
-        assert t.element_size() == 1
-    for t in (q_descale, k_descale, v_descale):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+    _lse("q_descale", q_descale, (B, Hq, (Sq + 127) // 128))
+    _lse("k_descale", k_descale, (B, Hkv, (Sk + 127) // 128))
+    _lse("v_descale", v_descale, (B, Hkv, (Sk + 127) // 128))
     if out is None:
         out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    _shape("out", out, q8.shape, torch.bfloat16)
+    _lse("lse", lse, (B, Hq, Sq))
+    _on_device(q8.device, q8=q8, k8=k8, v8=v8, q_descale=q_descale, k_descale=k_descale,
+               v_descale=v_descale, out=out, lse=lse)
     a = FwdArgs(FA_FP8_E4M3, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
                 _t4(q8), _t4(k8), _t4(v8), _t4(out), lse.data_ptr(), q_descale.data_ptr(),
                 k_descale.data_ptr(), v_descale.data_ptr(), None, 0)
@@ -459,12 +584,16 @@ def merge(o_parts, lse_parts, out=None, lse=None):
     [P,B,S,H,d] (bf16 or fp32) and lse_parts [P,B,H,S] fp32, contiguous ->
     (o [B,S,H,d] bf16, lse [B,H,S] fp32)."""
     P, B, S, H, d = o_parts.shape
-    assert o_parts.is_contiguous() and lse_parts.is_contiguous()
-    assert lse_parts.shape == (P, B, H, S) and lse_parts.dtype == torch.float32
+    _need(o_parts.is_contiguous() and lse_parts.is_contiguous(), "the parts must be contiguous")
+    _need(o_parts.dtype in (torch.bfloat16, torch.float32), "o_parts must be bf16 or fp32")
+    _lse("lse_parts", lse_parts, (P, B, H, S))
     if out is None:
         out = torch.empty((B, S, H, d), dtype=torch.bfloat16, device=o_parts.device)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    _shape("out", out, (B, S, H, d), torch.bfloat16)
+    _lse("lse", lse, (B, H, S))
+    _on_device(o_parts.device, o_parts=o_parts, lse_parts=lse_parts, out=out, lse=lse)
     dt = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}.get(o_parts.dtype, -1)
     a = MergeArgs(dt, P, B, S, H, d, o_parts.data_ptr(), lse_parts.data_ptr(), _t4(out),
                   lse.data_ptr())
@@ -477,7 +606,9 @@ def quantize_mxfp8(x, axis):
     uint8 [B,S,H,d] OCP E4M3 and E8M0 scale bytes, one per 32 elements --
     axis 0 (q, k): along d, scales [B,S,H,d/32]; axis 1 (v): along the
     tokens, scales [B,H,ceil(S/32),d]."""
-    assert x.dtype == torch.float32 and x.dim() == 4 and x.stride(3) == 1
+    _need(x.dtype == torch.float32 and x.dim() == 4 and x.stride(3) == 1,
+          "x must be fp32 [B,S,H,d] with d contiguous")
+    _on_device(x.device, x=x)
     B, S, H, d = x.shape
     codes = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
     shape = (B, S, H, d // 32) if axis == 0 else (B, H, (S + 31) // 32, d)
@@ -493,16 +624,22 @@ def fwd_mxfp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None, o
     """MX FP8 forward: E4M3 codes q8 [B,Sq,Hq,d], k8/v8 [B,Sk,Hkv,d] with the
     E8M0 scale bytes of quantize_mxfp8 (q, k: axis 0; v: axis 1).  Returns
     (o bf16, lse)."""
+    _check_fp8_codes(q8, k8, v8)
     B, Sq, Hq, d = q8.shape
     Sk, Hkv = k8.shape[1], k8.shape[2]
-    for t in (q8, k8, v8):
-        assert t.element_size() == 1
-    for t in (q_scale, k_scale, v_scale):
-        assert t.dtype == torch.uint8 and t.is_contiguous()
+    for name, t, shape in (("q_scale", q_scale, (B, Sq, Hq, d // 32)),
+                           ("k_scale", k_scale, (B, Sk, Hkv, d // 32)),
+                           ("v_scale", v_scale, (B, Hkv, (Sk + 31) // 32, d))):
+        _shape(name, t, shape, torch.uint8)
+        _need(t.is_contiguous(), f"{name} must be contiguous")
     if out is None:
         out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    _shape("out", out, q8.shape, torch.bfloat16)
+    _lse("lse", lse, (B, Hq, Sq))
+    _on_device(q8.device, q8=q8, k8=k8, v8=v8, q_scale=q_scale, k_scale=k_scale,
+               v_scale=v_scale, out=out, lse=lse)
     a = FwdMxfp8Args(B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
                      _t4(q8), _t4(k8), _t4(v8), _t4(out), lse.data_ptr(), q_scale.data_ptr(),
                      k_scale.data_ptr(), v_scale.data_ptr())

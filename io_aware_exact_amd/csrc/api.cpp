@@ -15,21 +15,56 @@ constexpr int kBM = 128;   // query rows per forward workgroup
 // multiple of 8, tiles (per query head of a kv group) to whole runs of at
 // most 8.  Holds for every kernel's run length.
 static int64_t varlen_grid_bound(int64_t rows, int64_t tiles, int64_t group) {
-  return (rows + 7) / 8 * 8 * (tiles + 8) * group;
+  int64_t r;
+  if (rows < 0 || tiles < 0 || group < 0 ||
+      __builtin_mul_overflow((rows + 7) / 8 * 8, (tiles + 8), &r) || __builtin_mul_overflow(r, group, &r))
+    return INT64_MAX;
+  return r;
 }
+
+// Products of sizes saturate instead of overflowing: a caller may pass any
+// int32 size or int64 stride, and a saturated product fails every range check.
+int64_t mul_sat(int64_t a, int64_t b) {
+  int64_t r;
+  if (a <= 0 || b <= 0) return a == 0 || b == 0 ? 0 : -1;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+int64_t mul_sat(int64_t a, int64_t b, int64_t c) { return mul_sat(mul_sat(a, b), c); }
+int64_t mul_sat(int64_t a, int64_t b, int64_t c, int64_t d) { return mul_sat(mul_sat(a, b, c), d); }
+
+// No device allocation is this large; extents beyond it are rejected as
+// FA_ERR_SHAPE before any overlap test.
+constexpr int64_t kMaxExtentBytes = int64_t(1) << 56;
 
 struct Span {
   uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+  bool bad;          // the extent overflows or exceeds kMaxExtentBytes
 };
+
+Span empty_span(const void* p) { return {(uintptr_t)p, (uintptr_t)p, false}; }
+
+// n elements of esize bytes from p.
+Span lin(const void* p, int64_t n, int64_t esize) {
+  if (n <= 0) return empty_span(p);
+  const int64_t bytes = mul_sat(n, esize);
+  if (bytes > kMaxExtentBytes) return {(uintptr_t)p, (uintptr_t)p, true};
+  return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, false};
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Byte span of a [B,S,H,d] tensor with non-negative element strides.
 Span span4(const void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb, int64_t ss,
            int64_t sh, int64_t esize) {
-  if (B <= 0 || S <= 0 || H <= 0 || d <= 0) return {(uintptr_t)ptr, (uintptr_t)ptr};
-  const int64_t last = (B - 1) * sb + (S - 1) * ss + (H - 1) * sh + (d - 1);
-  return {(uintptr_t)ptr, (uintptr_t)ptr + (uintptr_t)((last + 1) * esize)};
+  if (B <= 0 || S <= 0 || H <= 0 || d <= 0) return empty_span(ptr);
+  if (sb < 0 || ss < 0 || sh < 0) return {(uintptr_t)ptr, (uintptr_t)ptr, true};
+  int64_t last = d - 1, t;
+  bool of = false;
+  of |= __builtin_mul_overflow(B - 1, sb, &t) || __builtin_add_overflow(last, t, &last);
+  of |= __builtin_mul_overflow(S - 1, ss, &t) || __builtin_add_overflow(last, t, &last);
+  of |= __builtin_mul_overflow(H - 1, sh, &t) || __builtin_add_overflow(last, t, &last);
+  if (of) return {(uintptr_t)ptr, (uintptr_t)ptr, true};
+  return lin(ptr, last + 1, esize);
 }
 
 bool overlap(Span a, Span b) {
@@ -37,10 +72,20 @@ bool overlap(Span a, Span b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Kernels address one (batch, head) slice with 32-bit byte offsets, padded
-// by one tile of rows.
+template <size_t N>
+bool any_bad(const Span (&s)[N]) {
+  for (const Span& x : s)
+    if (x.bad) return true;
+  return false;
+}
+
+// Kernels address one (batch, head) slice with 32-bit byte offsets.  Rows
+// past the end of the last tile are addressed too (and read as zero through
+// the buffer bounds check), so the offsets must stay below 2^32 up to the end
+// of the largest tile any kernel uses: 256 query rows (the two-group forward).
+constexpr int64_t kMaxTileRows = 256;
 bool fits32(int64_t rows, int64_t row_stride_elems, int64_t esize) {
-  return (rows + 128) * row_stride_elems * esize < (int64_t)0xffffffffLL;
+  return mul_sat(rows + kMaxTileRows, row_stride_elems, esize) < (int64_t)0xffffffffLL;
 }
 
 bool strides_ok(const fa_tensor& t, int64_t mult) {
@@ -126,21 +171,25 @@ fa_status check_fwd(const fa_fwd_args* a) {
       !strides_ok(a->o, 16 / oes))
     return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
-  if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (mul_sat(tiles, a->Hq, a->B) > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!fits32(a->Sq, a->q.stride_s, es) || !fits32(a->Sq, a->o.stride_s, oes) ||
       !fits32(a->Sk, a->k.stride_s, es) || !fits32(a->Sk, a->v.stride_s, es))
     return FA_ERR_SHAPE;
   const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, oes);
-  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
+  const Span sl = lin(a->lse, mul_sat(a->B, a->Hq, a->Sq), 4);
   const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, es);
   const Span sk = span4(a->k.ptr, a->B, a->Sk, a->Hkv, a->d, a->k.stride_b, a->k.stride_s, a->k.stride_h, es);
   const Span sv = span4(a->v.ptr, a->B, a->Sk, a->Hkv, a->d, a->v.stride_b, a->v.stride_s, a->v.stride_h, es);
+  const Span all[5] = {so, sl, sq, sk, sv};
+  if (any_bad(all)) return FA_ERR_SHAPE;
   if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sl) || overlap(sl, sq) ||
       overlap(sl, sk) || overlap(sl, sv))
     return FA_ERR_ALIAS;
   if (a->workspace && a->workspace_bytes > 0) {
     if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
-    const Span sw = {(uintptr_t)a->workspace, (uintptr_t)a->workspace + a->workspace_bytes};
+    const Span sw = lin(a->workspace, a->workspace_bytes > (size_t)kMaxExtentBytes
+                                          ? INT64_MAX : (int64_t)a->workspace_bytes, 1);
+    if (sw.bad) return FA_ERR_WORKSPACE;
     if (overlap(sw, sq) || overlap(sw, sk) || overlap(sw, sv) || overlap(sw, so) || overlap(sw, sl))
       return FA_ERR_ALIAS;
   }
@@ -168,15 +217,17 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
   for (int i = 0; i < 8; ++i)
     if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->max_seqlen_q + kBM - 1) / kBM;
-  if (varlen_grid_bound((int64_t)a->Hkv * a->nseq, tiles, a->Hq / a->Hkv) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (varlen_grid_bound(mul_sat(a->Hkv, a->nseq), tiles, a->Hq / a->Hkv) > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!fits32(a->max_seqlen_q, a->q_stride_t, 2) || !fits32(a->max_seqlen_q, a->o_stride_t, 2) ||
       !fits32(a->max_seqlen_k, a->k_stride_t, 2) || !fits32(a->max_seqlen_k, a->v_stride_t, 2))
     return FA_ERR_SHAPE;
   const Span so = span4(a->o, 1, a->total_q, a->Hq, a->d, 0, a->o_stride_t, a->o_stride_h, 2);
-  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->Hq * a->total_q * 4};
+  const Span sl = lin(a->lse, mul_sat(a->Hq, a->total_q), 4);
   const Span sq = span4(a->q, 1, a->total_q, a->Hq, a->d, 0, a->q_stride_t, a->q_stride_h, 2);
   const Span sk = span4(a->k, 1, a->total_k, a->Hkv, a->d, 0, a->k_stride_t, a->k_stride_h, 2);
   const Span sv = span4(a->v, 1, a->total_k, a->Hkv, a->d, 0, a->v_stride_t, a->v_stride_h, 2);
+  const Span all[5] = {so, sl, sq, sk, sv};
+  if (any_bad(all)) return FA_ERR_SHAPE;
   if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sl) || overlap(sl, sq) ||
       overlap(sl, sk) || overlap(sl, sv))
     return FA_ERR_ALIAS;
@@ -184,9 +235,9 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
 }
 
 size_t bwd_delta_bytes(const fa_bwd_args* a) {
-  const size_t n = (size_t)(a->B > 0 ? a->B : 0) * (size_t)(a->Hq > 0 ? a->Hq : 0) *
-                   (size_t)(a->Sq > 0 ? a->Sq : 0) * 4;
-  return (n + 255) & ~(size_t)255;
+  // saturates for impossible sizes, which the argument check rejects
+  const int64_t n = mul_sat(a->B > 0 ? a->B : 0, a->Hq > 0 ? a->Hq : 0, a->Sq > 0 ? a->Sq : 0, 4);
+  return n > kMaxExtentBytes ? (size_t)kMaxExtentBytes : align256((size_t)n);
 }
 
 fa_status check_bwd(const fa_bwd_args* a) {
@@ -208,9 +259,9 @@ fa_status check_bwd(const fa_bwd_args* a) {
     if (!aligned16(ts[i]->ptr) || !strides_ok(*ts[i], 8)) return FA_ERR_ALIGN;
   if ((uintptr_t)a->lse & 3u) return FA_ERR_ALIGN;
   const int64_t B = a->B, Sq = a->Sq, Sk = a->Sk, Hq = a->Hq, Hkv = a->Hkv, d = a->d;
-  if (((Sq + 127) / 128) * Hq * B > 0x7fffffffLL || ((Sk + 127) / 128) * Hkv * B > 0x7fffffffLL)
+  if (mul_sat((Sq + 127) / 128, Hq, B) > 0x7fffffffLL || mul_sat((Sk + 127) / 128, Hkv, B) > 0x7fffffffLL)
     return FA_ERR_SHAPE;
-  if (B * Sq * Hq > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
+  if (mul_sat(B, Sq, Hq) > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
   if (!fits32(Sq, a->q.stride_s, 2) || !fits32(Sq, a->dout.stride_s, 2) ||
       !fits32(Sk, a->k.stride_s, 2) || !fits32(Sk, a->v.stride_s, 2))
     return FA_ERR_SHAPE;
@@ -224,12 +275,13 @@ fa_status check_bwd(const fa_bwd_args* a) {
       span4(a->v.ptr, B, Sk, Hkv, d, a->v.stride_b, a->v.stride_s, a->v.stride_h, 2),
       span4(a->o.ptr, B, Sq, Hq, d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2),
       span4(a->dout.ptr, B, Sq, Hq, d, a->dout.stride_b, a->dout.stride_s, a->dout.stride_h, 2),
-      {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)(B * Hq * Sq * 4)}};
+      lin(a->lse, mul_sat(B, Hq, Sq), 4)};
   const Span out[4] = {
       span4(a->dq.ptr, B, Sq, Hq, d, a->dq.stride_b, a->dq.stride_s, a->dq.stride_h, 2),
       span4(a->dk.ptr, B, Sk, Hkv, d, a->dk.stride_b, a->dk.stride_s, a->dk.stride_h, 2),
       span4(a->dv.ptr, B, Sk, Hkv, d, a->dv.stride_b, a->dv.stride_s, a->dv.stride_h, 2),
-      {(uintptr_t)a->workspace, (uintptr_t)a->workspace + need}};
+      lin(a->workspace, (int64_t)need, 1)};
+  if (any_bad(in) || any_bad(out)) return FA_ERR_SHAPE;
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlap(out[i], in[j])) return FA_ERR_ALIAS;
@@ -240,8 +292,8 @@ fa_status check_bwd(const fa_bwd_args* a) {
 }
 
 size_t bwd_varlen_delta_bytes(const fa_bwd_varlen_args* a) {
-  const size_t n = (size_t)(a->Hq > 0 ? a->Hq : 0) * (size_t)(a->total_q > 0 ? a->total_q : 0) * 4;
-  return align256(n);
+  const int64_t n = mul_sat(a->Hq > 0 ? a->Hq : 0, a->total_q > 0 ? a->total_q : 0, 4);
+  return n > kMaxExtentBytes ? (size_t)kMaxExtentBytes : align256((size_t)n);
 }
 
 fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
@@ -269,10 +321,10 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
   for (int i = 0; i < 16; ++i)
     if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_ALIGN;
   const int64_t qtiles = ((int64_t)a->max_seqlen_q + 127) / 128, ktiles = ((int64_t)a->max_seqlen_k + 127) / 128;
-  if (varlen_grid_bound((int64_t)a->Hkv * a->nseq, qtiles, a->Hq / a->Hkv) > 0x7fffffffLL ||
-      varlen_grid_bound((int64_t)a->Hkv * a->nseq, ktiles, 1) > 0x7fffffffLL)
+  if (varlen_grid_bound(mul_sat(a->Hkv, a->nseq), qtiles, a->Hq / a->Hkv) > 0x7fffffffLL ||
+      varlen_grid_bound(mul_sat(a->Hkv, a->nseq), ktiles, 1) > 0x7fffffffLL)
     return FA_ERR_SHAPE;
-  if ((int64_t)a->total_q * a->Hq > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
+  if (mul_sat(a->total_q, a->Hq) > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
   if (!fits32(a->max_seqlen_q, a->q_stride_t, 2) || !fits32(a->max_seqlen_q, a->do_stride_t, 2) ||
       !fits32(a->max_seqlen_k, a->k_stride_t, 2) || !fits32(a->max_seqlen_k, a->v_stride_t, 2))
     return FA_ERR_SHAPE;
@@ -287,14 +339,15 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
       span4(a->v, 1, Tk, Hkv, d, 0, a->v_stride_t, a->v_stride_h, 2),
       span4(a->o, 1, Tq, Hq, d, 0, a->o_stride_t, a->o_stride_h, 2),
       span4(a->dout, 1, Tq, Hq, d, 0, a->do_stride_t, a->do_stride_h, 2),
-      {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)(Hq * Tq * 4)},
-      {(uintptr_t)a->cu_seqlens_q, (uintptr_t)a->cu_seqlens_q + (uintptr_t)(a->nseq + 1) * 4},
-      {(uintptr_t)a->cu_seqlens_k, (uintptr_t)a->cu_seqlens_k + (uintptr_t)(a->nseq + 1) * 4}};
+      lin(a->lse, mul_sat(Hq, Tq), 4),
+      lin(a->cu_seqlens_q, (int64_t)a->nseq + 1, 4),
+      lin(a->cu_seqlens_k, (int64_t)a->nseq + 1, 4)};
   const Span out[4] = {
       span4(a->dq, 1, Tq, Hq, d, 0, a->dq_stride_t, a->dq_stride_h, 2),
       span4(a->dk, 1, Tk, Hkv, d, 0, a->dk_stride_t, a->dk_stride_h, 2),
       span4(a->dv, 1, Tk, Hkv, d, 0, a->dv_stride_t, a->dv_stride_h, 2),
-      {(uintptr_t)a->workspace, (uintptr_t)a->workspace + need}};
+      lin(a->workspace, (int64_t)need, 1)};
+  if (any_bad(in) || any_bad(out)) return FA_ERR_SHAPE;
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 8; ++j)
       if (overlap(out[i], in[j])) return FA_ERR_ALIAS;
@@ -366,14 +419,14 @@ fa_status check_kvcache(const fa_fwd_kvcache_args* a) {
       !strides8(a->v_stride_page, a->v_stride_s, a->v_stride_h))
     return FA_ERR_ALIGN;
   const int64_t tiles = ((int64_t)a->Sq + kBM - 1) / kBM;
-  if (tiles * a->Hq * (int64_t)a->B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (mul_sat(tiles, a->Hq, a->B) > 0x7fffffffLL) return FA_ERR_SHAPE;
   // q and o slices, and one page (or a dense cache's rows), are addressed
   // with 32-bit byte offsets
   if (!fits32(a->Sq, a->q.stride_s, 2) || !fits32(a->Sq, a->o.stride_s, 2) ||
       !fits32(a->page_size, a->k_stride_s, 2) || !fits32(a->page_size, a->v_stride_s, 2))
     return FA_ERR_SHAPE;
   const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
-  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
+  const Span sl = lin(a->lse, mul_sat(a->B, a->Hq, a->Sq), 4);
   const Span sq = span4(a->q.ptr, a->B, a->Sq, a->Hq, a->d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2);
   const Span skn = span4(a->k_new.ptr, a->B, a->Snew, a->Hkv, a->d, a->k_new.stride_b, a->k_new.stride_s,
                          a->k_new.stride_h, 2);
@@ -383,14 +436,20 @@ fa_status check_kvcache(const fa_fwd_kvcache_args* a) {
                          a->k_stride_h, 2);
   const Span svc = span4(a->v_cache, a->num_pages, a->page_size, a->Hkv, a->d, a->v_stride_page, a->v_stride_s,
                          a->v_stride_h, 2);
-  const Span sbt = paged ? Span{(uintptr_t)a->block_table,
-                                (uintptr_t)(a->block_table + ((int64_t)a->B - 1) * a->block_table_stride +
-                                            a->max_pages_per_seq)}
-                         : Span{0, 0};
-  const Span ssl = {(uintptr_t)a->cache_seqlens, (uintptr_t)(a->cache_seqlens + a->B)};
+  int64_t bt_n = INT64_MAX;
+  if (paged) {
+    int64_t t;
+    if (!__builtin_mul_overflow((int64_t)a->B - 1, a->block_table_stride, &t) &&
+        !__builtin_add_overflow(t, (int64_t)a->max_pages_per_seq, &t))
+      bt_n = t;
+  }
+  const Span sbt = paged ? lin(a->block_table, bt_n, 4) : empty_span(nullptr);
+  const Span ssl = lin(a->cache_seqlens, a->B, 4);
+  const Span all[9] = {so, sl, sq, skn, svn, skc, svc, sbt, ssl};
+  if (any_bad(all)) return FA_ERR_SHAPE;
   // outputs: o, lse, and (when appending) the caches
   const Span outs[2] = {so, sl};
-  const Span ins[8] = {sq, skn, svn, skc, svc, sbt, ssl, Span{0, 0}};
+  const Span ins[7] = {sq, skn, svn, skc, svc, sbt, ssl};
   for (const Span& o : outs)
     for (const Span& i : ins)
       if (overlap(o, i)) return FA_ERR_ALIAS;
@@ -402,8 +461,9 @@ fa_status check_kvcache(const fa_fwd_kvcache_args* a) {
   }
   if (a->workspace && a->workspace_bytes > 0) {
     if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
-    const Span sw = {(uintptr_t)a->workspace, (uintptr_t)a->workspace + a->workspace_bytes};
-    const Span all[9] = {so, sl, sq, skn, svn, skc, svc, sbt, ssl};
+    const Span sw = lin(a->workspace, a->workspace_bytes > (size_t)kMaxExtentBytes
+                                          ? INT64_MAX : (int64_t)a->workspace_bytes, 1);
+    if (sw.bad) return FA_ERR_WORKSPACE;
     for (const Span& x : all)
       if (overlap(sw, x)) return FA_ERR_ALIAS;
   }
@@ -621,8 +681,11 @@ fa_status fa_quantize_fp8(const float* x, int64_t sb, int64_t ss, int64_t sh, in
   if (B == 0 || S == 0) return FA_OK;
   const int64_t nb = ((int64_t)S + 127) / 128;
   const Span sx = span4(x, B, S, H, d, sb, ss, sh, 4);
-  const Span sc = {(uintptr_t)codes, (uintptr_t)codes + (uintptr_t)((int64_t)B * S * H * d)};
-  const Span ss_ = {(uintptr_t)scales, (uintptr_t)scales + (uintptr_t)((int64_t)B * H * nb * 4)};
+  const Span sc = lin(codes, mul_sat(B, S, H, d), 1);
+  const Span ss_ = lin(scales, mul_sat(B, H, nb), 4);
+  const Span all[3] = {sx, sc, ss_};
+  if (any_bad(all) || mul_sat(B, H, nb) > 0x7fffffffLL || mul_sat(B, S, H, d / 16) > 0x7fffffffLL * 256)
+    return FA_ERR_SHAPE;
   if (overlap(sx, sc) || overlap(sx, ss_) || overlap(sc, ss_)) return FA_ERR_ALIAS;
   return hip_status(launch_quantize_fp8(x, sb, ss, sh, B, S, H, d, per_tensor != 0, codes, scales, stream));
 }
@@ -632,7 +695,7 @@ fa_status fa_merge(const fa_merge_args* a, hipStream_t stream) {
   if (a->dtype != FA_BF16 && a->dtype != FA_FP32) return FA_ERR_DTYPE;
   if (a->nparts < 1 || a->B < 0 || a->S < 0 || a->H < 1) return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
-  const int64_t rows = (int64_t)a->B * a->S * a->H;
+  const int64_t rows = mul_sat(a->B, a->S, a->H);
   if (rows == 0) return FA_OK;
   if (!a->o_parts || !a->lse_parts || !a->o.ptr || !a->lse) return FA_ERR_NULL;
   const int64_t es = a->dtype == FA_FP32 ? 4 : 2;
@@ -640,11 +703,13 @@ fa_status fa_merge(const fa_merge_args* a, hipStream_t stream) {
       ((uintptr_t)a->lse & 3u) || ((uintptr_t)a->o.ptr & 1u))
     return FA_ERR_ALIGN;
   if (a->o.stride_b < 0 || a->o.stride_s < 0 || a->o.stride_h < 0) return FA_ERR_SHAPE;
-  if ((rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_SHAPE;
-  const Span sop = {(uintptr_t)a->o_parts, (uintptr_t)a->o_parts + (uintptr_t)(a->nparts * rows * a->d * es)};
-  const Span slp = {(uintptr_t)a->lse_parts, (uintptr_t)(a->lse_parts + a->nparts * rows)};
+  if (rows > 0x7fffffffLL * 4) return FA_ERR_SHAPE;
+  const Span sop = lin(a->o_parts, mul_sat(a->nparts, rows, a->d), es);
+  const Span slp = lin(a->lse_parts, mul_sat(a->nparts, rows), 4);
   const Span so = span4(a->o.ptr, a->B, a->S, a->H, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
-  const Span sl = {(uintptr_t)a->lse, (uintptr_t)(a->lse + rows)};
+  const Span sl = lin(a->lse, rows, 4);
+  const Span all[4] = {sop, slp, so, sl};
+  if (any_bad(all)) return FA_ERR_SHAPE;
   if (overlap(so, sop) || overlap(so, slp) || overlap(sl, sop) || overlap(sl, slp) || overlap(so, sl))
     return FA_ERR_ALIAS;
   MergeParams p = {};
@@ -674,13 +739,13 @@ fa_status fa_fwd_mxfp8(const fa_fwd_mxfp8_args* a, hipStream_t stream) {
   if (s != FA_OK) return s;
   if (a->B == 0 || a->Sq == 0) return FA_OK;
   const int64_t nb = a->d / 32;
-  const Span sqs = {(uintptr_t)a->q_scale, (uintptr_t)(a->q_scale + (int64_t)a->B * a->Sq * a->Hq * nb)};
-  const Span sks = {(uintptr_t)a->k_scale, (uintptr_t)(a->k_scale + (int64_t)a->B * a->Sk * a->Hkv * nb)};
-  const Span svs = {(uintptr_t)a->v_scale,
-                    (uintptr_t)(a->v_scale + (int64_t)a->B * a->Hkv * ((a->Sk + 31) / 32) * a->d)};
+  const Span sqs = lin(a->q_scale, mul_sat(a->B, a->Sq, a->Hq, nb), 1);
+  const Span sks = lin(a->k_scale, mul_sat(a->B, a->Sk, a->Hkv, nb), 1);
+  const Span svs = lin(a->v_scale, mul_sat(a->B, a->Hkv, ((int64_t)a->Sk + 31) / 32, a->d), 1);
   const Span so = span4(a->o.ptr, a->B, a->Sq, a->Hq, a->d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2);
-  const Span sl = {(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)a->B * a->Hq * a->Sq * 4};
+  const Span sl = lin(a->lse, mul_sat(a->B, a->Hq, a->Sq), 4);
   const Span sc[3] = {sqs, sks, svs};
+  if (any_bad(sc)) return FA_ERR_SHAPE;
   for (const Span& x : sc)
     if (overlap(x, so) || overlap(x, sl)) return FA_ERR_ALIAS;
   FwdParams p = {};
@@ -711,10 +776,12 @@ fa_status fa_quantize_mxfp8(const float* x, int64_t sb, int64_t ss, int64_t sh, 
   if (sb < 0 || ss < 0 || sh < 0) return FA_ERR_SHAPE;
   if (((uintptr_t)x & 3u) || ((uintptr_t)codes & 15u) || ((uintptr_t)scales & 3u)) return FA_ERR_ALIGN;
   if (B == 0 || S == 0) return FA_OK;
-  const int64_t nsc = axis == 0 ? (int64_t)B * S * H * (d / 32) : (int64_t)B * H * ((S + 31) / 32) * d;
+  const int64_t nsc = axis == 0 ? mul_sat(B, S, H, d / 32) : mul_sat(B, H, ((int64_t)S + 31) / 32, d);
   const Span sx = span4(x, B, S, H, d, sb, ss, sh, 4);
-  const Span sc = {(uintptr_t)codes, (uintptr_t)codes + (uintptr_t)((int64_t)B * S * H * d)};
-  const Span ss_ = {(uintptr_t)scales, (uintptr_t)scales + (uintptr_t)nsc};
+  const Span sc = lin(codes, mul_sat(B, S, H, d), 1);
+  const Span ss_ = lin(scales, nsc, 1);
+  const Span all[3] = {sx, sc, ss_};
+  if (any_bad(all) || nsc > 0x7fffffffLL * 256) return FA_ERR_SHAPE;
   if (overlap(sx, sc) || overlap(sx, ss_) || overlap(sc, ss_)) return FA_ERR_ALIAS;
   return hip_status(launch_quantize_mxfp8(x, sb, ss, sh, B, S, H, d, axis, codes, scales, stream));
 }

@@ -1,0 +1,181 @@
+// Host driver for the AddressSanitizer / UndefinedBehaviorSanitizer build of
+// libfa's entry points (test infrastructure).  The kernel launches are
+// replaced by stubs that count calls, so every argument check and every
+// parameter block runs on the host: each entry point is called with random
+// combinations of extreme sizes, strides, flags and (never dereferenced)
+// pointers, and with a few hand-made valid argument sets.  Any signed
+// overflow, bad shift or out-of-bounds access aborts the run.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <random>
+
+#include "fa.h"
+
+extern long g_launches;
+
+namespace {
+
+std::mt19937_64 rng(2024);
+template <class T, size_t N>
+T pick(const T (&v)[N]) {
+  return v[rng() % N];
+}
+
+const int32_t kI[] = {-2147483647 - 1, -1, 0, 1, 2, 3, 8, 16, 31, 32, 33, 64, 127, 128, 129,
+                      256, 1000, 4096, 65535, 1 << 20, 1 << 30, 2147483647};
+const int32_t kHead[] = {-1, 0, 1, 2, 4, 8, 32, 1 << 16, 2147483647};
+const int32_t kD[] = {0, 16, 32, 64, 96, 128, 256, -64};
+const int64_t kStride[] = {-8, 0, 1, 8, 64, 128, 4096, int64_t(1) << 20, int64_t(1) << 31,
+                           int64_t(1) << 40, INT64_MAX / 4, INT64_MAX - 7, INT64_MIN};
+const uintptr_t kBase = uintptr_t(0x100000000000ull);
+uintptr_t ptr() {
+  static const uintptr_t off[] = {0, 1, 2, 16, 64, 256, uintptr_t(1) << 24, uintptr_t(1) << 32,
+                                  uintptr_t(3) << 40, ~uintptr_t(0) - 15};
+  const uintptr_t o = pick(off);
+  return o == 0 ? 0 : (o > (uintptr_t(1) << 44) ? o : kBase + o + ((rng() % 64) << 26));
+}
+fa_tensor tensor() { return fa_tensor{(void*)ptr(), pick(kStride), pick(kStride), pick(kStride)}; }
+float scale() {
+  static const float v[] = {0.125f, 1.f, 0.f, -1.f, 1e30f, 1e-30f, __builtin_inff(), __builtin_nanf("")};
+  return pick(v);
+}
+
+// A valid dense layout: contiguous [B,S,H,d] at base + 2^32 * slot.
+fa_tensor dense(int slot, int64_t S, int64_t H, int64_t d) {
+  return fa_tensor{(void*)(kBase + (uintptr_t(slot) << 32)), S * H * d, H * d, d};
+}
+
+}  // namespace
+
+int main() {
+  long ok[16] = {0}, total = 0;
+  for (int it = 0; it < 100000; ++it) {
+    {
+      fa_fwd_args a;
+      memset(&a, 0, sizeof a);
+      a.dtype = fa_dtype(rng() % 4);
+      a.B = pick(kI), a.Sq = pick(kI), a.Sk = pick(kI), a.Hq = pick(kHead), a.Hkv = pick(kHead);
+      a.d = pick(kD), a.causal = int(rng() % 2), a.softmax_scale = scale();
+      a.q = tensor(), a.k = tensor(), a.v = tensor(), a.o = tensor();
+      a.lse = (float*)ptr();
+      a.q_descale = (const float*)ptr(), a.k_descale = (const float*)ptr(), a.v_descale = (const float*)ptr();
+      a.workspace = (void*)ptr(), a.workspace_bytes = size_t(pick(kStride));
+      fa_fwd_workspace_size(&a);
+      ok[fa_fwd(&a, nullptr) == FA_OK]++;
+    }
+    {
+      fa_bwd_args a;
+      memset(&a, 0, sizeof a);
+      a.dtype = fa_dtype(rng() % 4);
+      a.B = pick(kI), a.Sq = pick(kI), a.Sk = pick(kI), a.Hq = pick(kHead), a.Hkv = pick(kHead);
+      a.d = pick(kD), a.causal = int(rng() % 2), a.softmax_scale = scale();
+      a.q = tensor(), a.k = tensor(), a.v = tensor(), a.o = tensor(), a.dout = tensor();
+      a.dq = tensor(), a.dk = tensor(), a.dv = tensor();
+      a.lse = (const float*)ptr(), a.workspace = (void*)ptr(), a.workspace_bytes = size_t(pick(kStride));
+      a.stages = int(rng() % 9) - 1;
+      fa_bwd_workspace_size(&a);
+      ok[2 + (fa_bwd(&a, nullptr) == FA_OK)]++;
+    }
+    {
+      fa_fwd_varlen_args a;
+      memset(&a, 0, sizeof a);
+      a.dtype = fa_dtype(rng() % 3);
+      a.nseq = pick(kI), a.Hq = pick(kHead), a.Hkv = pick(kHead), a.d = pick(kD);
+      a.max_seqlen_q = pick(kI), a.max_seqlen_k = pick(kI), a.total_q = pick(kI), a.total_k = pick(kI);
+      a.causal = int(rng() % 2), a.softmax_scale = scale();
+      a.q = (void*)ptr(), a.k = (void*)ptr(), a.v = (void*)ptr(), a.o = (void*)ptr();
+      int64_t* st = &a.q_stride_t;
+      for (int i = 0; i < 8; ++i) st[i] = pick(kStride);
+      a.cu_seqlens_q = (const int32_t*)ptr(), a.cu_seqlens_k = (const int32_t*)ptr(), a.lse = (float*)ptr();
+      ok[4 + (fa_fwd_varlen(&a, nullptr) == FA_OK)]++;
+    }
+    {
+      fa_bwd_varlen_args a;
+      memset(&a, 0, sizeof a);
+      a.dtype = fa_dtype(rng() % 3);
+      a.nseq = pick(kI), a.Hq = pick(kHead), a.Hkv = pick(kHead), a.d = pick(kD);
+      a.max_seqlen_q = pick(kI), a.max_seqlen_k = pick(kI), a.total_q = pick(kI), a.total_k = pick(kI);
+      a.causal = int(rng() % 2), a.softmax_scale = scale();
+      a.q = (void*)ptr(), a.k = (void*)ptr(), a.v = (void*)ptr(), a.o = (void*)ptr(), a.dout = (void*)ptr();
+      a.dq = (void*)ptr(), a.dk = (void*)ptr(), a.dv = (void*)ptr();
+      int64_t* st = &a.q_stride_t;
+      for (int i = 0; i < 16; ++i) st[i] = pick(kStride);
+      a.cu_seqlens_q = (const int32_t*)ptr(), a.cu_seqlens_k = (const int32_t*)ptr(), a.lse = (const float*)ptr();
+      a.workspace = (void*)ptr(), a.workspace_bytes = size_t(pick(kStride));
+      fa_bwd_varlen_workspace_size(&a);
+      ok[6 + (fa_bwd_varlen(&a, nullptr) == FA_OK)]++;
+    }
+    {
+      fa_fwd_kvcache_args a;
+      memset(&a, 0, sizeof a);
+      a.dtype = fa_dtype(rng() % 3);
+      a.B = pick(kI), a.Sq = pick(kI), a.Hq = pick(kHead), a.Hkv = pick(kHead), a.d = pick(kD);
+      a.Snew = pick(kI), a.causal = int(rng() % 2), a.softmax_scale = scale();
+      a.q = tensor(), a.o = tensor(), a.lse = (float*)ptr();
+      a.k_cache = (void*)ptr(), a.v_cache = (void*)ptr();
+      a.k_stride_page = pick(kStride), a.k_stride_s = pick(kStride), a.k_stride_h = pick(kStride);
+      a.v_stride_page = pick(kStride), a.v_stride_s = pick(kStride), a.v_stride_h = pick(kStride);
+      a.num_pages = pick(kI), a.page_size = pick(kI), a.max_pages_per_seq = pick(kI);
+      a.max_seqlen_k = pick(kI);
+      a.block_table = (const int32_t*)ptr(), a.block_table_stride = pick(kStride);
+      a.cache_seqlens = (const int32_t*)ptr(), a.k_new = tensor(), a.v_new = tensor();
+      a.workspace = (void*)ptr(), a.workspace_bytes = size_t(pick(kStride));
+      fa_fwd_kvcache_workspace_size(&a);
+      ok[8 + (fa_fwd_kvcache(&a, nullptr) == FA_OK)]++;
+    }
+    {
+      fa_fwd_mxfp8_args a;
+      memset(&a, 0, sizeof a);
+      a.B = pick(kI), a.Sq = pick(kI), a.Sk = pick(kI), a.Hq = pick(kHead), a.Hkv = pick(kHead);
+      a.d = pick(kD), a.causal = int(rng() % 2), a.softmax_scale = scale();
+      a.q = tensor(), a.k = tensor(), a.v = tensor(), a.o = tensor(), a.lse = (float*)ptr();
+      a.q_scale = (const uint8_t*)ptr(), a.k_scale = (const uint8_t*)ptr(), a.v_scale = (const uint8_t*)ptr();
+      ok[10 + (fa_fwd_mxfp8(&a, nullptr) == FA_OK)]++;
+    }
+    {
+      fa_merge_args a;
+      memset(&a, 0, sizeof a);
+      a.dtype = fa_dtype(rng() % 3);
+      a.nparts = pick(kHead), a.B = pick(kI), a.S = pick(kI), a.H = pick(kHead), a.d = pick(kD);
+      a.o_parts = (const void*)ptr(), a.lse_parts = (const float*)ptr(), a.o = tensor(), a.lse = (float*)ptr();
+      ok[12 + (fa_merge(&a, nullptr) == FA_OK)]++;
+    }
+    {
+      const int r = fa_quantize_fp8((const float*)ptr(), pick(kStride), pick(kStride), pick(kStride), pick(kI),
+                                    pick(kI), pick(kHead), pick(kD), int(rng() % 2), (void*)ptr(),
+                                    (float*)ptr(), nullptr);
+      const int r2 = fa_quantize_mxfp8((const float*)ptr(), pick(kStride), pick(kStride), pick(kStride),
+                                       pick(kI), pick(kI), pick(kHead), pick(kD), int(rng() % 3),
+                                       (void*)ptr(), (uint8_t*)ptr(), nullptr);
+      ok[14 + (r == FA_OK && r2 == FA_OK)]++;
+    }
+    ++total;
+  }
+  // valid argument sets: each must pass and launch
+  const long before = g_launches;
+  for (int causal = 0; causal < 2; ++causal)
+    for (int d = 64; d <= 128; d += 64) {
+      fa_fwd_args f;
+      memset(&f, 0, sizeof f);
+      f.dtype = FA_BF16, f.B = 2, f.Sq = 300, f.Sk = 500, f.Hq = 8, f.Hkv = 2, f.d = d, f.causal = causal;
+      f.softmax_scale = 0.125f;
+      f.q = dense(1, 300, 8, d), f.k = dense(2, 500, 2, d), f.v = dense(3, 500, 2, d), f.o = dense(4, 300, 8, d);
+      f.lse = (float*)(kBase + (uintptr_t(5) << 32));
+      if (fa_fwd(&f, nullptr) != FA_OK) return 2;
+      fa_bwd_args b;
+      memset(&b, 0, sizeof b);
+      b.dtype = FA_BF16, b.B = 2, b.Sq = 300, b.Sk = 500, b.Hq = 8, b.Hkv = 2, b.d = d, b.causal = causal;
+      b.softmax_scale = 0.125f;
+      b.q = f.q, b.k = f.k, b.v = f.v, b.o = dense(4, 300, 8, d), b.dout = dense(6, 300, 8, d);
+      b.dq = dense(7, 300, 8, d), b.dk = dense(8, 500, 2, d), b.dv = dense(9, 500, 2, d);
+      b.lse = f.lse, b.workspace = (void*)(kBase + (uintptr_t(10) << 32));
+      b.workspace_bytes = fa_bwd_workspace_size(&b);
+      if (fa_bwd(&b, nullptr) != FA_OK) return 3;
+    }
+  printf("api fuzz: %ld rounds; accepted fwd %ld bwd %ld varlen %ld bwd_varlen %ld kvcache %ld mx %ld "
+         "merge %ld quant %ld; valid-set launches %ld\n",
+         total, ok[1], ok[3], ok[5], ok[7], ok[9], ok[11], ok[13], ok[15], g_launches - before);
+  return g_launches - before >= 8 ? 0 : 4;
+}

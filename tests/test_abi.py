@@ -288,3 +288,23 @@ def test_merge_rejects():
                    (dict(o=fa.FaTensor(FAKE + 256, 512, 128, 64)), 8)):
         assert L.fa_merge(ctypes.byref(m(**kw)), None) == st, kw
     assert L.fa_merge(ctypes.byref(m(S=0)), None) == 0
+
+
+def test_fwd_rejects_slices_beyond_32bit_offsets():
+    """A (batch, head) slice is addressed with 32-bit byte offsets up to the
+    end of its last 256-row tile: with 64 KB rows (Hq = 512, d = 64) the
+    largest accepted Sq is 65279; Sq = 65300 is refused even though it would
+    fit with only 128 rows of padding.  (Sq = 65270 passes this check and
+    fails the later overlap check instead, so nothing launches.)"""
+    Hq, d = 512, 64
+    row = Hq * d
+
+    def args(Sq, o_ptr):
+        t = fa.FaTensor(FAKE, Sq * row, row, d)
+        o = fa.FaTensor(o_ptr, Sq * row, row, d)
+        return fa.FwdArgs(0, 1, Sq, 16, Hq, Hq, d, 0, 0.125, t,
+                          fa.FaTensor(FAKE + (1 << 40), 16 * row, row, d),
+                          fa.FaTensor(FAKE + (2 << 40), 16 * row, row, d), o,
+                          FAKE + (3 << 40), None, None, None, None, 0)
+    assert fa.lib().fa_fwd(ctypes.byref(args(65300, FAKE + 64)), None) == 2
+    assert fa.lib().fa_fwd(ctypes.byref(args(65270, FAKE + 64)), None) == 8

@@ -5,20 +5,33 @@ dequantised inputs.
 The FP8 forward rounds every probability to E4M3 (3 mantissa bits) before
 the P.V product; which value a probability takes depends on the running
 maximum at the time, i.e. on the kernel's key order, so the exact output is
-not a plain definition the oracle can reproduce (parity unpinned).  It is
-pinned statistically instead:
+not a plain definition the oracle can reproduce.  It is bounded instead, per
+element, by what that rounding can do:
   * LSE comes from unrounded probabilities, so its error is that of the
     scores.  The FP8 matrix instruction sums its 64 products with less than
     fp32 precision (measured: about 2^-13 of the largest product), so the
     bar is the usual floating-point dot-product bound,
-        |dLSE_i| <= 1e-3 + 2^-11 * scale * max_j sum_c |q_ic k_jc|,
+        |dLSE_i| <= 1e-3 + eps_i,  eps_i = 2^-11 * scale * max_j sum_c |q_ic k_jc|,
     which is the bf16 bar of 1e-3 when no single product dominates (plain
     N(0,1) inputs reach ~1e-5) and scales with the outlier products;
-  * O: relative L2 error <= 5e-2.  Round-to-nearest onto a 3-bit mantissa
-    has a relative error of at most 2^-4 and an RMS relative error of about
-    0.026 over a binade; O's error is a probability-weighted sum of such
-    independent errors, so its relative L2 error is about the same; 5e-2 is
-    twice that.
+  * O, element by element.  The kernel rounds x_j = 2^8 exp(s_j - m) (m the
+    running maximum, so x_j <= 2^8 and the final row sum l >= 2^8) to E4M3:
+    the error is at most 2^-4 x_j for normal values and min(x_j, 2^-10) for
+    subnormal ones, i.e. at most 2^-4 P_ij + min(P_ij, 2^-18) in units of the
+    exact probability P_ij.  Score errors of at most eps_i move each P_ij by
+    a factor within exp(+-2 eps_i) after normalisation; the row sum and the
+    FP8 P.V instruction's own summation add at most 2^-9 relative, and the
+    bf16 output rounding 2^-9 |O_ic|.  Hence
+        |dO_ic| <= ((1 + 2^-4) e^(2 eps_i) - 1 + 2^-9) sum_j P_ij |v_jc|
+                   + sum_j min(P_ij, 2^-18) |v_jc| + 2^-9 |O_ic| + 1e-4,
+    with P and O from the oracle's fp64 scores and LSE on the same
+    (dequantised) inputs.  A wrong or dropped scale block breaks this bound
+    by a factor far above 1 on every element it touches;
+  * O, statistically: the relative L2 error over each (batch, head) and over
+    the whole tensor is at most 3e-2.  Round-to-nearest onto a 3-bit
+    mantissa has an RMS relative error of about 0.026 over a binade, and O's
+    error is a probability-weighted sum of such independent errors (a CPU
+    simulation of the rounding alone gives 0.023-0.025 at S = 256..16384).
 """
 import numpy as np
 import pytest
@@ -33,7 +46,7 @@ FP8_DOT_REL = 2.0 ** -11
 
 pytestmark = pytest.mark.gpu
 
-FP8_O_REL_L2 = 5e-2
+FP8_O_REL_L2 = 3e-2
 
 
 @pytest.mark.parametrize("shape", [(1, 300, 3, 64), (2, 128, 2, 128), (1, 1, 1, 16),
@@ -97,6 +110,61 @@ def check_lse_fp8(got, ref, absdot):
     assert (err <= bar).all()
 
 
+def o_bound_rows(Q, K, V, grp, scale, causal, bi, hi, ii, lse_ref, o_ref):
+    """Element-wise bound on |O_kernel - O_exact| for the listed rows (see
+    the module docstring): Q [B,Sq,Hq,d], K and V [B,Sk,Hkv,d] dequantised
+    float64, rows (bi[r], hi[r], ii[r]) with the oracle's LSE and O."""
+    bi, hi, ii = (np.asarray(x) for x in (bi, hi, ii))
+    Sq, Sk = Q.shape[1], K.shape[1]
+    bound = np.zeros_like(o_ref, dtype=np.float64)
+    for b, h in sorted(set(zip(bi.tolist(), hi.tolist()))):
+        r = np.nonzero((bi == b) & (hi == h))[0]
+        q = Q[b, ii[r], h]
+        k, v = K[b, :, h // grp], V[b, :, h // grp]
+        s = scale * (q @ k.T)
+        eps = 2.0 ** -11 * scale * (np.abs(q) @ np.abs(k).T).max(axis=1, initial=0.0)
+        lse = np.asarray(lse_ref)[r]
+        with np.errstate(invalid="ignore", over="ignore"):
+            P = np.exp(s - lse[:, None])
+        if causal:
+            P[np.arange(Sk)[None, :] > (ii[r] + Sk - Sq)[:, None]] = 0.0
+        P[~np.isfinite(lse)] = 0.0
+        av = np.abs(v)
+        coef = (1 + 2.0 ** -4) * np.exp(2 * eps) - 1 + 2.0 ** -9
+        bound[r] = (coef[:, None] * (P @ av) + np.minimum(P, 2.0 ** -18) @ av
+                    + 2.0 ** -9 * np.abs(o_ref[r]) + 1e-4)
+    return bound
+
+
+def check_o_fp8(o, o_ref, bound, bi, hi):
+    """The element-wise bound, then relative L2 per (batch, head) and overall."""
+    o, o_ref = np.asarray(o, np.float64), np.asarray(o_ref, np.float64)
+    assert np.isfinite(o).all()
+    err = np.abs(o - o_ref)
+    worst = float((err / bound).max(initial=0.0))
+    rel = float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
+    bi, hi = np.asarray(bi), np.asarray(hi)
+    per_head = []
+    for b, h in sorted(set(zip(bi.tolist(), hi.tolist()))):
+        r = (bi == b) & (hi == h)
+        nr = np.linalg.norm(o_ref[r])
+        if nr > 0:
+            per_head.append(float(np.linalg.norm(o[r] - o_ref[r]) / nr))
+    print(f"  O rel_l2={rel:.3e} worst head rel_l2={max(per_head, default=0):.3e} "
+          f"max_abs={float(err.max(initial=0)):.3e} worst err/bound={worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+    assert rel <= FP8_O_REL_L2, rel
+    assert max(per_head, default=0.0) <= FP8_O_REL_L2, per_head
+    return rel
+
+
+def all_rows(B, Hq, Sq):
+    bi = [b for b in range(B) for h in range(Hq) for _ in range(Sq)]
+    hi = [h for b in range(B) for h in range(Hq) for _ in range(Sq)]
+    ii = [i for b in range(B) for h in range(Hq) for i in range(Sq)]
+    return bi, hi, ii
+
+
 def run_fp8(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
     print(f"fp8 B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}",
           flush=True)
@@ -114,13 +182,23 @@ def run_fp8(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
     Q, K, V = dequant(qc, qs), dequant(kc, ks), dequant(vc, vs)
     o_ref, lse_ref = oracle.attention_fwd(Q, K, V, causal, scale)
     o = go.t.float().cpu().numpy()
-    assert np.isfinite(o).all()
-    rel = float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
-    print(f"  O rel_l2={rel:.3e} max_abs={float(np.abs(o - o_ref).max()):.3e}", flush=True)
     sc = 1.0 / np.sqrt(d) if scale is None else scale
     check_lse_fp8(gl.t.cpu().numpy(), lse_ref, abs_dot_max(Q, K, Hq // Hkv, sc))
-    assert rel <= FP8_O_REL_L2, rel
+    check_fp8_all_rows(o, o_ref, lse_ref, Q, K, V, Hq // Hkv, sc, causal)
     return o, o_ref
+
+
+def check_fp8_all_rows(o, o_ref, lse_ref, Q, K, V, grp, scale, causal):
+    """check_o_fp8 over every row of dense [B,Sq,Hq,d] results."""
+    B, Sq, Hq, d = o.shape
+    if B * Sq == 0:
+        return
+    bi, hi, ii = all_rows(B, Hq, Sq)
+    rows_o = o[bi, ii, hi]
+    rows_ref = o_ref[bi, ii, hi]
+    lse_rows = lse_ref[bi, hi, ii]
+    bound = o_bound_rows(Q, K, V, grp, scale, causal, bi, hi, ii, lse_rows, rows_ref)
+    check_o_fp8(rows_o, rows_ref, bound, bi, hi)
 
 
 @pytest.mark.parametrize("shape", [(1, 256, 256, 2, 2, 64), (2, 300, 300, 4, 2, 128),
@@ -167,13 +245,13 @@ def test_fp8_full_size_rms():
     deq = [dequant(c, s) for c, s in blk]
     o_ref_b, l_ref_b = oracle.attention_fwd_rows(*deq, bi, hi, ii, False)
     got = o_blk[bi, ii, hi].float().cpu().numpy()
-    rel = float(np.linalg.norm(got - o_ref_b) / np.linalg.norm(o_ref_b))
-    print(f"  (b) per-block vs oracle on dequantised inputs: rel_l2={rel:.3e}", flush=True)
+    print("  (b) per-block vs oracle on dequantised inputs:", flush=True)
     Qr = deq[0][0][np.asarray(ii), np.asarray(hi)]                       # [n, d]
     absdot = np.array([(np.abs(Qr[r]) @ np.abs(deq[1][0, :, hi[r]]).T).max() / np.sqrt(d)
                        for r in range(len(ii))])
     check_lse_fp8(l_blk[bi, hi, ii].cpu().numpy(), l_ref_b, absdot)
-    assert rel <= FP8_O_REL_L2
+    bound = o_bound_rows(*deq, 1, 1.0 / np.sqrt(d), False, bi, hi, ii, l_ref_b, o_ref_b)
+    check_o_fp8(got, o_ref_b, bound, bi, hi)
     o_ref, _ = oracle.attention_fwd_rows(*[x.cpu() for x in X], bi, hi, ii, False)
     rms = {}
     for name, o in (("fp8_block", o_blk), ("fp8_tensor", o_ten), ("bf16", o_bf)):

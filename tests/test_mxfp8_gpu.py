@@ -1,10 +1,13 @@
 """GPU checks of the MX FP8 path (E4M3 elements with one E8M0 scale per 32
 elements along each product's reduction dimension): the quantiser bit for
 bit against the oracle's MX encoder, and the forward against the fp64
-oracle on the dequantised inputs, with the statistical bars of the FP8 path
-(the probabilities are rounded to E4M3 at the running maximum of the
-kernel's key order, which no plain definition fixes: parity unpinned for
-the exact output; see tests/test_fp8_gpu.py for the bars' derivation)."""
+oracle on the dequantised inputs, with the element-wise bound and relative L2
+bars of the FP8 path (the probabilities are rounded to E4M3 at the running
+maximum of the kernel's key order, which no plain definition fixes; the
+bound on what that rounding can do is derived in tests/test_fp8_gpu.py and
+holds unchanged here: the E8M0 block scales are powers of two applied
+inside the matrix instruction, so the dequantised Q, K and V are exactly
+what the products see)."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +16,7 @@ import oracle
 from oracle import fp8 as ofp8
 from io_aware_exact_amd import fa, inputs
 from parity import Guarded
-from test_fp8_gpu import FP8_O_REL_L2, abs_dot_max, check_lse_fp8
+from test_fp8_gpu import abs_dot_max, check_fp8_all_rows, check_lse_fp8, check_o_fp8, o_bound_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -66,12 +69,9 @@ def run_mx(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
     V = ofp8.dequantize_mx(vc.cpu().numpy(), vs.cpu().numpy(), "s")
     o_ref, lse_ref = oracle.attention_fwd(Q, K, V, causal, scale)
     o = go.t.float().cpu().numpy()
-    assert np.isfinite(o).all()
-    rel = float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
-    print(f"  O rel_l2={rel:.3e} max_abs={float(np.abs(o - o_ref).max()):.3e}", flush=True)
     sc = 1.0 / np.sqrt(d) if scale is None else scale
     check_lse_fp8(gl.t.cpu().numpy(), lse_ref, abs_dot_max(Q, K, Hq // Hkv, sc))
-    assert rel <= FP8_O_REL_L2, rel
+    check_fp8_all_rows(o, o_ref, lse_ref, Q, K, V, Hq // Hkv, sc, causal)
 
 
 @pytest.mark.parametrize("shape", [(1, 256, 256, 2, 2, 64), (2, 300, 300, 4, 2, 128),
@@ -118,13 +118,13 @@ def test_mx_full_size():
            for (c, s), a in zip(mx, ("d", "d", "s"))]
     o_ref_m, l_ref_m = oracle.attention_fwd_rows(*deq, bi, hi, ii, False)
     got = o_mx[bi, ii, hi].float().cpu().numpy()
-    rel = float(np.linalg.norm(got - o_ref_m) / np.linalg.norm(o_ref_m))
-    print(f"  MX vs oracle on dequantised inputs: rel_l2={rel:.3e}", flush=True)
+    print("  MX vs oracle on dequantised inputs:", flush=True)
     Qr = deq[0][0][np.asarray(ii), np.asarray(hi)]
     absdot = np.array([(np.abs(Qr[r]) @ np.abs(deq[1][0, :, hi[r]]).T).max() / np.sqrt(d)
                        for r in range(len(ii))])
     check_lse_fp8(l_mx[bi, hi, ii].cpu().numpy(), l_ref_m, absdot)
-    assert rel <= FP8_O_REL_L2
+    bound = o_bound_rows(*deq, 1, 1.0 / np.sqrt(d), False, bi, hi, ii, l_ref_m, o_ref_m)
+    check_o_fp8(got, o_ref_m, bound, bi, hi)
     o_ref, _ = oracle.attention_fwd_rows(*[x.cpu() for x in X], bi, hi, ii, False)
     deq_b = [ofp8.dequantize_blocks(c.cpu().numpy(), s.cpu().numpy()) for c, s in blk]
     o_deq_b, _ = oracle.attention_fwd_rows(*deq_b, bi, hi, ii, False)

@@ -69,32 +69,30 @@ def traffic_from_profile(name, files):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(q, k, v, do, causal, with_bwd):
-    """The fp64 oracle on one full (batch 0, head 0) slice of the step,
-    converted to a TFLOP/s rate with the same algorithmic flop count."""
-    import oracle
-    B, S, H, d = q.shape
-    t0 = time.perf_counter()
-    if with_bwd:
-        oracle.attention_bwd(q[:1, :, :1], k[:1, :, :1], v[:1, :, :1], do[:1, :, :1],
-                             causal, None)
-    else:
-        oracle.attention_fwd(q[:1, :, :1], k[:1, :, :1], v[:1, :, :1], causal, None)
-    dt = time.perf_counter() - t0
-    flops = (3.5 if with_bwd else 1.0) * fwd_flops(1, S, S, 1, d, causal)
-    what = "forward+backward" if with_bwd else "forward"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 {what} of one full (b,h) slice of the step (S={S}, d={d}) "
-                      f"took {dt:.1f} s; rate uses the step's algorithmic flops"}
-
-
-def sampled_check(q, k, v, o, lse, causal):
-    """Oracle rows {0, 1, S-1} plus 13 seeded rows of (b, h) = (0, 0) and (B-1, H-1)."""
+def cpu_baseline_leg(q, k, v, do, o, lse, causal, fp8_rows):
+    """Everything that runs the fp64 oracle (it never enters a timed GPU
+    region):
+      * the baseline: the oracle's forward+backward on one full (batch 0,
+        head 0) slice of the step, converted to a TFLOP/s rate with the same
+        algorithmic flop count;
+      * a sampled check of the step's O and LSE (rows {0, 1, S-1} plus 13
+        seeded rows of (b, h) = (0, 0) and (B-1, H-1));
+      * the FP8 workload's RMS error against the oracle on the original fp32
+        inputs, for per-block FP8, per-tensor FP8 and bf16 inputs (rows
+        sampled by leg_fp8), and the per-tensor / per-block ratio."""
     import numpy as np
     import oracle
     from io_aware_exact_amd import inputs
     B, S, H, d = q.shape
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q[:1, :, :1], k[:1, :, :1], v[:1, :, :1], do[:1, :, :1], causal, None)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, S, S, 1, d, causal)
+    out = {"cpu_baseline": {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 forward+backward of one full (b,h) slice of the step (S={S}, d={d}) "
+                  f"took {dt:.1f} s; rate uses the step's algorithmic flops"}}
     rows = inputs.sample_indices(S, 13, 77, always=(0, 1, S - 1))
     bi, hi, ii = [], [], []
     for b, h in ((0, 0), (B - 1, H - 1)):
@@ -103,13 +101,27 @@ def sampled_check(q, k, v, o, lse, causal):
     o_ref, lse_ref = oracle.attention_fwd_rows(q, k, v, bi, hi, ii, causal)
     o_got = o[bi, ii, hi].float().cpu().numpy()
     l_got = lse[bi, hi, ii].cpu().numpy()
-    return float(np.abs(o_got - o_ref).max()), float(np.abs(l_got - lse_ref).max())
+    out["check"] = {"o_max_abs": float(np.abs(o_got - o_ref).max()),
+                    "lse_max_abs": float(np.abs(l_got - lse_ref).max())}
+    if fp8_rows is not None:
+        X, (fbi, fhi, fii), got = fp8_rows
+        ref, _ = oracle.attention_fwd_rows(*X, fbi, fhi, fii, False)
+        rms = {name: float(np.sqrt(np.mean((g - ref) ** 2))) for name, g in got.items()}
+        out["fp8_rms"] = {
+            "workload": "fp8 workload, 64 seeded rows x 16 heads, vs fp64 oracle on the "
+                        "original fp32 inputs",
+            "per_block_fp8": rms["fp8_block"], "per_tensor_fp8": rms["fp8_tensor"],
+            "bf16": rms["bf16"], "mx_fp8": rms["mx"],
+            "per_tensor_over_per_block": rms["fp8_tensor"] / rms["fp8_block"]}
+    return out
 
 
-def time_calls(fn, reps, warmup=2, warm_ms=100.0):
-    """Average ms of fn() over reps back-to-back calls on the current stream,
-    after at least `warmup` calls and about `warm_ms` of untimed work (the
-    first launches on fresh buffers run slower)."""
+def time_calls(fn, reps, warmup=2, warm_ms=100.0, min_ms=200.0):
+    """Times fn() launched back to back on the current stream, after at
+    least `warmup` calls and about `warm_ms` of untimed work (the first
+    launches on fresh buffers run slower): max(reps, 20) calls, more if
+    needed to cover `min_ms`.  Each call is bracketed by HIP events on the
+    stream.  Returns {"mean", "median", "min"} in ms and the call count."""
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -118,16 +130,24 @@ def time_calls(fn, reps, warmup=2, warm_ms=100.0):
         fn()
     e1.record(stream)
     torch.cuda.synchronize()
-    per_call = e0.elapsed_time(e1) / max(warmup, 1)
-    for _ in range(min(int(warm_ms / max(per_call, 1e-3)), 200)):
+    per_call = max(e0.elapsed_time(e1) / max(warmup, 1), 1e-3)
+    for _ in range(min(int(warm_ms / per_call), 200)):
         fn()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
+    n = max(reps, 20, min(int(min_ms / per_call) + 1, 2000))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    return {"mean": ev[0].elapsed_time(ev[n]) / n, "median": each[n // 2], "min": each[0], "n": n}
+
+
+def timing(t):
+    return {"mean_ms": round(t["mean"], 4), "median_ms": round(t["median"], 4),
+            "min_ms": round(t["min"], 4), "calls": t["n"]}
 
 
 def leg_causal(reps):
@@ -137,13 +157,18 @@ def leg_causal(reps):
     q, k, v, do = inputs.qkv(B, S, S, H, H, d, 2000, device="cuda", with_dout=True)
     o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-    ms_f = time_calls(lambda: fa.fwd(q, k, v, True, out=o, lse=lse), reps)
-    ms_b = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, True), reps)
+    grads = tuple(torch.empty_like(x) for x in (q, k, v))
+    a = fa.bwd_args(q, k, v, o, do, lse, *grads, True, None)
+    ws = torch.empty(int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a))), dtype=torch.uint8,
+                     device="cuda")
+    tf_ = time_calls(lambda: fa.fwd(q, k, v, True, out=o, lse=lse), reps)
+    tb = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, True, out=grads, workspace=ws), reps)
+    ms_f, ms_b = tf_["mean"], tb["mean"]
     ff = fwd_flops(B, S, S, H, d, True)
     return {"workload": "B=2 H=16 Sq=Sk=8192 d=128 causal",
             "fwd_tflops": round(ff / ms_f / 1e9, 2), "fwd_ms": round(ms_f, 4),
             "fwd_bwd_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2),
-            "bwd_ms": round(ms_b, 4)}
+            "bwd_ms": round(ms_b, 4), "fwd_timing": timing(tf_), "bwd_timing": timing(tb)}
 
 
 def leg_decode(reps):
@@ -155,13 +180,14 @@ def leg_decode(reps):
     o = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
     ws = torch.empty(fa.fwd_workspace_bytes(q, k, v, True), dtype=torch.uint8, device="cuda")
-    ms = time_calls(lambda: fa.fwd(q, k, v, True, out=o, lse=lse, workspace=ws), reps)
+    t = time_calls(lambda: fa.fwd(q, k, v, True, out=o, lse=lse, workspace=ws), reps)
+    ms = t["mean"]
     kv_bytes = 2 * B * Sk * Hkv * d * 2
     io_bytes = kv_bytes + 2 * (B * Sq * Hq * d * 2) + B * Hq * Sq * 4
     return {"workload": "decode B=64 Sq=1 Sk=32768 Hq=32 Hkv=8 d=128",
             "ms": round(ms, 4), "gbps": round(io_bytes / ms / 1e6, 1),
             "frac_of_hbm": round(io_bytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
-            "tflops": round(4.0 * B * Hq * Sq * Sk * d / ms / 1e9, 2)}
+            "tflops": round(4.0 * B * Hq * Sq * Sk * d / ms / 1e9, 2), "timing": timing(t)}
 
 
 def leg_varlen(reps):
@@ -179,13 +205,15 @@ def leg_varlen(reps):
     T, mx = sum(lens), max(lens)
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
-    ms = time_calls(lambda: fa.fwd_varlen(q, k, v, cu, cu, mx, mx, True, out=o, lse=lse), reps)
+    tv = time_calls(lambda: fa.fwd_varlen(q, k, v, cu, cu, mx, mx, True, out=o, lse=lse), reps)
+    ms = tv["mean"]
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     a = fa.bwd_varlen_args(q, k, v, o, do, lse, *grads, cu, cu, mx, mx, True, None)
     ws = torch.empty(max(int(fa.lib().fa_bwd_varlen_workspace_size(ctypes.byref(a))), 1),
                      dtype=torch.uint8, device="cuda")
-    ms_b = time_calls(lambda: fa.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, True,
-                                            out=grads, workspace=ws), reps)
+    tvb = time_calls(lambda: fa.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, True,
+                                           out=grads, workspace=ws), reps)
+    ms_b = tvb["mean"]
     pairs = sum(L * (L + 1) // 2 for L in lens)
     flops_half = sum(2.0 * Hq * d * L * L for L in lens)
     return {"workload": "varlen 16 seqs U[128,32768] Hq=32 Hkv=8 d=128 causal",
@@ -194,7 +222,8 @@ def leg_varlen(reps):
             "tflops_exact_pairs": round(4.0 * Hq * d * pairs / ms / 1e9, 2),
             "bwd_ms": round(ms_b, 3),
             "fwd_bwd_tflops": round(3.5 * flops_half / (ms + ms_b) / 1e9, 2),
-            "fwd_bwd_tflops_exact_pairs": round(14.0 * Hq * d * pairs / (ms + ms_b) / 1e9, 2)}
+            "fwd_bwd_tflops_exact_pairs": round(14.0 * Hq * d * pairs / (ms + ms_b) / 1e9, 2),
+            "fwd_timing": timing(tv), "bwd_timing": timing(tvb)}
 
 
 def leg_kvcache(reps):
@@ -226,8 +255,9 @@ def leg_kvcache(reps):
         a = fa.kvcache_args(q, kc, vc, lens, bt, kn, vn, o, lse, True, None)
         n = int(fa.lib().fa_fwd_kvcache_workspace_size(ctypes.byref(a)))
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
-        ms = time_calls(lambda: fa.fwd_kvcache(q, kc, vc, lens, bt, kn, vn, True, out=o, lse=lse,
-                                               workspace=ws), reps)
+        t = time_calls(lambda: fa.fwd_kvcache(q, kc, vc, lens, bt, kn, vn, True, out=o, lse=lse,
+                                              workspace=ws), reps)
+        ms = t["mean"]
         Lk = L + sq
         kv_bytes = 2 * B * Lk * Hkv * d * 2
         io_bytes = kv_bytes + 2 * B * sq * Hq * d * 2 + B * Hq * sq * 4 + 2 * B * sq * Hkv * d * 2
@@ -236,37 +266,56 @@ def leg_kvcache(reps):
                                  f"d={d} page={ps} causal",
                      "ms": round(ms, 4), "gbps": round(io_bytes / ms / 1e6, 1),
                      "frac_of_hbm": round(io_bytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
-                     "tflops": round(4.0 * Hq * d * pairs / ms / 1e9, 2)}
+                     "tflops": round(4.0 * Hq * d * pairs / ms / 1e9, 2), "timing": timing(t)}
         del kc, vc
         torch.cuda.empty_cache()
     return out
 
 
-def leg_fp8(reps):
+def leg_fp8(reps, keep_rows=None):
     """FP8 (E4M3, per-block scales) forward: B=1, H=16, S=16384, d=128,
-    non-causal, inputs N(0,1) + Bernoulli(0.001) N(0,100) (seed 4000).
-    Quantisation is input preparation and is not timed."""
+    non-causal, inputs N(0,1) + Bernoulli(0.001) N(0,100) (seed 4000), and
+    the MX variant on the same inputs.  Quantisation is input preparation and
+    is not timed.  With keep_rows (a dict), 64 seeded rows of every head of
+    the per-block, per-tensor, MX and bf16 outputs are left there, with the
+    inputs, for the RMS comparison against the oracle."""
     from io_aware_exact_amd import fa, inputs
     B, S, H, d = 1, 16384, 16, 128
-    qkv = [fa.quantize_fp8(inputs.outlier_normal((B, S, H, d), 4000 + i, device="cuda"))
-           for i in range(3)]
+    X = [inputs.outlier_normal((B, S, H, d), 4000 + i, device="cuda") for i in range(3)]
+    qkv = [fa.quantize_fp8(x) for x in X]
     codes = [c for c, _ in qkv]
     scales = [s for _, s in qkv]
     o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-    ms = time_calls(lambda: fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse), reps)
+    t = time_calls(lambda: fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse), reps)
+    ms = t["mean"]
     ff = fwd_flops(B, S, S, H, d, False)
-    X = [inputs.outlier_normal((B, S, H, d), 4000 + i, device="cuda") for i in range(3)]
     mx = [fa.quantize_mxfp8(X[0], 0), fa.quantize_mxfp8(X[1], 0), fa.quantize_mxfp8(X[2], 1)]
-    del X
-    ms_mx = time_calls(lambda: fa.fwd_mxfp8(*[c for c, _ in mx], *[s for _, s in mx], False,
-                                            out=o, lse=lse), reps)
+    o_mx = torch.empty_like(o)
+    tm = time_calls(lambda: fa.fwd_mxfp8(*[c for c, _ in mx], *[s for _, s in mx], False,
+                                         out=o_mx, lse=lse), reps)
+    ms_mx = tm["mean"]
+    if keep_rows is not None:
+        rows = inputs.sample_indices(S, 61, 4001, always=(0, 1, S - 1))
+        bi = [0] * (len(rows) * H)
+        hi = [h for h in range(H) for _ in rows]
+        ii = [i for _ in range(H) for i in rows]
+        ten = [fa.quantize_fp8(x, per_tensor=True) for x in X]
+        o_ten, _ = fa.fwd_fp8(*[c for c, _ in ten], *[s for _, s in ten], False)
+        o_bf, _ = fa.fwd(*[x.to(torch.bfloat16) for x in X], False)
+        fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse)
+        torch.cuda.synchronize()
+        keep_rows["rows"] = ([x.cpu() for x in X], (bi, hi, ii),
+                             {name: y[bi, ii, hi].float().cpu().numpy()
+                              for name, y in (("fp8_block", o), ("fp8_tensor", o_ten),
+                                              ("bf16", o_bf), ("mx", o_mx))})
     return {"workload": "fp8 e4m3 fwd B=1 H=16 S=16384 d=128 non-causal, per-block scales",
             "ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2),
-            "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4), "timing": timing(t),
             "mx": {"workload": "MX fp8 (E8M0 scale per 32 elements) fwd, same shape and inputs",
                    "ms": round(ms_mx, 4), "tflops": round(ff / ms_mx / 1e9, 2),
-                   "frac_of_fp8_peak": round(ff / ms_mx / 1e9 / PEAK_FP8_TFLOPS, 4)}}
+                   "frac_of_fp8_peak": round(ff / ms_mx / 1e9 / PEAK_FP8_TFLOPS, 4),
+                   "timing": timing(tm)}}
 
 
 def leg_sweep(reps):
@@ -282,7 +331,7 @@ def leg_sweep(reps):
                 q, k, v = inputs.qkv(B, S, S, H, H, d, 1000, device="cuda")
                 o = torch.empty_like(q)
                 lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-                ms = time_calls(lambda: fa.fwd(q, k, v, causal, out=o, lse=lse), reps)
+                ms = time_calls(lambda: fa.fwd(q, k, v, causal, out=o, lse=lse), reps)["mean"]
                 row[str(S)] = round(fwd_flops(B, S, S, H, d, causal) / ms / 1e9, 1)
             out[f"d{d}_{'causal' if causal else 'noncausal'}"] = row
     return out
@@ -297,27 +346,32 @@ def leg_main(reps, with_bwd):
     q, k, v, do = inputs.qkv(B, S, S, H, H, d, W["seed"], device="cuda", with_dout=True)
     o = torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    grads = tuple(torch.empty_like(x) for x in (q, k, v))
+    a = fa.bwd_args(q, k, v, o, do, lse, *grads, causal, None)
+    ws = torch.empty(int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a))), dtype=torch.uint8,
+                     device="cuda")
 
     def step():
         fa.fwd(q, k, v, causal, out=o, lse=lse)
         if with_bwd:
-            fa.bwd(q, k, v, o, do, lse, causal)
-    ms = time_calls(step, reps)
+            fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws)
+    t = time_calls(step, reps)
+    ms = t["mean"]
     ff = fwd_flops(B, S, S, H, d, causal) * (3.5 if with_bwd else 1.0)
-    return {"ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2)}
+    return {"ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2), "timing": timing(t)}
 
 
-def extra_legs(args):
+def extra_legs(args, keep_rows=None):
     out = {}
     if args.only in ("fwd", "fwdbwd"):
         return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
-    for name, fn, reps in (("causal", leg_causal, 10), ("decode", leg_decode, 20),
-                           ("varlen", leg_varlen, 5), ("kvcache", leg_kvcache, 10),
-                           ("fp8", leg_fp8, 10),
-                           ("sweep", leg_sweep, 5)):
+    for name, fn, reps in (("causal", leg_causal, 20), ("decode", leg_decode, 20),
+                           ("varlen", leg_varlen, 20), ("kvcache", leg_kvcache, 20),
+                           ("fp8", leg_fp8, 20),
+                           ("sweep", leg_sweep, 20)):
         if args.only and args.only != name:
             continue
-        out[name] = fn(reps)
+        out[name] = fn(reps, keep_rows) if name == "fp8" else fn(reps)
         torch.cuda.empty_cache()
     return out
 
@@ -378,28 +432,31 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # exactly args.steps steps between two synchronisations; an event after
+    # each step also gives the per-step median and minimum
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[args.steps]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
     # each kernel of the step alone, launched back to back on the same stream
     # (one launch per call: fa_fwd, and fa_bwd restricted to one stage; the
     # workspace already holds D from the step above)
-    reps = max(args.steps, 10)
-    ms_fwd = time_calls(lambda: fa.fwd(q, k, v, causal, out=o, lse=lse), reps)
-    ms_pre = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
-                                       stages=fa.FA_BWD_PREPROCESS), reps)
-    ms_dkdv = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
-                                        stages=fa.FA_BWD_DKDV), reps)
-    ms_dq = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
-                                      stages=fa.FA_BWD_DQ), reps)
+    reps = max(args.steps, 20)
+    t_fwd = time_calls(lambda: fa.fwd(q, k, v, causal, out=o, lse=lse), reps)
+    t_pre = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
+                                      stages=fa.FA_BWD_PREPROCESS), reps)
+    t_dkdv = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
+                                       stages=fa.FA_BWD_DKDV), reps)
+    t_dq = time_calls(lambda: fa.bwd(q, k, v, o, do, lse, causal, out=grads, workspace=ws,
+                                     stages=fa.FA_BWD_DQ), reps)
+    ms_fwd, ms_pre, ms_dkdv, ms_dq = t_fwd["mean"], t_pre["mean"], t_dkdv["mean"], t_dq["mean"]
 
     ff = fwd_flops(B, S, S, H, d, causal)
     gemm = ff / 2                       # one GEMM-shaped product: 2*B*H*Sq*Sk*d
@@ -410,14 +467,15 @@ def main():
         return round(flops / ms / 1e9, 2)
 
     kernels = {
-        "fwd_bf16_pp_kernel": {"ms": round(ms_fwd, 4), "algorithmic_tflops": tf(2 * gemm, ms_fwd)},
-        "bwd_preprocess_kernel": {"ms": round(ms_pre, 4)},
-        "bwd_dkdv_kernel": {"ms": round(ms_dkdv, 4), "algorithmic_tflops": tf(4 * gemm, ms_dkdv)},
+        "fwd_bf16_pp_kernel": {"ms": round(ms_fwd, 4), "algorithmic_tflops": tf(2 * gemm, ms_fwd),
+                               "timing": timing(t_fwd)},
+        "bwd_preprocess_kernel": {"ms": round(ms_pre, 4), "timing": timing(t_pre)},
+        "bwd_dkdv_kernel": {"ms": round(ms_dkdv, 4), "algorithmic_tflops": tf(4 * gemm, ms_dkdv),
+                            "timing": timing(t_dkdv)},
         "bwd_dq_kernel": {"ms": round(ms_dq, 4), "algorithmic_tflops": tf(gemm, ms_dq),
-                          "executed_tflops": tf(3 * gemm, ms_dq)},
+                          "executed_tflops": tf(3 * gemm, ms_dq), "timing": timing(t_dq)},
     }
     dk_tf = 4 * gemm / ms_dkdv / 1e9
-    err_o, err_lse = sampled_check(q, k, v, o, lse, causal)
 
     line = {
         "metric": "attention fwd+bwd TFLOP/s (bf16, d=128)",
@@ -427,6 +485,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_median_ms": round(per_step[len(per_step) // 2], 4),
+        "step_min_ms": round(per_step[0], 4),
         "wall_s": round(wall, 3),
         "higher_is_better": True,
         "scaling": "weak",
@@ -447,12 +507,12 @@ def main():
                          "achieved": tf(ff, ms_fwd), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ff / ms_fwd / 1e9 / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profile("fwd_bf16_b2_h16_s8192_d128", FWD_SOURCES)},
-        "check": {"o_max_abs": err_o, "lse_max_abs": err_lse},
     }
+    keep = {} if not args.no_cpu_baseline else None
     if not args.no_extra:
-        line["extra"] = extra_legs(args)
+        line["extra"] = extra_legs(args, keep)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(q, k, v, do, causal, True)
+        line.update(cpu_baseline_leg(q, k, v, do, o, lse, causal, keep.get("rows")))
     print(json.dumps(line), flush=True)
 
 

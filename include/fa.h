@@ -329,6 +329,24 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args* args, hipStream_t stream);
 /* Dense backward; see fa_bwd_args. */
 fa_status fa_bwd(const fa_bwd_args* args, hipStream_t stream);
 
+/* Dense backward that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Arguments, checks and
+ * results are fa_bwd's (bitwise the same gradients), except that
+ * args->workspace and args->workspace_bytes are ignored: the scratch fa_bwd
+ * keeps there (D = rowsum(dO o O), 4 bytes per query row and head, rounded
+ * up to 256 bytes) lives in a fixed array of FA_BWD_NOALLOC_MAX_SCRATCH bytes
+ * in the library's device code, one per GPU, held until the process ends.
+ * Calls with B * Hq * Sq * 4 > FA_BWD_NOALLOC_MAX_SCRATCH (8,388,608 query
+ * rows x heads) return FA_ERR_WORKSPACE.  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents: calls that overlap in
+ * time on one GPU (several streams or host threads) race on it and must be
+ * serialised by the caller, and a call whose stages skip FA_BWD_PREPROCESS
+ * uses the D left by the previous call on that GPU.  The first call on a
+ * device looks up the array's address there (FA_ERR_HIP if that fails). */
+#define FA_BWD_NOALLOC_MAX_SCRATCH (32u << 20)
+fa_status fa_bwd_noalloc(const fa_bwd_args* args, hipStream_t stream);
+
 /* Workspace bytes fa_bwd_varlen needs for these arguments. */
 size_t fa_bwd_varlen_workspace_size(const fa_bwd_varlen_args* args);
 

@@ -621,6 +621,22 @@ fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
   return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, false, stages, stream));
 }
 
+fa_status fa_bwd_noalloc(const fa_bwd_args* a, hipStream_t stream) {
+  if (!a) return FA_ERR_NULL;
+  static_assert(kNoallocScratchBytes == FA_BWD_NOALLOC_MAX_SCRATCH, "scratch size in the header");
+  fa_bwd_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  const size_t need = bwd_delta_bytes(&b);
+  if (need > kNoallocScratchBytes) return FA_ERR_WORKSPACE;
+  if (need > 0) {
+    // the library's own per-device scratch array; no allocation
+    if (noalloc_scratch(&b.workspace) != hipSuccess) return FA_ERR_HIP;
+    b.workspace_bytes = kNoallocScratchBytes;
+  }
+  return fa_bwd(&b, stream);
+}
+
 size_t fa_bwd_varlen_workspace_size(const fa_bwd_varlen_args* a) {
   if (!a) return 0;
   return bwd_varlen_delta_bytes(a);

@@ -152,3 +152,9 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool varlen, 
 // Zero a bf16 [B,S,H,d] tensor with element strides (d contiguous).
 hipError_t launch_zero_bf16(void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb,
                             int64_t ss, int64_t sh, hipStream_t stream);
+
+// Scratch for the no-allocation entry points: a fixed per-device array of
+// kNoallocScratchBytes in the library's device code.  noalloc_scratch returns
+// its address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);

@@ -136,7 +136,7 @@ EXPORTS = ["fa_abi_version", "fa_status_string", "fa_fwd_workspace_size",
            "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
            "fa_bwd_varlen_workspace_size", "fa_bwd_varlen", "fa_fwd_kvcache_workspace_size",
            "fa_fwd_kvcache", "fa_quantize_fp8", "fa_fwd_mxfp8", "fa_quantize_mxfp8",
-           "fa_merge"]
+           "fa_merge", "fa_bwd_noalloc"]
 
 _lib = None
 
@@ -163,6 +163,8 @@ def lib():
         L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), vp]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.POINTER(BwdArgs), vp]
+        L.fa_bwd_noalloc.restype = ctypes.c_int
+        L.fa_bwd_noalloc.argtypes = [ctypes.POINTER(BwdArgs), vp]
         L.fa_bwd_varlen_workspace_size.restype = ctypes.c_size_t
         L.fa_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(BwdVarlenArgs)]
         L.fa_bwd_varlen.restype = ctypes.c_int
@@ -458,6 +460,20 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, out=None, workspace=Non
         workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q.device)
     a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace, stages)
     _check("fa_bwd", lib().fa_bwd(ctypes.byref(a), _stream()))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, causal=False, scale=None, out=None, stages=0):
+    """Dense backward through fa_bwd_noalloc: no workspace and no allocation
+    in the library (its scratch is a fixed per-device array shared by every
+    call on that GPU).  Returns (dq, dk, dv) bf16; `out` may be passed in."""
+    if out is None:
+        out = (torch.empty_like(q, dtype=torch.bfloat16),
+               torch.empty(k.shape, dtype=torch.bfloat16, device=k.device),
+               torch.empty(v.shape, dtype=torch.bfloat16, device=v.device))
+    dq, dk, dv = out
+    a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, None, stages)
+    _check("fa_bwd_noalloc", lib().fa_bwd_noalloc(ctypes.byref(a), _stream()))
     return dq, dk, dv
 
 

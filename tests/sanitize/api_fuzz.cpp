@@ -77,6 +77,7 @@ int main() {
       a.stages = int(rng() % 9) - 1;
       fa_bwd_workspace_size(&a);
       ok[2 + (fa_bwd(&a, nullptr) == FA_OK)]++;
+      fa_bwd_noalloc(&a, nullptr);
     }
     {
       fa_fwd_varlen_args a;
@@ -173,9 +174,11 @@ int main() {
       b.lse = f.lse, b.workspace = (void*)(kBase + (uintptr_t(10) << 32));
       b.workspace_bytes = fa_bwd_workspace_size(&b);
       if (fa_bwd(&b, nullptr) != FA_OK) return 3;
+      b.workspace = nullptr, b.workspace_bytes = 0;
+      if (fa_bwd_noalloc(&b, nullptr) != FA_OK) return 5;
     }
   printf("api fuzz: %ld rounds; accepted fwd %ld bwd %ld varlen %ld bwd_varlen %ld kvcache %ld mx %ld "
          "merge %ld quant %ld; valid-set launches %ld\n",
          total, ok[1], ok[3], ok[5], ok[7], ok[9], ok[11], ok[13], ok[15], g_launches - before);
-  return g_launches - before >= 8 ? 0 : 4;
+  return g_launches - before >= 12 ? 0 : 4;
 }

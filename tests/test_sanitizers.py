@@ -48,11 +48,15 @@ def test_oracle_under_sanitizers(tmp_path):
 def launch_stubs():
     """Counting stubs for every launch function fa_internal.h declares."""
     text = open(os.path.join(ROOT, "io_aware_exact_amd", "csrc", "fa_internal.h")).read()
-    decls = re.findall(r"^hipError_t\s+(launch_\w+)\s*\(([^;]*?)\)\s*;", text, flags=re.M | re.S)
+    decls = re.findall(r"^hipError_t\s+(launch_\w+|noalloc_scratch)\s*\(([^;]*?)\)\s*;", text,
+                       flags=re.M | re.S)
     assert len(decls) >= 10
     body = ['#include "fa_internal.h"', "long g_launches = 0;"]
     for name, params in decls:
-        body.append(f"hipError_t {name}({params}) {{ ++g_launches; return hipSuccess; }}")
+        if name == "noalloc_scratch":   # a fixed stand-in address, never dereferenced
+            body.append(f"hipError_t {name}({params}) {{ *ptr = (void*)0x200000000000ull; return hipSuccess; }}")
+        else:
+            body.append(f"hipError_t {name}({params}) {{ ++g_launches; return hipSuccess; }}")
     return "\n".join(body) + "\n"
 
 

@@ -290,6 +290,23 @@ def leg_fp8(reps, keep_rows=None):
     t = time_calls(lambda: fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse), reps)
     ms = t["mean"]
     ff = fwd_flops(B, S, S, H, d, False)
+    # FP8 backward on the same inputs: dO ~ N(0,1) (seed 4003), the forward's
+    # O and LSE; gradients and workspace allocated before timing
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4003)
+    dout = torch.randn((B, S, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    fa.fwd_fp8(*codes, *scales, False, out=o, lse=lse)
+    grads = tuple(torch.empty((B, S, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    a = fa.bwd_fp8_args(*codes, scales, o, dout, lse, *grads, False, None)
+    ws = torch.empty(int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a))), dtype=torch.uint8, device="cuda")
+
+    def bwd(stages=0):
+        return lambda: fa.bwd_fp8(*codes, scales, o, dout, lse, False, out=grads, workspace=ws, stages=stages)
+    tb = time_calls(bwd(), reps)
+    tb_k = {name: time_calls(bwd(st), reps) for name, st in
+            (("bwd_fp8_preprocess_kernel", fa.FA_BWD_PREPROCESS), ("bwd_dkdv_fp8_kernel", fa.FA_BWD_DKDV),
+             ("bwd_dq_fp8_kernel", fa.FA_BWD_DQ))}
+    del ws, grads, dout
     mx = [fa.quantize_mxfp8(X[0], 0), fa.quantize_mxfp8(X[1], 0), fa.quantize_mxfp8(X[2], 1)]
     o_mx = torch.empty_like(o)
     tm = time_calls(lambda: fa.fwd_mxfp8(*[c for c, _ in mx], *[s for _, s in mx], False,
@@ -312,6 +329,13 @@ def leg_fp8(reps, keep_rows=None):
     return {"workload": "fp8 e4m3 fwd B=1 H=16 S=16384 d=128 non-causal, per-block scales",
             "ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2),
             "frac_of_fp8_peak": round(ff / ms / 1e9 / PEAK_FP8_TFLOPS, 4), "timing": timing(t),
+            "bwd": {"workload": "FP8 backward (all five products on FP8 MFMA), same shape and inputs, "
+                                "dO ~ N(0,1)",
+                    "ms": round(tb["mean"], 4), "bwd_tflops": round(2.5 * ff / tb["mean"] / 1e9, 2),
+                    "fwd_bwd_tflops": round(3.5 * ff / (ms + tb["mean"]) / 1e9, 2),
+                    "fwd_bwd_frac_of_fp8_peak": round(3.5 * ff / (ms + tb["mean"]) / 1e9 / PEAK_FP8_TFLOPS, 4),
+                    "timing": timing(tb),
+                    "kernels": {k: timing(v) for k, v in tb_k.items()}},
             "mx": {"workload": "MX fp8 (E8M0 scale per 32 elements) fwd, same shape and inputs",
                    "ms": round(ms_mx, 4), "tflops": round(ff / ms_mx / 1e9, 2),
                    "frac_of_fp8_peak": round(ff / ms_mx / 1e9 / PEAK_FP8_TFLOPS, 4),

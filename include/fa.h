@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -142,11 +142,25 @@ typedef struct {
   float* lse;
 } fa_fwd_varlen_args;
 
-/* Dense backward (bf16).  Inputs: q, k, v, the forward output o, its
- * gradient dout [B,Sq,Hq,d], and the forward's lse [B,Hq,Sq].  Outputs dq
- * [B,Sq,Hq,d], dk and dv [B,Sk,Hkv,d] (bf16; for GQA, dk/dv sum over the query
- * heads of each kv head).  workspace: at least fa_bwd_workspace_size bytes,
- * 256-byte aligned.  The result is bitwise reproducible run to run.
+/* Dense backward.  Inputs: q, k, v, the forward output o, its gradient dout
+ * [B,Sq,Hq,d], and the forward's lse [B,Hq,Sq].  Outputs dq [B,Sq,Hq,d], dk
+ * and dv [B,Sk,Hkv,d] (bf16; for GQA, dk/dv sum over the query heads of each
+ * kv head).  workspace: at least fa_bwd_workspace_size bytes, 256-byte
+ * aligned.  The result is bitwise reproducible run to run.
+ *
+ * dtype FA_BF16: q, k, v, o, dout bf16.
+ * dtype FA_FP8_E4M3 (the FP8 forward's gradient; "FlashAttention-3: Fast
+ * and Accurate Attention with Asynchrony and Low-precision", summary, third
+ * contribution, carried to the backward): q, k, v are the E4M3 codes and
+ * q_descale, k_descale, v_descale the per-block fp32 scales of fa_fwd's FP8
+ * path (strides in bytes; the gradient is taken with respect to the
+ * dequantised values); o and dout are bf16.  All five products run on the
+ * FP8 matrix instruction: dO is rounded to E4M3 with one power-of-two scale
+ * per (batch, head, 128-row block) (kept in the workspace, with D computed
+ * from it), P to E4M3 after a 2^8 prescale, and dS to E4M3 with one
+ * power-of-two scale per 32 elements along each product's reduction
+ * dimension.  The workspace is then D, the dO codes [B,Hq,Sq,d] and their
+ * scales.
  *
  * stages: 0 (or FA_BWD_ALL) runs the whole backward.  Otherwise a bitmask of
  * FA_BWD_PREPROCESS (D = rowsum(dO o O) into the workspace), FA_BWD_DKDV and
@@ -168,6 +182,9 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   int32_t stages;
+  const float* q_descale;   /* FP8 only: [B,Hq,ceil(Sq/128)] */
+  const float* k_descale;   /* FP8 only: [B,Hkv,ceil(Sk/128)] */
+  const float* v_descale;   /* FP8 only: [B,Hkv,ceil(Sk/128)] */
 } fa_bwd_args;
 
 /* Packed variable-length backward (bf16), the gradient of fa_fwd_varlen.
@@ -334,15 +351,16 @@ fa_status fa_bwd(const fa_bwd_args* args, hipStream_t stream);
  * serving loops, harnesses that forbid allocation).  Arguments, checks and
  * results are fa_bwd's (bitwise the same gradients), except that
  * args->workspace and args->workspace_bytes are ignored: the scratch fa_bwd
- * keeps there (D = rowsum(dO o O), 4 bytes per query row and head, rounded
- * up to 256 bytes) lives in a fixed array of FA_BWD_NOALLOC_MAX_SCRATCH bytes
- * in the library's device code, one per GPU, held until the process ends.
- * Calls with B * Hq * Sq * 4 > FA_BWD_NOALLOC_MAX_SCRATCH (8,388,608 query
- * rows x heads) return FA_ERR_WORKSPACE.  Every call on one GPU shares that
- * GPU's array, which keeps the last call's contents: calls that overlap in
- * time on one GPU (several streams or host threads) race on it and must be
- * serialised by the caller, and a call whose stages skip FA_BWD_PREPROCESS
- * uses the D left by the previous call on that GPU.  The first call on a
+ * keeps there (fa_bwd_workspace_size bytes: D = rowsum(dO o O), 4 bytes per
+ * query row and head, rounded up to 256 bytes; for FP8 also the dO codes and
+ * scales) lives in a fixed array of FA_BWD_NOALLOC_MAX_SCRATCH bytes in the
+ * library's device code, one per GPU, held until the process ends.  Calls
+ * needing more (bf16: B * Hq * Sq > 8,388,608 query rows x heads) return
+ * FA_ERR_WORKSPACE.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap in time on one GPU
+ * (several streams or host threads) race on it and must be serialised by
+ * the caller, and a call whose stages skip FA_BWD_PREPROCESS uses the
+ * scratch left by the previous call on that GPU.  The first call on a
  * device looks up the array's address there (FA_ERR_HIP if that fails). */
 #define FA_BWD_NOALLOC_MAX_SCRATCH (32u << 20)
 fa_status fa_bwd_noalloc(const fa_bwd_args* args, hipStream_t stream);

@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "fwd.hip", "fwd_pp.hip", "fwd_f32.hip", "bwd.hip", "decode.hip", "fp8.hip",
-           "kvcache.hip", "merge.hip", "noalloc.hip"]
+           "kvcache.hip", "merge.hip", "noalloc.hip", "bwd_fp8.hip"]
 
 # Packed fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

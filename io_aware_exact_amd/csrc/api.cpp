@@ -234,15 +234,34 @@ fa_status check_varlen(const fa_fwd_varlen_args* a) {
   return FA_OK;
 }
 
-size_t bwd_delta_bytes(const fa_bwd_args* a) {
-  // saturates for impossible sizes, which the argument check rejects
-  const int64_t n = mul_sat(a->B > 0 ? a->B : 0, a->Hq > 0 ? a->Hq : 0, a->Sq > 0 ? a->Sq : 0, 4);
-  return n > kMaxExtentBytes ? (size_t)kMaxExtentBytes : align256((size_t)n);
+// Backward workspace: D = rowsum(dO o O) [B,Hq,Sq] fp32; for FP8 also the
+// E4M3 codes of dO [B,Hq,Sq,d] and their E8M0 scale bytes [B,Hq,nqb] (int32),
+// each region 256-byte aligned.  Sizes saturate for impossible shapes, which
+// the argument check rejects.
+struct BwdWorkspace {
+  size_t delta, do8, do_scale, total;
+};
+
+size_t region(int64_t n) { return n > kMaxExtentBytes ? (size_t)kMaxExtentBytes : align256((size_t)n); }
+
+BwdWorkspace bwd_workspace(const fa_bwd_args* a) {
+  const int64_t B = a->B > 0 ? a->B : 0, Hq = a->Hq > 0 ? a->Hq : 0, Sq = a->Sq > 0 ? a->Sq : 0;
+  BwdWorkspace w = {region(mul_sat(B, Hq, Sq, 4)), 0, 0, 0};
+  if (a->dtype == FA_FP8_E4M3) {
+    w.do8 = region(mul_sat(B, Hq, Sq, a->d > 0 ? a->d : 0));
+    w.do_scale = region(mul_sat(B, Hq, (Sq + 127) / 128, 4));
+  }
+  w.total = w.delta + w.do8 + w.do_scale;
+  return w;
 }
+
+size_t bwd_delta_bytes(const fa_bwd_args* a) { return bwd_workspace(a).total; }
 
 fa_status check_bwd(const fa_bwd_args* a) {
   if (!a) return FA_ERR_NULL;
-  if (a->dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (a->dtype != FA_BF16 && a->dtype != FA_FP8_E4M3) return FA_ERR_DTYPE;
+  const bool fp8 = a->dtype == FA_FP8_E4M3;
+  const int64_t es = fp8 ? 1 : 2;   // bytes per q, k, v element
   if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1) return FA_ERR_SHAPE;
   if (a->d != 64 && a->d != 128) return FA_ERR_HEADDIM;
   if (a->Hq % a->Hkv != 0) return FA_ERR_GQA;
@@ -255,27 +274,36 @@ fa_status check_bwd(const fa_bwd_args* a) {
   for (int i = 0; i < 8; ++i)
     if (!ts[i]->ptr && (is_q_side[i] ? q_side : k_side)) return FA_ERR_NULL;
   if (!a->lse && q_side) return FA_ERR_NULL;
+  if (fp8 && ((q_side && !a->q_descale) || (k_side && (!a->k_descale || !a->v_descale)))) return FA_ERR_NULL;
   for (int i = 0; i < 8; ++i)
-    if (!aligned16(ts[i]->ptr) || !strides_ok(*ts[i], 8)) return FA_ERR_ALIGN;
+    if (!aligned16(ts[i]->ptr) || !strides_ok(*ts[i], i < 3 ? 16 / es : 8)) return FA_ERR_ALIGN;
   if ((uintptr_t)a->lse & 3u) return FA_ERR_ALIGN;
+  if (fp8 && (((uintptr_t)a->q_descale & 3u) || ((uintptr_t)a->k_descale & 3u) ||
+              ((uintptr_t)a->v_descale & 3u)))
+    return FA_ERR_ALIGN;
   const int64_t B = a->B, Sq = a->Sq, Sk = a->Sk, Hq = a->Hq, Hkv = a->Hkv, d = a->d;
   if (mul_sat((Sq + 127) / 128, Hq, B) > 0x7fffffffLL || mul_sat((Sk + 127) / 128, Hkv, B) > 0x7fffffffLL)
     return FA_ERR_SHAPE;
   if (mul_sat(B, Sq, Hq) > 0x7fffffffLL * 16) return FA_ERR_SHAPE;
-  if (!fits32(Sq, a->q.stride_s, 2) || !fits32(Sq, a->dout.stride_s, 2) ||
-      !fits32(Sk, a->k.stride_s, 2) || !fits32(Sk, a->v.stride_s, 2))
+  if (!fits32(Sq, a->q.stride_s, es) || !fits32(Sq, a->dout.stride_s, 2) ||
+      !fits32(Sk, a->k.stride_s, es) || !fits32(Sk, a->v.stride_s, es))
     return FA_ERR_SHAPE;
+  if (fp8 && !fits32(Sq, d, 1)) return FA_ERR_SHAPE;   // one head's dO codes in the workspace
   const size_t need = bwd_delta_bytes(a);
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return FA_ERR_WORKSPACE;
   if ((uintptr_t)a->workspace & 255u) return FA_ERR_ALIGN;
   // outputs must not overlap each other, the inputs or the workspace
-  const Span in[6] = {
-      span4(a->q.ptr, B, Sq, Hq, d, a->q.stride_b, a->q.stride_s, a->q.stride_h, 2),
-      span4(a->k.ptr, B, Sk, Hkv, d, a->k.stride_b, a->k.stride_s, a->k.stride_h, 2),
-      span4(a->v.ptr, B, Sk, Hkv, d, a->v.stride_b, a->v.stride_s, a->v.stride_h, 2),
+  const int64_t nqb = (Sq + 127) / 128, nkb = (Sk + 127) / 128;
+  const Span in[9] = {
+      span4(a->q.ptr, B, Sq, Hq, d, a->q.stride_b, a->q.stride_s, a->q.stride_h, es),
+      span4(a->k.ptr, B, Sk, Hkv, d, a->k.stride_b, a->k.stride_s, a->k.stride_h, es),
+      span4(a->v.ptr, B, Sk, Hkv, d, a->v.stride_b, a->v.stride_s, a->v.stride_h, es),
       span4(a->o.ptr, B, Sq, Hq, d, a->o.stride_b, a->o.stride_s, a->o.stride_h, 2),
       span4(a->dout.ptr, B, Sq, Hq, d, a->dout.stride_b, a->dout.stride_s, a->dout.stride_h, 2),
-      lin(a->lse, mul_sat(B, Hq, Sq), 4)};
+      lin(a->lse, mul_sat(B, Hq, Sq), 4),
+      fp8 ? lin(a->q_descale, mul_sat(B, Hq, nqb), 4) : empty_span(nullptr),
+      fp8 ? lin(a->k_descale, mul_sat(B, Hkv, nkb), 4) : empty_span(nullptr),
+      fp8 ? lin(a->v_descale, mul_sat(B, Hkv, nkb), 4) : empty_span(nullptr)};
   const Span out[4] = {
       span4(a->dq.ptr, B, Sq, Hq, d, a->dq.stride_b, a->dq.stride_s, a->dq.stride_h, 2),
       span4(a->dk.ptr, B, Sk, Hkv, d, a->dk.stride_b, a->dk.stride_s, a->dk.stride_h, 2),
@@ -283,7 +311,7 @@ fa_status check_bwd(const fa_bwd_args* a) {
       lin(a->workspace, (int64_t)need, 1)};
   if (any_bad(in) || any_bad(out)) return FA_ERR_SHAPE;
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 9; ++j)
       if (overlap(out[i], in[j])) return FA_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
       if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
@@ -618,6 +646,15 @@ fa_status fa_bwd(const fa_bwd_args* a, hipStream_t stream) {
   p.scale = a->softmax_scale;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
   const int stages = a->stages == FA_BWD_ALL ? (FA_BWD_PREPROCESS | FA_BWD_DKDV | FA_BWD_DQ) : a->stages;
+  if (a->dtype == FA_FP8_E4M3) {
+    const BwdWorkspace w = bwd_workspace(a);
+    p.q_descale = a->q_descale;
+    p.k_descale = a->k_descale;
+    p.v_descale = a->v_descale;
+    p.do8 = (uint8_t*)a->workspace + w.delta;
+    p.do_e8m0 = (int*)((char*)a->workspace + w.delta + w.do8);
+    return hip_status(launch_bwd_fp8(p, a->d, a->causal != 0, stages, stream));
+  }
   return hip_status(launch_bwd_bf16(p, a->d, a->causal != 0, false, stages, stream));
 }
 

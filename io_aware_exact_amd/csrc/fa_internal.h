@@ -77,6 +77,15 @@ struct BwdParams {
   int causal;
   float scale;
   float scale_log2;
+  // FP8 backward only: per-block fp32 scales of the E4M3 q, k, v codes
+  // ([B,Hq,ceil(Sq/128)], [B,Hkv,ceil(Sk/128)]), and the workspace's
+  // quantised dO: codes [B,Hq,Sq,d] and one power-of-two scale per
+  // (batch, head, 128-row block) stored as its E8M0 byte [B,Hq,ceil(Sq/128)]
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  uint8_t* do8;
+  int* do_e8m0;
 };
 
 // Split-KV decode: partial results per (row, split) in the caller's workspace.
@@ -149,6 +158,7 @@ hipError_t launch_fwd_bf16_pp_kvcache(const FwdParams& p, int d, bool causal, hi
 hipError_t launch_kv_append(const KvAppendParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool varlen, int stages,
                            hipStream_t stream);
+hipError_t launch_bwd_fp8(const BwdParams& p, int d, bool causal, int stages, hipStream_t stream);
 // Zero a bf16 [B,S,H,d] tensor with element strides (d contiguous).
 hipError_t launch_zero_bf16(void* ptr, int64_t B, int64_t S, int64_t H, int64_t d, int64_t sb,
                             int64_t ss, int64_t sh, hipStream_t stream);

@@ -68,7 +68,9 @@ class BwdArgs(ctypes.Structure):
                 ("q", FaTensor), ("k", FaTensor), ("v", FaTensor), ("o", FaTensor),
                 ("dout", FaTensor), ("dq", FaTensor), ("dk", FaTensor), ("dv", FaTensor),
                 ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stages", ctypes.c_int32)]
+                ("workspace_bytes", ctypes.c_size_t), ("stages", ctypes.c_int32),
+                ("q_descale", ctypes.c_void_p), ("k_descale", ctypes.c_void_p),
+                ("v_descale", ctypes.c_void_p)]
 
 
 class BwdVarlenArgs(ctypes.Structure):
@@ -459,6 +461,56 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, out=None, workspace=Non
         nbytes = lib().fa_bwd_workspace_size(ctypes.byref(a))
         workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q.device)
     a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, workspace, stages)
+    _check("fa_bwd", lib().fa_bwd(ctypes.byref(a), _stream()))
+    return dq, dk, dv
+
+
+def bwd_fp8_args(q8, k8, v8, descales, o, dout, lse, dq, dk, dv, causal, scale, workspace=None,
+                 stages=0):
+    """fa_bwd_args for the FP8 backward: E4M3 codes q8 [B,Sq,Hq,d], k8/v8
+    [B,Sk,Hkv,d] with the forward's fp32 block scales (q, k, v descales);
+    o, dout and the gradients bf16."""
+    _check_fp8_codes(q8, k8, v8)
+    B, Sq, Hq, d = q8.shape
+    Sk, Hkv = k8.shape[1], k8.shape[2]
+    q_descale, k_descale, v_descale = descales
+    _lse("q_descale", q_descale, (B, Hq, (Sq + 127) // 128))
+    _lse("k_descale", k_descale, (B, Hkv, (Sk + 127) // 128))
+    _lse("v_descale", v_descale, (B, Hkv, (Sk + 127) // 128))
+    for name, t, shape in (("o", o, q8.shape), ("dout", dout, q8.shape), ("dq", dq, q8.shape),
+                           ("dk", dk, k8.shape), ("dv", dv, k8.shape)):
+        _shape(name, t, shape, torch.bfloat16)
+    _lse("lse", lse, (B, Hq, Sq))
+    _workspace(workspace)
+    _on_device(q8.device, q8=q8, k8=k8, v8=v8, q_descale=q_descale, k_descale=k_descale,
+               v_descale=v_descale, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    a = BwdArgs(FA_FP8_E4M3, B, Sq, Sk, Hq, Hkv, d, int(bool(causal)), _scale(d, scale),
+                _t4(q8), _t4(k8), _t4(v8), _t4(o), _t4(dout), _t4(dq), _t4(dk), _t4(dv),
+                lse.data_ptr(), ws_ptr, ws_bytes, int(stages))
+    a.q_descale, a.k_descale, a.v_descale = (q_descale.data_ptr(), k_descale.data_ptr(),
+                                             v_descale.data_ptr())
+    return a
+
+
+def bwd_fp8(q8, k8, v8, descales, o, dout, lse, causal=False, scale=None, out=None,
+            workspace=None, stages=0):
+    """FP8 backward (the gradient of fwd_fp8 with respect to the dequantised
+    q, k, v): all five products on FP8 matrix instructions.  descales =
+    (q_descale, k_descale, v_descale) as for fwd_fp8; o, dout bf16, lse from
+    the forward.  Returns (dq, dk, dv) bf16."""
+    B, Sq, Hq, d = q8.shape
+    if out is None:
+        out = (torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device),
+               torch.empty(k8.shape, dtype=torch.bfloat16, device=k8.device),
+               torch.empty(v8.shape, dtype=torch.bfloat16, device=v8.device))
+    dq, dk, dv = out
+    if workspace is None:
+        a = bwd_fp8_args(q8, k8, v8, descales, o, dout, lse, dq, dk, dv, causal, scale)
+        nbytes = lib().fa_bwd_workspace_size(ctypes.byref(a))
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=q8.device)
+    a = bwd_fp8_args(q8, k8, v8, descales, o, dout, lse, dq, dk, dv, causal, scale, workspace, stages)
     _check("fa_bwd", lib().fa_bwd(ctypes.byref(a), _stream()))
     return dq, dk, dv
 

@@ -75,6 +75,7 @@ int main() {
       a.dq = tensor(), a.dk = tensor(), a.dv = tensor();
       a.lse = (const float*)ptr(), a.workspace = (void*)ptr(), a.workspace_bytes = size_t(pick(kStride));
       a.stages = int(rng() % 9) - 1;
+      a.q_descale = (const float*)ptr(), a.k_descale = (const float*)ptr(), a.v_descale = (const float*)ptr();
       fa_bwd_workspace_size(&a);
       ok[2 + (fa_bwd(&a, nullptr) == FA_OK)]++;
       fa_bwd_noalloc(&a, nullptr);
@@ -176,9 +177,20 @@ int main() {
       if (fa_bwd(&b, nullptr) != FA_OK) return 3;
       b.workspace = nullptr, b.workspace_bytes = 0;
       if (fa_bwd_noalloc(&b, nullptr) != FA_OK) return 5;
+      // the FP8 backward: e4m3 q, k, v (strides in bytes) with block scales
+      fa_bwd_args c = b;
+      c.dtype = FA_FP8_E4M3;
+      c.q = dense(11, 300, 8, d), c.k = dense(12, 500, 2, d), c.v = dense(13, 500, 2, d);
+      c.q_descale = (const float*)(kBase + (uintptr_t(14) << 32));
+      c.k_descale = (const float*)(kBase + (uintptr_t(15) << 32));
+      c.v_descale = (const float*)(kBase + (uintptr_t(16) << 32));
+      c.workspace = (void*)(kBase + (uintptr_t(17) << 32));
+      c.workspace_bytes = fa_bwd_workspace_size(&c);
+      if (c.workspace_bytes <= fa_bwd_workspace_size(&b)) return 6;
+      if (fa_bwd(&c, nullptr) != FA_OK) return 7;
     }
   printf("api fuzz: %ld rounds; accepted fwd %ld bwd %ld varlen %ld bwd_varlen %ld kvcache %ld mx %ld "
          "merge %ld quant %ld; valid-set launches %ld\n",
          total, ok[1], ok[3], ok[5], ok[7], ok[9], ok[11], ok[13], ok[15], g_launches - before);
-  return g_launches - before >= 12 ? 0 : 4;
+  return g_launches - before >= 16 ? 0 : 4;
 }

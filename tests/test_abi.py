@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = fa.lib()
-    assert L.fa_abi_version() == 1
+    assert L.fa_abi_version() == 2
     assert L.fa_status_string(0) == b"ok"
     assert b"head dimension" in L.fa_status_string(3)
 
@@ -308,3 +308,27 @@ def test_fwd_rejects_slices_beyond_32bit_offsets():
                           FAKE + (3 << 40), None, None, None, None, 0)
     assert fa.lib().fa_fwd(ctypes.byref(args(65300, FAKE + 64)), None) == 2
     assert fa.lib().fa_fwd(ctypes.byref(args(65270, FAKE + 64)), None) == 8
+
+
+def test_fp8_bwd_rejects_and_workspace():
+    """FP8 backward: descale arrays are required, q/k/v strides are in bytes
+    (16-byte rows), and the workspace adds the dO codes and their scales."""
+    d, S, H = 64, 16, 2
+    def args(dtype=2, **kw):
+        t8 = fa.FaTensor(FAKE, S * H * d, H * d, d)
+        t16 = lambda i: fa.FaTensor(FAKE + (i << 24), S * H * d, H * d, d)
+        a = fa.BwdArgs(dtype, 1, S, S, H, H, d, 0, 0.125, t8, fa.FaTensor(FAKE + (1 << 24), S * H * d, H * d, d),
+                       fa.FaTensor(FAKE + (2 << 24), S * H * d, H * d, d), t16(3), t16(4), t16(5), t16(6), t16(7),
+                       FAKE + (8 << 24), FAKE + (9 << 24), 1 << 20, 0)
+        a.q_descale = kw.get("qd", FAKE + (10 << 24))
+        a.k_descale = kw.get("kd", FAKE + (11 << 24))
+        a.v_descale = kw.get("vd", FAKE + (12 << 24))
+        return a
+    L = fa.lib()
+    assert L.fa_bwd(ctypes.byref(args(qd=None)), None) == 1
+    assert L.fa_bwd(ctypes.byref(args(vd=None)), None) == 1
+    assert L.fa_bwd(ctypes.byref(args(kd=FAKE + (11 << 24) + 2)), None) == 6
+    assert L.fa_bwd(ctypes.byref(args(dtype=1)), None) == 4
+    # D [1,2,16] fp32 (256 B) + codes [1,2,16,64] (2 KiB) + scales [1,2,1] int32 (256 B)
+    assert L.fa_bwd_workspace_size(ctypes.byref(args())) == 256 + 2048 + 256
+    assert L.fa_bwd_workspace_size(ctypes.byref(args(dtype=0))) == 256

@@ -1,0 +1,269 @@
+"""GPU parity of the FP8 backward (fa_bwd with FA_FP8_E4M3) against the fp64
+oracle's gradients on the dequantised inputs.
+
+The kernel rounds three operands to E4M3 that the oracle keeps exact: dO
+(one power-of-two scale per (batch, head, 128-row block)), P (after a 2^8
+prescale) and dS (one power-of-two scale per 32 elements along the
+reduction).  Which codes result depends on values the oracle never forms,
+so the exact gradients are not a plain definition it can reproduce; they
+are bounded instead, element by element, by what those roundings can do,
+with every term computed in fp64 from the oracle's inputs:
+  * dO: |d dO_ic| <= 2^-4 |dO_ic| + 2^-10 * 2^e_I (half a subnormal step of
+    its block, 2^e_I the block scale);
+  * scores: the FP8 instruction's dot product is within
+    eps_ij = 2^-11 scale sum_c |q_ic k_jc| (plus fp32 rounding of the exp2
+    argument), so the kernel's P_ij is within a factor exp(+-eps_ij); the P
+    the dS side uses passes through bf16 (2^-9);
+  * dP = dO V^T and D = rowsum(dO o O) inherit the dO error (the instruction's
+    own summation adds 2^-11 of sum |dO||v|; the bf16 O passed in 2^-9);
+  * dS = P (dP - D) is then within
+        E_ij = P_ij (|d dP_ij| + |d D_i|) + |dS_ij| (e^eps_ij - 1 + 2^-8),
+    and its E4M3 rounding adds 2^-4 (|dS_ij| + E_ij) plus half a subnormal
+    step of its 32-element block, at most 2^-10 * max_block(|dS| + E) / 224;
+  * dK = scale dS^T Q and dQ = scale dS K sum those errors with |q| or |k|,
+    dV = P^T dO sums the P rounding (2^-4 P + min(P, 2^-18)) and the dO
+    rounding, each product adds 2^-11 of its sum of magnitudes and the bf16
+    output 2^-9 of the value.
+The relative L2 error of each gradient is also held to 6e-2: a CPU
+simulation of these roundings gives 0.035-0.041 (S = 512..2048, d = 64 and
+128, with and without the causal mask).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+from io_aware_exact_amd import fa, inputs
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_L2 = 6e-2
+
+
+def do_steps(g):
+    """2^e per row of one head's dO [S, d]: the smallest power of two with
+    amax <= 448 * 2^e over each 128-row block (zero block: 1)."""
+    S = g.shape[0]
+    steps = np.ones(S)
+    for r0 in range(0, S, 128):
+        e = ofp8.mx_exponent(np.abs(g[r0:r0 + 128]).max())
+        steps[r0:r0 + 128] = 2.0 ** float(np.clip(e, -126, 126))
+    return steps
+
+
+def block_max(m, axis):
+    """Maximum over aligned 32-element blocks along `axis`, broadcast back."""
+    n = m.shape[axis]
+    pad = (-n) % 32
+    mm = np.moveaxis(m, axis, -1)
+    if pad:
+        mm = np.concatenate([mm, np.zeros(mm.shape[:-1] + (pad,))], axis=-1)
+    bm = mm.reshape(mm.shape[:-1] + (-1, 32)).max(axis=-1)
+    out = np.repeat(bm, 32, axis=-1)[..., :n]
+    return np.moveaxis(out, -1, axis)
+
+
+def head_bounds(q, k, v, g, O, lse, scale, causal, chunk=1024):
+    """Element-wise bounds on |kernel - exact| of dQ (this head's rows) and
+    the contributions of this query head to dK and dV (see the module
+    docstring).  q, g, O [Sq, d]; k, v [Sk, d]; lse [Sq]; float64."""
+    Sq, d = q.shape
+    Sk = k.shape[0]
+    aq, ak, av, ag, aO = np.abs(q), np.abs(k), np.abs(v), np.abs(g), np.abs(O)
+    delta = 2.0 ** -4 * ag + 2.0 ** -10 * do_steps(g)[:, None]
+    bq = np.zeros((Sq, d))
+    bk = np.zeros((Sk, d))
+    bv = np.zeros((Sk, d))
+    for r0 in range(0, Sq, chunk):
+        r = slice(r0, min(Sq, r0 + chunk))
+        rows = np.arange(r0, min(Sq, r0 + chunk))
+        s = scale * (q[r] @ k.T)
+        with np.errstate(invalid="ignore", over="ignore"):
+            P = np.exp(s - lse[r][:, None])
+        if causal:
+            P[np.arange(Sk)[None, :] > (rows + Sk - Sq)[:, None]] = 0.0
+        P[~np.isfinite(lse[r])] = 0.0
+        P = np.nan_to_num(P, nan=0.0, posinf=0.0)
+        lfin = np.where(np.isfinite(lse[r]), np.abs(lse[r]), 0.0)
+        eps = 2.0 ** -11 * scale * (aq[r] @ ak.T) + 2.0 ** -22 * (np.abs(s) + lfin[:, None])
+        ee = np.expm1(eps)
+        dP = g[r] @ v.T
+        D = (g[r] * O[r]).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        ddP = delta[r] @ av.T + 2.0 ** -11 * (1 + 2.0 ** -4) * (ag[r] @ av.T)
+        dD = (delta[r] * aO[r]).sum(axis=1) + 2.0 ** -9 * (ag[r] * aO[r]).sum(axis=1)
+        E = P * (ddP + dD[:, None]) + np.abs(dS) * (ee + 2.0 ** -8)
+        M = np.abs(dS) + E
+        # dK: dS quantised in blocks of 32 query rows per key
+        QK = (1 + 2.0 ** -4) * E + 2.0 ** -4 * np.abs(dS) + 2.0 ** -10 * block_max(M, 0) / 224
+        bk += scale * (QK.T @ aq[r] + 2.0 ** -11 * ((M + QK).T @ aq[r]))
+        # dQ: dS quantised in blocks of 32 keys per query row
+        QQ = (1 + 2.0 ** -4) * E + 2.0 ** -4 * np.abs(dS) + 2.0 ** -10 * block_max(M, 1) / 224
+        bq[r] = scale * (QQ @ ak + 2.0 ** -11 * ((M + QQ) @ ak))
+        # dV: P rounded to E4M3 (2^8 p), dO rounded
+        Pt = P * np.exp(eps)
+        dP8 = P * ee + 2.0 ** -4 * Pt + np.minimum(Pt, 2.0 ** -18)
+        gd = ag[r] + delta[r]
+        bv += dP8.T @ gd + P.T @ delta[r] + 2.0 ** -11 * (1 + 2.0 ** -4) * (Pt.T @ gd)
+    return bq, bk, bv
+
+
+def check_fp8_grad(name, got, ref, bound):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert np.isfinite(got).all(), name
+    bound = bound + 2.0 ** -9 * np.abs(ref) + 1e-5
+    err = np.abs(got - ref)
+    worst = float((err / bound).max(initial=0.0))
+    nref = np.linalg.norm(ref)
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got))
+    print(f"  {name}: max_abs={float(err.max(initial=0)):.3e} rel_l2={rel:.3e} worst err/bound={worst:.3f}",
+          flush=True)
+    assert worst <= 1.0, (name, worst)
+    assert rel <= GRAD_REL_L2 or nref == 0, (name, rel)
+    return rel
+
+
+def quantised_inputs(B, Sq, Sk, Hq, Hkv, d, seed):
+    xs = [inputs.outlier_normal(s, seed + i) for i, s in
+          enumerate([(B, Sq, Hq, d), (B, Sk, Hkv, d), (B, Sk, Hkv, d)])]
+    q8 = [fa.quantize_fp8(x.cuda()) for x in xs]
+    deq = [ofp8.dequantize_blocks(c.cpu().numpy(), s.cpu().numpy()) for c, s in q8]
+    g = torch.Generator().manual_seed(seed + 7)
+    dout = torch.randn((B, Sq, Hq, d), generator=g).to(torch.bfloat16)
+    return q8, deq, dout
+
+
+def run_fp8_bwd(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None, heads=None):
+    print(f"fp8 bwd B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}",
+          flush=True)
+    ((qc, qs), (kc, ks), (vc, vs)), (Q, K, V), dout = quantised_inputs(B, Sq, Sk, Hq, Hkv, d, seed)
+    sc = 1.0 / np.sqrt(d) if scale is None else scale
+    grp = Hq // Hkv
+    # the forward's O (bf16) and LSE, from the oracle, so that the check sees
+    # the backward's own rounding
+    o_ref, lse_ref = oracle.attention_fwd(Q, K, V, causal, scale)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_ref.astype(np.float32))
+    dq, dk, dv = fa.bwd_fp8(qc, kc, vc, (qs, ks, vs), o.cuda(), dout.cuda(), lse.cuda(), causal, scale)
+    torch.cuda.synchronize()
+    _, _, dq_r, dk_r, dv_r = oracle.attention_bwd(Q, K, V, dout, causal, scale)
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    On = o.double().numpy()
+    gn = dout.double().numpy()
+    for b in range(B):
+        for kvh in range(Hkv):
+            if heads is not None and (b, kvh) not in heads:
+                continue
+            bk = np.zeros((Sk, d))
+            bv = np.zeros((Sk, d))
+            for h in range(kvh * grp, (kvh + 1) * grp):
+                bq_h, bk_h, bv_h = head_bounds(Q[b, :, h], K[b, :, kvh], V[b, :, kvh], gn[b, :, h],
+                                               On[b, :, h], lse_ref[b, h], sc, causal)
+                bk += bk_h
+                bv += bv_h
+                check_fp8_grad(f"dQ[{b},{h}]", dq[b, :, h], dq_r[b, :, h], bq_h)
+            check_fp8_grad(f"dK[{b},{kvh}]", dk[b, :, kvh], dk_r[b, :, kvh], bk)
+            check_fp8_grad(f"dV[{b},{kvh}]", dv[b, :, kvh], dv_r[b, :, kvh], bv)
+    if heads is None:
+        for name, x, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+            n = np.linalg.norm(r)
+            if n > 0:
+                assert np.linalg.norm(x - r) / n <= GRAD_REL_L2, name
+
+
+@pytest.mark.parametrize("shape", [(1, 256, 256, 2, 2, 64), (2, 300, 300, 4, 2, 128),
+                                   (1, 129, 500, 2, 1, 128), (1, 700, 200, 2, 2, 64),
+                                   (1, 1, 130, 4, 4, 128), (1, 200, 333, 8, 2, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_bwd(shape, causal):
+    B, Sq, Sk, Hq, Hkv, d = shape
+    run_fp8_bwd(B, Sq, Sk, Hq, Hkv, d, causal, seed=900 + sum(shape))
+
+
+def test_fp8_bwd_scale():
+    run_fp8_bwd(1, 190, 190, 2, 2, 128, True, seed=91, scale=0.05)
+
+
+def test_fp8_bwd_deterministic():
+    """Three runs into NaN-filled outputs are bitwise equal (fixed-order
+    sums, no atomics)."""
+    (qc, qs), (kc, ks), (vc, vs) = quantised_inputs(1, 600, 600, 4, 2, 128, 92)[0]
+    o, lse = fa.fwd_fp8(qc, kc, vc, qs, ks, vs, True)
+    dout = torch.randn(o.shape, device="cuda").to(torch.bfloat16)
+    runs = []
+    for _ in range(3):
+        out = tuple(torch.full(x.shape, float("nan"), dtype=torch.bfloat16, device="cuda") for x in (qc, kc, vc))
+        runs.append(fa.bwd_fp8(qc, kc, vc, (qs, ks, vs), o, dout, lse, True, out=out))
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for x, y in zip(r, runs[0]):
+            assert torch.equal(x, y)
+
+
+def test_fp8_bwd_pipeline_and_stages():
+    """fwd_fp8 then bwd_fp8 (the FP8 forward's own O and LSE): the gradients
+    stay within the relative bar of the oracle's; running the three stages as
+    separate calls equals one call bitwise."""
+    B, S, H, d = 1, 384, 2, 128
+    ((qc, qs), (kc, ks), (vc, vs)), (Q, K, V), dout = quantised_inputs(B, S, S, H, H, d, 93)
+    o, lse = fa.fwd_fp8(qc, kc, vc, qs, ks, vs, False)
+    full = fa.bwd_fp8(qc, kc, vc, (qs, ks, vs), o, dout.cuda(), lse, False)
+    out = tuple(torch.full_like(x, float("nan")) for x in full)
+    a = fa.bwd_fp8_args(qc, kc, vc, (qs, ks, vs), o, dout.cuda(), lse, *out, False, None)
+    import ctypes
+    ws = torch.empty(int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a))), dtype=torch.uint8, device="cuda")
+    for st in (fa.FA_BWD_PREPROCESS, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.bwd_fp8(qc, kc, vc, (qs, ks, vs), o, dout.cuda(), lse, False, out=out, workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    for x, y in zip(out, full):
+        assert torch.equal(x, y)
+    _, _, dq_r, dk_r, dv_r = oracle.attention_bwd(Q, K, V, dout, False)
+    for name, x, r in (("dQ", full[0], dq_r), ("dK", full[1], dk_r), ("dV", full[2], dv_r)):
+        rel = float(np.linalg.norm(x.float().cpu().numpy() - r) / np.linalg.norm(r))
+        print(f"  pipeline {name}: rel_l2={rel:.3e}", flush=True)
+        assert rel <= GRAD_REL_L2
+
+
+def test_fp8_bwd_full_size():
+    """B=2, H=16, S=8192, d=128, non-causal (the fwd+bwd workload's shape)
+    with the FP8 workload's inputs: three runs bitwise equal, and the oracle
+    on (batch, head) = (0, 0) and (1, 15) with the element-wise bound."""
+    B, S, H, d = 2, 8192, 16, 128
+    print("fp8 bwd full size", flush=True)
+    X = [inputs.outlier_normal((B, S, H, d), 4000 + i, device="cuda") for i in range(3)]
+    (qc, qs), (kc, ks), (vc, vs) = [fa.quantize_fp8(x) for x in X]
+    del X
+    g = torch.Generator(device="cuda").manual_seed(4003)
+    dout = torch.randn((B, S, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    o, lse = fa.fwd_fp8(qc, kc, vc, qs, ks, vs, False)
+    runs = [fa.bwd_fp8(qc, kc, vc, (qs, ks, vs), o, dout, lse, False) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for x, y in zip(r, runs[0]):
+            assert torch.equal(x, y)
+    dq, dk, dv = runs[0]
+    for b, h in ((0, 0), (1, 15)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        Q = ofp8.dequantize_blocks(qc[sl].cpu().numpy(), qs[b:b + 1, h:h + 1].cpu().numpy())
+        K = ofp8.dequantize_blocks(kc[sl].cpu().numpy(), ks[b:b + 1, h:h + 1].cpu().numpy())
+        V = ofp8.dequantize_blocks(vc[sl].cpu().numpy(), vs[b:b + 1, h:h + 1].cpu().numpy())
+        gn = dout[sl].cpu()
+        _, _, dq_r, dk_r, dv_r = oracle.attention_bwd(Q, K, V, gn, False)
+        # bound with the O and LSE the kernel was given (the FP8 forward's)
+        On = o[sl].double().cpu().numpy()[0, :, 0]
+        ln = lse[b, h].double().cpu().numpy()
+        bq, bk, bv = head_bounds(Q[0, :, 0], K[0, :, 0], V[0, :, 0], gn.double().numpy()[0, :, 0], On, ln,
+                                 1.0 / np.sqrt(d), False)
+        # the forward's own O and LSE errors move D and P: bounded through
+        # the relative bar only; the element-wise bound covers the backward
+        rels = []
+        for name, x, r, bd in (("dQ", dq, dq_r, bq), ("dK", dk, dk_r, bk), ("dV", dv, dv_r, bv)):
+            xn = x[sl].float().cpu().numpy()[0, :, 0]
+            rn = r[0, :, 0]
+            rel = float(np.linalg.norm(xn - rn) / np.linalg.norm(rn))
+            err = np.abs(xn - rn)
+            print(f"  {name}[{b},{h}]: rel_l2={rel:.3e} max_abs={err.max():.3e} "
+                  f"worst err/bound={float((err / (bd + 2.0 ** -9 * np.abs(rn) + 1e-5)).max()):.3f}", flush=True)
+            rels.append(rel)
+        assert max(rels) <= GRAD_REL_L2, rels

@@ -20,6 +20,8 @@
 //     2t+1.
 // Operand layouts, the transposed score orientation, lazy rescaling and
 // masking are those of the one-group forward kernel.
+#include <type_traits>
+
 #include "device_common.h"
 #include "fa_internal.h"
 
@@ -29,10 +31,12 @@ constexpr int BM = 256;
 constexpr int BN = 64;
 constexpr int NT = 512;
 
-template <int D>
+// DMA: K and V tiles go from HBM straight into swizzled LDS stages (swz in
+// device_common.h, no padding); otherwise through registers into padded rows.
+template <int D, bool DMA>
 struct PpTile {
-  static constexpr int KSTR = D + 8;    // K rows: 16 rows x 16 bytes per 16 lanes
-  static constexpr int VSTR = D + 32;   // V rows: read transposed, 4 rows x 64 bytes
+  static constexpr int KSTR = DMA ? D : D + 8;    // K rows: 16 rows x 16 bytes per 16 lanes
+  static constexpr int VSTR = DMA ? D : D + 32;   // V rows: read transposed, 4 rows x 64 bytes
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
   static constexpr int CH = D / 8;
@@ -40,15 +44,20 @@ struct PpTile {
   static constexpr int NP = BN / RPP;
   static constexpr int KSTAGE = BN * KSTR;
   static constexpr int VSTAGE = BN * VSTR;
-  static constexpr int LDS_ELEMS = 2 * (KSTAGE + VSTAGE);
 };
 
-// Workgroup barrier that the instruction scheduler may not move work across:
-// register-only work (the exponentials) would otherwise drift into the
-// neighbouring phase and the two groups would no longer alternate.
+// Workgroup barrier between phases.  The instruction scheduler may not move
+// work across it: register-only work (the exponentials) would otherwise
+// drift into the neighbouring phase and the two groups would no longer
+// alternate.  It waits for this wave's LDS accesses only, not for loads in
+// flight (a fenced barrier would also wait for the LDS DMAs issued in the
+// phase); tiles that must have landed are waited for explicitly.
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -57,8 +66,16 @@ __device__ __forceinline__ void phase_barrier() {
 // (each layout its own instance, which folds away the paths it cannot take)
 template <int D, bool CAUSAL, bool VARLEN, int KVC>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
-  using T = PpTile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
+  // dense and packed tensors: tiles by LDS DMA; KV caches (whose small pages
+  // need a page per row) through registers
+  constexpr bool DMA = KVC == 0;
+  using T = PpTile<D, DMA>;
+  // one array per stage: the compiler then knows that a DMA into one stage
+  // does not write the others, and makes reads of the others wait for it
+  __shared__ __attribute__((aligned(16))) __bf16 ks0[T::KSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 ks1[T::KSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 vs0[T::VSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 vs1[T::VSTAGE];
 
   // Dense: consecutive query tiles of one head share an XCD.  Packed
   // sequences: runs of query tiles of the query heads of one (sequence, kv
@@ -134,8 +151,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   const uint32_t koff = (uint32_t)(lrow * p.k_ss + lcol) * 2;
   const uint32_t voff = (uint32_t)(lrow * p.v_ss + lcol) * 2;
   u32x4 kreg[T::NP], vreg[T::NP];
-  auto kstage = [&](int st) { return smem + st * T::KSTAGE; };
-  auto vstage = [&](int st) { return smem + 2 * T::KSTAGE + st * T::VSTAGE; };
+  // stages are chosen at compile time (St: std::integral_constant)
+  auto kstage = [&](auto St) -> __bf16* { return decltype(St)::value ? ks1 : ks0; };
+  auto vstage = [&](auto St) -> __bf16* { return decltype(St)::value ? vs1 : vs0; };
   // KV cache.  Without a block table the sequence's cache is one dense
   // region, read like the dense path.  With pages of >= 64 tokens a tile (64
   // keys from a multiple of 64) lies in one page, found in a window of
@@ -184,18 +202,55 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       for (int u = 0; u < T::NP; ++u) regs[u] = buf_load16(rd, off + (uint32_t)(j0 + u * T::RPP) * (uint32_t)ss * 2);
     }
   };
-  auto gload_k = [&](int j0) { gload_one(kreg, KVC ? rkc : rk, koff, kb, p.kv.k_sp, p.k_ss, j0); };
-  auto gload_v = [&](int j0) { gload_one(vreg, KVC ? rvc : rv, voff, vb, p.kv.v_sp, p.v_ss, j0); };
-  auto lstore_k = [&](int st) {
+  auto gload_k = [&](int j0) __attribute__((always_inline)) { gload_one(kreg, KVC ? rkc : rk, koff, kb, p.kv.k_sp, p.k_ss, j0); };
+  auto gload_v = [&](int j0) __attribute__((always_inline)) { gload_one(vreg, KVC ? rvc : rv, voff, vb, p.kv.v_sp, p.v_ss, j0); };
+  auto lstore_k = [&](auto st) __attribute__((always_inline)) {
     __bf16* Ks = kstage(st);
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) *(u32x4*)(Ks + (lrow + u * T::RPP) * T::KSTR + lcol) = kreg[u];
   };
-  auto lstore_v = [&](int st) {
+  auto lstore_v = [&](auto st) __attribute__((always_inline)) {
     __bf16* Vs = vstage(st);
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) *(u32x4*)(Vs + (lrow + u * T::RPP) * T::VSTR + lcol) = vreg[u];
   };
+  // LDS DMA: each wave fills rows [8 w, 8 w + 8) of a tile, one 1 KB block
+  // (RPI rows) per load, every lane fetching the logical chunk that belongs
+  // at its physical place in the swizzled row.  The data is in LDS once
+  // vmcnt has drained (waited for before the barrier that ends phase 2t+1).
+  constexpr int RPI = 512 / D;
+  constexpr int NLD = 8 / RPI;
+  uint32_t kdoff[NLD], vdoff[NLD];
+  if constexpr (DMA) {
+    const int lrow_in = lane / (64 / RPI), lpc = lane % (64 / RPI);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int row = 8 * wave + RPI * u + lrow_in;
+      const int col = swz<D>(row, 8 * lpc) - row * D;   // logical column of this chunk
+      kdoff[u] = (uint32_t)(row * p.k_ss + col) * 2;
+      vdoff[u] = (uint32_t)(row * p.v_ss + col) * 2;
+    }
+  }
+  auto dma_k = [&](int j0, auto st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u)
+      buf_load16_lds(rk, (uint32_t)j0 * (uint32_t)p.k_ss * 2 + kdoff[u], kstage(st) + (8 * wave + RPI * u) * D);
+  };
+  auto dma_v = [&](int j0, auto st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u)
+      buf_load16_lds(rv, (uint32_t)j0 * (uint32_t)p.v_ss * 2 + vdoff[u], vstage(st) + (8 * wave + RPI * u) * D);
+  };
+  // operand addresses in the swizzled stages: per-lane bases plus constants
+  // (the chunk permutation depends on the row modulo 16 only)
+  int aoff[T::NC], toff[2][T::ND];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) aoff[c] = DMA ? swz<D>(kperm, 16 * c + 8 * hh) : kperm * T::KSTR + 8 * hh + 16 * c;
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db) {
+    toff[0][db] = DMA ? swz<D>(tr_row, 32 * db + tr_col) : tr_row * T::VSTR + tr_col + 32 * db;
+    toff[1][db] = DMA ? swz<D>(tr_row + 4, 32 * db + tr_col) : (tr_row + 4) * T::VSTR + tr_col + 32 * db;
+  }
 
   f32x16 oacc[T::ND];
 #pragma unroll
@@ -210,15 +265,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   const float lazy_margin = 8.f / c2;   // 2^8 growth of the probabilities, in score units
   const int wave_first_row = q0 + wave * 32;
 
-  // O^T += V^T P^T for tile t (V in stage t & 1)
-  auto pv_product = [&](int t) {
-    const __bf16* vbase = vstage(t & 1) + tr_row * T::VSTR + tr_col;
+  // O^T += V^T P^T for the tile whose V is in stage st
+  auto pv_product = [&](auto st) __attribute__((always_inline)) {
+    const __bf16* vs = vstage(st);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) {
-        const __bf16* vp = vbase + 16 * c * T::VSTR + 32 * db;
-        const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
+        const bf16x8 vf = cat_bf16(lds_read_tr16(vs + toff[0][db] + 16 * c * T::VSTR),
+                                   lds_read_tr16(vs + toff[1][db] + 16 * c * T::VSTR));
         oacc[db] = mfma32(vf, pf[c], oacc[db]);
       }
     }
@@ -231,16 +286,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, T::ND, 0);
   };
-  // S^T = K Q^T for tile t (K in stage t & 1)
-  auto scores = [&](int t) {
-    const __bf16* kbase = kstage(t & 1) + kperm * T::KSTR + 8 * hh;
+  // S^T = K Q^T for the tile whose K is in stage st
+  auto scores = [&](auto st) __attribute__((always_inline)) {
+    const __bf16* ks = kstage(st);
     sacc[0] = (f32x16){};
     sacc[1] = (f32x16){};
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 kf = *(const bf16x8*)(kbase + 32 * kb2 * T::KSTR + 16 * c);
+        const bf16x8 kf = *(const bf16x8*)(ks + aoff[c] + 32 * kb2 * T::KSTR);
         sacc[kb2] = mfma32(kf, qf[c], sacc[kb2]);
       }
     }
@@ -256,7 +311,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   // O = O_acc / l is the same for any running max that keeps the
   // exponentials finite, so m, l and O_acc are rescaled only when some row's
   // max grew by more than 2^8 in exp2 units.
-  auto softmax = [&](int t) {
+  auto softmax = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
     const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > wave_first_row + diag);
     if (need_mask) {
@@ -270,7 +325,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
         }
     }
     float rs = 0.f;
-    auto exponentials = [&](float nb) {
+    auto exponentials = [&](float nb) __attribute__((always_inline)) {
       rs = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -315,11 +370,44 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     __asm__ volatile("" : "+v"(l_run));   // the row sum belongs to this phase
   };
 
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // K_{t+1} and V_t (Par = t mod 2): issued in phase 2t into the stages
+  // last read in phase 2t-1, in LDS after phase 2t+1
+  auto issue = [&](int t, auto Par) __attribute__((always_inline)) {
+    constexpr int par = decltype(Par)::value;
+    using Next = std::integral_constant<int, 1 - par>;
+    const bool more = t + 1 < ntiles;
+    if constexpr (DMA) {
+      if (more) dma_k((t + 1) * BN, Next{});
+      dma_v(t * BN, Par);
+    } else {
+      (void)Next{};
+      if (more) gload_k((t + 1) * BN);
+      gload_v(t * BN);
+    }
+  };
+  auto land = [&](int t, auto Par) __attribute__((always_inline)) {
+    constexpr int par = decltype(Par)::value;
+    using Next = std::integral_constant<int, 1 - par>;
+    if constexpr (DMA) {
+      (void)Next{};
+      wait_vmem();
+    } else {
+      if (t + 1 < ntiles) lstore_k(Next{});
+      lstore_v(Par);
+    }
+  };
+
   if (ntiles > 0) {
-    gload_k(0);
-    lstore_k(0);
+    if constexpr (DMA) {
+      dma_k(0, S0{});
+    } else {
+      gload_k(0);
+      lstore_k(S0{});
+    }
   }
-  wait_vmem();  // Q fragments have landed on every path into the loop
+  wait_vmem();  // Q fragments (and K_0) have landed on every path into the loop
   __syncthreads();
 
   // A wave sees tile t iff t < nt_w (monotone in t under the causal mask).
@@ -330,56 +418,70 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   }
   const bool is_a = grp == 0;
 
-  // The two groups run separate programs with the same number of barriers.
-  // Global loads of K_{t+1} and V_t are issued in phase 2t and written to LDS
-  // at the end of phase 2t+1, into the stages last read in phase 2t-1.
+  // The two groups run separate programs with the same number of barriers;
+  // the loops are unrolled by two so that every stage is known at compile
+  // time.  Phases 2t and 2t+1 of group A, t >= 1 (Par = t mod 2):
+  auto iter_a = [&](int t, auto Par) __attribute__((always_inline)) {
+    using Prev = std::integral_constant<int, 1 - decltype(Par)::value>;
+    issue(t, Par);
+    __builtin_amdgcn_sched_barrier(0);   // loads first, ahead of the products
+    if (t - 1 < nt_w) pv_product(Prev{});
+    if (t < nt_w) scores(Par);
+    phase_barrier();                                     // phase 2t
+    if (t < nt_w) softmax(t);
+    land(t, Par);
+    phase_barrier();                                     // phase 2t+1
+  };
+  // and of group B
+  auto iter_b = [&](int t, auto Par) __attribute__((always_inline)) {
+    using Prev = std::integral_constant<int, 1 - decltype(Par)::value>;
+    issue(t, Par);
+    if (t - 1 < nt_w) softmax(t - 1);
+    phase_barrier();                                     // phase 2t
+    if (t - 1 < nt_w) pv_product(Prev{});
+    if (t < nt_w) scores(Par);
+    land(t, Par);
+    phase_barrier();                                     // phase 2t+1
+  };
   if (ntiles > 0) {
+    const int last = ntiles - 1;
     if (is_a) {
-      if (ntiles > 1) gload_k(BN);
-      gload_v(0);
-      if (nt_w > 0) scores(0);
+      issue(0, S0{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (nt_w > 0) scores(S0{});
       phase_barrier();                                   // phase 0
       if (nt_w > 0) softmax(0);
-      if (ntiles > 1) lstore_k(1);
-      lstore_v(0);
+      land(0, S0{});
       phase_barrier();                                   // phase 1
-      for (int t = 1; t < ntiles; ++t) {
-        const bool more = t + 1 < ntiles;
-        if (more) gload_k((t + 1) * BN);
-        gload_v(t * BN);
-        if (t - 1 < nt_w) pv_product(t - 1);
-        if (t < nt_w) scores(t);
-        phase_barrier();                                 // phase 2t
-        if (t < nt_w) softmax(t);
-        if (more) lstore_k((t + 1) & 1);
-        lstore_v(t & 1);
-        phase_barrier();                                 // phase 2t+1
+      int t = 1;
+      for (; t + 1 < ntiles; t += 2) {
+        iter_a(t, S1{});
+        iter_a(t + 1, S0{});
       }
-      if (ntiles - 1 < nt_w) pv_product(ntiles - 1);
+      if (t < ntiles) iter_a(t, S1{});
+      if (last < nt_w) {
+        if (last & 1) pv_product(S1{});
+        else pv_product(S0{});
+      }
       phase_barrier();                                   // phase 2n
     } else {
-      if (ntiles > 1) gload_k(BN);
-      gload_v(0);
+      issue(0, S0{});
       phase_barrier();                                   // phase 0
-      if (nt_w > 0) scores(0);
-      if (ntiles > 1) lstore_k(1);
-      lstore_v(0);
+      if (nt_w > 0) scores(S0{});
+      land(0, S0{});
       phase_barrier();                                   // phase 1
-      for (int t = 1; t < ntiles; ++t) {
-        const bool more = t + 1 < ntiles;
-        if (more) gload_k((t + 1) * BN);
-        gload_v(t * BN);
-        if (t - 1 < nt_w) softmax(t - 1);
-        phase_barrier();                                 // phase 2t
-        if (t - 1 < nt_w) pv_product(t - 1);
-        if (t < nt_w) scores(t);
-        if (more) lstore_k((t + 1) & 1);
-        lstore_v(t & 1);
-        phase_barrier();                                 // phase 2t+1
+      int t = 1;
+      for (; t + 1 < ntiles; t += 2) {
+        iter_b(t, S1{});
+        iter_b(t + 1, S0{});
       }
-      if (ntiles - 1 < nt_w) softmax(ntiles - 1);
+      if (t < ntiles) iter_b(t, S1{});
+      if (last < nt_w) softmax(last);
       phase_barrier();                                   // phase 2n
-      if (ntiles - 1 < nt_w) pv_product(ntiles - 1);     // phase 2n+1
+      if (last < nt_w) {                                 // phase 2n+1
+        if (last & 1) pv_product(S1{});
+        else pv_product(S0{});
+      }
     }
   }
 

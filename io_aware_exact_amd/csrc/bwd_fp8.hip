@@ -324,8 +324,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
       if (++ld_h < p.group) set_head(ld_h);
     }
   };
-  // LSE is stored as a log2 value (no visible key or padding row: +inf, so
-  // the probabilities are zero); D is stored times the tile's Q scale
+  // LSE is stored as a log2 value minus 8, so that exp2 gives 2^8 p, the
+  // value the E4M3 P operand holds (no visible key or padding row: +inf, so
+  // the probabilities are zero); D is stored times the tile's Q scale and
+  // 2^-8, which the dS side needs with the 2^8 p it receives
   auto lstore = [&](int st) {
     uint8_t* Qs = stage(st);
     uint8_t* Os = Qs + T::TILE;
@@ -334,8 +336,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
       *(u32x4*)(Qs + lrow * T::STR + lcol) = qreg;
       *(u32x4*)(Os + lrow * T::STR + lcol) = doreg;
     }
-    if (tid < T::BQ) stats[tid] = (sval == -INFINITY) ? INFINITY : sval * LOG2E;
-    else if (tid < 2 * T::BQ) stats[tid] = sval * sqv;
+    if (tid < T::BQ) stats[tid] = (sval == -INFINITY) ? INFINITY : __builtin_fmaf(sval, LOG2E, -8.f);
+    else if (tid < 2 * T::BQ) stats[tid] = sval * sqv * (1.f / 256.f);
     else if (tid == 2 * T::BQ) stats[2 * T::BQ] = sqv;
     else if (tid == 2 * T::BQ + 1) ((int*)stats)[2 * T::BQ + 1] = edo;
   };
@@ -407,6 +409,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
               if (key >= Lk || (CAUSAL && key > iq + diag)) v[qb][i] = 0.f;
             }
           }
+          // v = 2^8 P: the bf16 exchange carries it exactly scaled
           bf16x8 ob0, ob1;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -418,8 +421,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
           pe[64] = __builtin_bit_cast(u32x4, ob1);
         }
       } else {
-        // dS * sq = P (dP sv sq - D sq), P from the P-wave of this tile
-        const float f = skv * sq_t;
+        // dS * sq = 2^8 P (dP sv sq 2^-8 - D sq 2^-8), 2^8 P from the P-wave
+        const float f = skv * sq_t * (1.f / 256.f);
         const float* dels = stats + T::BQ;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
         }
       }
       // ---- B operand of the second product: 2^8 P (P-wave) or dS (dS-wave)
-      const i32x8 ob = pwave ? pack_tile(v, 256.f, 256.f) : quantise_ds(v, hh, sb_byte);
+      const i32x8 ob = pwave ? pack_tile(v, 1.f, 1.f) : quantise_ds(v, hh, sb_byte);
       const int ta = pwave ? edo_t : UNIT;   // scale of dO^T (P-wave) or Q^T (dS-wave)
       // ---- acc += Ts^T ob (64 query rows per instruction)
       const uint8_t* tbase = Ts + tr_row * T::STR + tr_col;

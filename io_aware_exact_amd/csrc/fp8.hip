@@ -15,13 +15,20 @@
 // one K scale sk_J and one V scale sv_J, so
 //   * the scores are s = (scale * sq * sk_J) * (q8 . k8): the whole factor,
 //     times log2(e), is the per-tile constant of the exp2 FMA;
-//   * p = exp2(s - m) is stored in e4m3 as 2^8 p (the factor rides in the
-//     exp2 FMA constant), so that probabilities down to 2^-14 keep 3 mantissa
-//     bits (448 bounds 2^8 * 1);
-//   * V's scale is folded into the running rescale: the accumulator holds
-//     O_hat = O_acc / sv_J, updated as O_hat <- O_hat * alpha * sv_{J-1} / sv_J
-//     + P8 V8_J (skipped when the factor is 1: same V block, no new row max),
-//     and the epilogue writes O = sv_last * O_hat / l with l = sum 2^8 p.
+//   * p = exp2(s - m) is stored in e4m3 with a power-of-two prescale that
+//     rides in the exp2 FMA constant, so that small probabilities keep 3
+//     mantissa bits; m is a lazily moved reference (see LAZY), so p may
+//     exceed 1 by up to 2^LAZY;
+//   * per-block scales: V's scale rides in the P V product.  With sv_ref the
+//     head's largest V scale, sv_J / sv_ref = 2^k r (k <= 0 an integer, r in
+//     [1, 2)); p is stored as 2^7 r p (log2 r joins the exp2 constant) and
+//     2^(k - 7) is the instruction's E8M0 scale of the P operand, exact; the
+//     accumulator holds O_acc = sum p v8 sv_J / sv_ref, the row sum
+//     l = sum 2^7 p (each tile's sum of stored values times 1/r), and the
+//     epilogue writes O = sv_ref 2^7 O_acc / l.  No rescale happens when the
+//     V block changes;
+//   * MX scales: p is stored as 2^8 p and the V block scales are the E8M0
+//     scales of the V operand.
 //
 // gfx950 mapping.  As in the bf16 forward (S^T = K Q^T with query rows in the
 // MFMA columns, 4 waves x 32 rows, 2-stage LDS ring of 64-key tiles), with the
@@ -59,9 +66,16 @@ constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NTHREADS = 256;
 constexpr int QBLK = 128;          // tokens per quantisation block
-// Probabilities are stored in e4m3 as 2^P_LOG2 p <= 2^8 < 448; values down
-// to 2^-(6 + P_LOG2) keep 3 mantissa bits.
+// Probabilities are stored in e4m3 as 2^P_LOG2 p (MX) or 2^P_LOG2_BLK r p
+// with r in [1, 2) (per-block scales, see the kernel); values down to
+// 2^-(6 + P_LOG2) keep 3 mantissa bits.
 constexpr float P_LOG2 = 8.f;
+constexpr float P_LOG2_BLK = 7.f;
+// The running maximum m is a reference, moved (and the accumulators rescaled)
+// only when a tile's maximum exceeds it by more than LAZY (exp2 units): the
+// largest stored value is then below 2^8 * 2^LAZY = 445.7 <= 448, in both
+// paths.
+constexpr float LAZY = 0.8f;
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
@@ -218,9 +232,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < T::ND; ++i) oacc[i] = (f32x16){};
   float m_run = -INFINITY;   // running max in log2 units of the scaled scores
-  float l_run = 0.f;         // sum of 2^P_LOG2 p
-  float sv_prev = 1.f;       // V scale the accumulator is currently in units of
+  constexpr float PL = MX ? P_LOG2 : P_LOG2_BLK;
+  float l_run = 0.f;         // sum of 2^PL p
   const float cq = p.scale_log2 * sq;
+  // per-block path: the head's largest V scale, the reference of O_acc
+  float sv_ref = 1.f;
+  if (!MX) {
+    float m = 0.f;
+    for (int i = lane; i < nkb; i += 64) m = fmaxf(m, vsc[i]);
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) m = fmaxf(m, __shfl_xor(m, w, 64));
+    sv_ref = m > 0.f ? m : 1.f;
+  }
+  const float inv_sv_ref = __builtin_amdgcn_rcpf(sv_ref);
 
   if (ntiles > 0) {
     gload(0);
@@ -244,7 +268,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
       const uint8_t* Ks = smem + st * T::STAGE;
       const uint8_t* Vs = Ks + BN * T::STR;
       const float c2 = MX ? p.scale_log2 : cq * ksc[j0 / QBLK];
-      const float sv = MX ? 1.f : vsc[j0 / QBLK];
+      // per-block path: sv_J / sv_ref = 2^kv r, r in [1, 2)
+      int pbyte = 127;            // E8M0 scale of the P operand
+      float log2r = 0.f, inv_r = 1.f;
+      if (!MX) {
+        const uint32_t rb = __builtin_bit_cast(uint32_t, vsc[j0 / QBLK] * inv_sv_ref);
+        const int kv = max(-119, min(0, (int)(rb >> 23) - 127));
+        const float r = __builtin_bit_cast(float, (rb & 0x7FFFFFu) | 0x3F800000u);
+        pbyte = 127 + kv - (int)P_LOG2_BLK;
+        log2r = __builtin_amdgcn_logf(r);
+        inv_r = __builtin_amdgcn_rcpf(r);
+      }
       const uint8_t* kbase = Ks + kperm * T::STR;
       f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
@@ -277,22 +311,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
       mx = fmaxf(mx, wave_xor32(mx)) * c2;
-      const bool grow = mx > m_run;
-      const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
-      if (grow) m_run = mx;
+      // move the reference only when the tile's maximum exceeds it by more
+      // than LAZY (first tile: always).  A new reference sits log2 r above
+      // the maximum, so that the largest stored value, 2^PL r exp2(mx - m),
+      // is exactly 2^PL: a row dominated by one key then carries no e4m3
+      // rounding on that key's probability.
+      const float m_new = mx + log2r;
+      const bool grow = mx > m_run + LAZY;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+      if (grow) m_run = m_new;
       l_run *= alpha;
-      // O_hat <- O_hat alpha sv_prev / sv; skipped when that factor is 1 in
-      // every lane (same V block, no row max grew)
-      // (sv changes every other tile; the hardware reciprocal's last-bit
-      // error only changes the units O_hat is kept in)
-      const float resc = sv == sv_prev ? alpha : alpha * (sv_prev * __builtin_amdgcn_rcpf(sv));
-      if (__builtin_amdgcn_ballot_w64(resc != 1.f) != 0) {
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-        for (int i = 0; i < T::ND; ++i) oacc[i] *= resc;
+        for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
       }
-      sv_prev = sv;
-      // p8 = 2^P_LOG2 exp2(s c2 - m): the prescale rides in the FMA constant
-      const float nb = (m_run == -INFINITY ? 0.f : -m_run) + P_LOG2;
+      // stored value 2^PL r exp2(s c2 - m): the prescale and log2 r ride in
+      // the FMA constant
+      const float nb = (m_run == -INFINITY ? 0.f : -m_run) + PL + log2r;
       float rs = 0.f;
       i32x8 pf;
 #pragma unroll
@@ -306,7 +341,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
         pf[2 * r] = pack4_fp8(pv[0], pv[1], pv[2], pv[3]);
         pf[2 * r + 1] = pack4_fp8(pv[4], pv[5], pv[6], pv[7]);
       }
-      l_run += rs;
+      l_run += MX ? rs : rs * inv_r;
       // O_hat^T += V8^T P8^T (64 keys per MFMA)
       const uint8_t* vbase = Vs + tr_row * T::STR + tr_col;
 #pragma unroll
@@ -321,7 +356,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
         if constexpr (MX)
           oacc[db] = mfma_mx(vf, pf, oacc[db], (int)vsc_t[db], 127);
         else
-          oacc[db] = mfma_fp8(vf, pf, oacc[db]);
+          oacc[db] = mfma_mx(vf, pf, oacc[db], 127, pbyte);
       }
     }
     if (more) {
@@ -331,10 +366,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = sv_last O_hat / l, LSE = ln 2 (m - P_LOG2) + ln l
+  // ---- epilogue: O = sv_ref 2^PL O_acc / l (MX: O_acc / l, l in units of
+  // 2^PL), LSE = ln 2 (m - PL) + ln l
   const float l_tot = l_run + wave_xor32(l_run);
   if (qrow < Lq) {
-    const float inv = l_tot > 0.f ? sv_prev / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (MX ? 1.f : sv_ref * exp2f(PL)) / l_tot : 0.f;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)((int64_t)Lq * p.o_ss * 2));
     const uint32_t orow = (uint32_t)(qrow * p.o_ss) * 2;
 #pragma unroll
@@ -346,7 +382,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
         for (int r = 0; r < 4; ++r) w[r] = (__bf16)(oacc[db][4 * gi + r] * inv);
         buf_store8(__builtin_bit_cast(u32x2, w), ro, orow + (uint32_t)(32 * db + 8 * gi + 4 * hh) * 2);
       }
-    if (hh == 0) lseb[qrow] = l_tot > 0.f ? (m_run - P_LOG2) * 0.6931471805599453f + logf(l_tot) : -INFINITY;
+    if (hh == 0) lseb[qrow] = l_tot > 0.f ? (m_run - PL) * 0.6931471805599453f + logf(l_tot) : -INFINITY;
   }
 }
 

@@ -14,16 +14,21 @@ element, by what that rounding can do:
         |dLSE_i| <= 1e-3 + eps_i,  eps_i = 2^-11 * scale * max_j sum_c |q_ic k_jc|,
     which is the bf16 bar of 1e-3 when no single product dominates (plain
     N(0,1) inputs reach ~1e-5) and scales with the outlier products;
-  * O, element by element.  The kernel rounds x_j = 2^8 exp(s_j - m) (m the
-    running maximum, so x_j <= 2^8 and the final row sum l >= 2^8) to E4M3:
-    the error is at most 2^-4 x_j for normal values and min(x_j, 2^-10) for
-    subnormal ones, i.e. at most 2^-4 P_ij + min(P_ij, 2^-18) in units of the
-    exact probability P_ij.  Score errors of at most eps_i move each P_ij by
+  * O, element by element.  The kernel rounds x_j = c exp(s_j - m) to E4M3,
+    with c = 2^7 r, r in [1, 2) (per-block scales: r is the mantissa of the V
+    block's scale relative to the head's largest) or c = 2^8 (MX), and m a
+    reference that moves only when a tile's maximum exceeds it by more than
+    0.8 in exp2 units, to log2 r above that maximum (so x_j <= 445.7, the
+    element that last set m is stored exactly as 2^7, or 2^8 for MX, and the
+    row sum, counted in units of 2^7 p, is at least 2^7).  The
+    rounding error is at most 2^-4 x_j for normal values and min(x_j, 2^-10)
+    for subnormal ones, i.e. at most 2^-4 P_ij + min(P_ij, 2^-17) in units of
+    the exact probability P_ij.  Score errors of at most eps_i move each P_ij by
     a factor within exp(+-2 eps_i) after normalisation; the row sum and the
     FP8 P.V instruction's own summation add at most 2^-9 relative, and the
     bf16 output rounding 2^-9 |O_ic|.  Hence
         |dO_ic| <= ((1 + 2^-4) e^(2 eps_i) - 1 + 2^-9) sum_j P_ij |v_jc|
-                   + sum_j min(P_ij, 2^-18) |v_jc| + 2^-9 |O_ic| + 1e-4,
+                   + sum_j min(P_ij, 2^-17) |v_jc| + 2^-9 |O_ic| + 1e-4,
     with P and O from the oracle's fp64 scores and LSE on the same
     (dequantised) inputs.  A wrong or dropped scale block breaks this bound
     by a factor far above 1 on every element it touches;
@@ -131,7 +136,7 @@ def o_bound_rows(Q, K, V, grp, scale, causal, bi, hi, ii, lse_ref, o_ref):
         P[~np.isfinite(lse)] = 0.0
         av = np.abs(v)
         coef = (1 + 2.0 ** -4) * np.exp(2 * eps) - 1 + 2.0 ** -9
-        bound[r] = (coef[:, None] * (P @ av) + np.minimum(P, 2.0 ** -18) @ av
+        bound[r] = (coef[:, None] * (P @ av) + np.minimum(P, 2.0 ** -17) @ av
                     + 2.0 ** -9 * np.abs(o_ref[r]) + 1e-4)
     return bound
 

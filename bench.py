@@ -361,6 +361,24 @@ def leg_sweep(reps):
     return out
 
 
+def leg_gemm(reps):
+    """The box's sustained dense bf16 MFMA rate, measured on a plain library
+    GEMM (torch.matmul -> hipBLASLt, M = N = K = 8192, bf16 in, fp32
+    accumulate, bf16 out): the practical ceiling the attention kernels'
+    MFMA rate is compared with (not part of the attention path)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    n = 8192
+    a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    t = time_calls(lambda: torch.matmul(a, b, out=c), reps)
+    flops = 2.0 * n ** 3
+    return {"workload": "bf16 GEMM 8192x8192x8192 (torch.matmul, hipBLASLt)", "ms": round(t["mean"], 4),
+            "tflops": round(flops / t["mean"] / 1e9, 2),
+            "frac_of_peak": round(flops / t["mean"] / 1e9 / PEAK_BF16_TFLOPS, 4), "timing": timing(t)}
+
+
 def leg_main(reps, with_bwd):
     """The main workload alone (B=2, H=16, S=8192, d=128, non-causal): fwd, or
     fwd then bwd, reps times -- for profiling."""
@@ -389,7 +407,7 @@ def extra_legs(args, keep_rows=None):
     out = {}
     if args.only in ("fwd", "fwdbwd"):
         return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
-    for name, fn, reps in (("causal", leg_causal, 20), ("decode", leg_decode, 20),
+    for name, fn, reps in (("gemm", leg_gemm, 20), ("causal", leg_causal, 20), ("decode", leg_decode, 20),
                            ("varlen", leg_varlen, 20), ("kvcache", leg_kvcache, 20),
                            ("fp8", leg_fp8, 20),
                            ("sweep", leg_sweep, 20)):
@@ -409,7 +427,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
     ap.add_argument("--only", choices=["decode", "varlen", "kvcache", "causal", "fp8", "sweep", "fwd",
-                                       "fwdbwd"],
+                                       "fwdbwd", "gemm"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

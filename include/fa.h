@@ -48,6 +48,14 @@
  * and surface at the caller's next synchronisation.  The contents of
  * cu_seqlens arrays live on the device and are trusted (they must be
  * non-decreasing, start at 0 and stay within the packed tensors).
+ *
+ * Debug checks.  When the environment variable FA_DEBUG is set to a value
+ * other than "0" at the time of a call, the packed-sequence calls
+ * (fa_fwd_varlen, fa_bwd_varlen) also check the cu_seqlens contents: they
+ * synchronise `stream`, copy both arrays to the host and return
+ * FA_ERR_SEQLENS, with nothing enqueued, unless each starts at 0, never
+ * decreases, ends at its total (total_q, total_k) and has no step above its
+ * max_seqlen.  This is the one case in which the library synchronises.
  */
 #ifndef FA_H
 #define FA_H
@@ -73,7 +81,8 @@ typedef enum {
   FA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
   FA_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
-  FA_ERR_SCALE = 10       /* softmax scale is not a finite number > 0 */
+  FA_ERR_SCALE = 10,      /* softmax scale is not a finite number > 0 */
+  FA_ERR_SEQLENS = 11     /* FA_DEBUG only: cu_seqlens contents are inconsistent */
 } fa_status;
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1, FA_FP8_E4M3 = 2 } fa_dtype;

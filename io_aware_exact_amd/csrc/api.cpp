@@ -2,7 +2,10 @@
 // caller's stream.  Nothing here allocates device memory or synchronises.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
@@ -193,6 +196,38 @@ fa_status check_fwd(const fa_fwd_args* a) {
     if (overlap(sw, sq) || overlap(sw, sk) || overlap(sw, sv) || overlap(sw, so) || overlap(sw, sl))
       return FA_ERR_ALIAS;
   }
+  return FA_OK;
+}
+
+// FA_DEBUG (read at every call): any value other than "0" turns on the
+// host-side check of cu_seqlens contents.
+bool debug_checks() {
+  const char* e = getenv("FA_DEBUG");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+// One cu_seqlens array of nseq + 1 entries: starts at 0, never decreases,
+// ends at `total`, no step above `max_len`.
+bool seqlens_ok(const std::vector<int32_t>& cu, int32_t total, int32_t max_len) {
+  if (cu.empty() || cu[0] != 0 || cu.back() != total) return false;
+  for (size_t i = 1; i < cu.size(); ++i) {
+    const int64_t len = (int64_t)cu[i] - cu[i - 1];
+    if (len < 0 || len > max_len) return false;
+  }
+  return true;
+}
+
+// The FA_DEBUG check of both arrays (after the argument check passed):
+// synchronises the stream, copies them to the host and checks them.
+fa_status check_seqlens_debug(const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int32_t total_q,
+                              int32_t total_k, int32_t max_q, int32_t max_k, hipStream_t stream) {
+  if (!debug_checks()) return FA_OK;
+  std::vector<int32_t> hq((size_t)nseq + 1), hk((size_t)nseq + 1);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(hq.data(), cu_q, hq.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(hk.data(), cu_k, hk.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return FA_ERR_HIP;
+  if (!seqlens_ok(hq, total_q, max_q) || !seqlens_ok(hk, total_k, max_k)) return FA_ERR_SEQLENS;
   return FA_OK;
 }
 
@@ -517,6 +552,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_ALIAS: return "an output overlaps another tensor";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_SCALE: return "softmax scale must be finite and positive";
+    case FA_ERR_SEQLENS: return "cu_seqlens contents are inconsistent (FA_DEBUG check)";
   }
   return "unknown status";
 }
@@ -580,6 +616,11 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
 fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, hipStream_t stream) {
   const fa_status s = check_varlen(a);
   if (s != FA_OK) return s;
+  if (a->nseq > 0) {
+    const fa_status sd = check_seqlens_debug(a->cu_seqlens_q, a->cu_seqlens_k, a->nseq, a->total_q,
+                                             a->total_k, a->max_seqlen_q, a->max_seqlen_k, stream);
+    if (sd != FA_OK) return sd;
+  }
   if (a->nseq == 0 || a->max_seqlen_q == 0 || a->total_q == 0) return FA_OK;
   FwdParams p = {};
   p.q = a->q;
@@ -682,6 +723,11 @@ size_t fa_bwd_varlen_workspace_size(const fa_bwd_varlen_args* a) {
 fa_status fa_bwd_varlen(const fa_bwd_varlen_args* a, hipStream_t stream) {
   const fa_status s = check_bwd_varlen(a);
   if (s != FA_OK) return s;
+  if (a->nseq > 0) {
+    const fa_status sd = check_seqlens_debug(a->cu_seqlens_q, a->cu_seqlens_k, a->nseq, a->total_q,
+                                             a->total_k, a->max_seqlen_q, a->max_seqlen_k, stream);
+    if (sd != FA_OK) return sd;
+  }
   if (a->nseq == 0 || a->total_q == 0 || a->total_k == 0) {
     // no query rows or no keys anywhere: the gradients are zero
     if (a->total_q > 0 &&

@@ -7,6 +7,7 @@
 // overflow, bad shift or out-of-bounds access aborts the run.
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <random>
@@ -50,6 +51,7 @@ fa_tensor dense(int slot, int64_t S, int64_t H, int64_t d) {
 }  // namespace
 
 int main() {
+  unsetenv("FA_DEBUG");   // the fuzzed pointers must never be read
   long ok[16] = {0}, total = 0;
   for (int it = 0; it < 100000; ++it) {
     {
@@ -189,6 +191,37 @@ int main() {
       if (c.workspace_bytes <= fa_bwd_workspace_size(&b)) return 6;
       if (fa_bwd(&c, nullptr) != FA_OK) return 7;
     }
+  // FA_DEBUG: the cu_seqlens contents are checked on the host (arrays here
+  // are host memory; the runtime stubs copy them)
+  {
+    const int32_t good_q[4] = {0, 100, 100, 250}, good_k[4] = {0, 70, 300, 310};
+    const int32_t bad_start[4] = {1, 100, 100, 250}, bad_order[4] = {0, 120, 100, 250};
+    const int32_t bad_end[4] = {0, 100, 100, 249}, bad_max[4] = {0, 10, 200, 250};
+    fa_fwd_varlen_args v;
+    memset(&v, 0, sizeof v);
+    v.dtype = FA_BF16, v.nseq = 3, v.Hq = 8, v.Hkv = 2, v.d = 128, v.max_seqlen_q = 150;
+    v.max_seqlen_k = 230, v.total_q = 250, v.total_k = 310, v.softmax_scale = 0.125f;
+    v.q = (const void*)(kBase + (uintptr_t(20) << 32)), v.k = (const void*)(kBase + (uintptr_t(21) << 32));
+    v.v = (const void*)(kBase + (uintptr_t(22) << 32)), v.o = (void*)(kBase + (uintptr_t(23) << 32));
+    v.lse = (float*)(kBase + (uintptr_t(24) << 32));
+    v.q_stride_t = 8 * 128, v.q_stride_h = 128, v.o_stride_t = 8 * 128, v.o_stride_h = 128;
+    v.k_stride_t = v.v_stride_t = 2 * 128, v.k_stride_h = v.v_stride_h = 128;
+    v.cu_seqlens_k = good_k;
+    const long l0 = g_launches;
+    setenv("FA_DEBUG", "1", 1);
+    v.cu_seqlens_q = good_q;
+    if (fa_fwd_varlen(&v, nullptr) != FA_OK || g_launches == l0) return 8;
+    const int32_t* bad[4] = {bad_start, bad_order, bad_end, bad_max};
+    for (const int32_t* b : bad) {
+      v.cu_seqlens_q = b;
+      const long l1 = g_launches;
+      if (fa_fwd_varlen(&v, nullptr) != FA_ERR_SEQLENS || g_launches != l1) return 9;
+    }
+    setenv("FA_DEBUG", "0", 1);   // off again: contents are not read
+    v.cu_seqlens_q = bad_order;
+    if (fa_fwd_varlen(&v, nullptr) != FA_OK) return 10;
+    unsetenv("FA_DEBUG");
+  }
   printf("api fuzz: %ld rounds; accepted fwd %ld bwd %ld varlen %ld bwd_varlen %ld kvcache %ld mx %ld "
          "merge %ld quant %ld; valid-set launches %ld\n",
          total, ok[1], ok[3], ok[5], ok[7], ok[9], ok[11], ok[13], ok[15], g_launches - before);

@@ -105,6 +105,36 @@ def test_varlen_equals_dense_per_sequence():
         assert torch.equal(od[0], o[qs:qe]) and torch.equal(ld[0], lse[:, qs:qe])
 
 
+def test_varlen_debug_check(monkeypatch):
+    """FA_DEBUG: the packed calls check the cu_seqlens contents on the host
+    and reject inconsistent ones before enqueuing anything (outputs keep
+    their sentinel); valid ones run as without the check."""
+    lens = [100, 37, 256]
+    q, k, v = inputs.packed_qkv(lens, lens, 4, 1, 128, 23, device="cuda")
+    good = inputs.cu_seqlens(lens, device="cuda")
+    o_ref, lse_ref = fa.fwd_varlen(q, k, v, good, good, max(lens), max(lens), True)
+    monkeypatch.setenv("FA_DEBUG", "1")
+    o, lse = fa.fwd_varlen(q, k, v, good, good, max(lens), max(lens), True)
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    bad = [torch.tensor(c, dtype=torch.int32, device="cuda") for c in
+           ([0, 150, 137, 393], [1, 101, 138, 393], [0, 100, 137, 392])]
+    # a step above max_seqlen_q is also rejected
+    tight = (good, max(lens) - 1)
+    for cu, mx in [(c, max(lens)) for c in bad] + [tight]:
+        out = torch.full_like(o, 7.0)
+        with pytest.raises(fa.FaError) as e:
+            fa.fwd_varlen(q, k, v, cu, good, mx, max(lens), True, out=out)
+        assert e.value.status == 11
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all())
+        dq, dk, dv = (torch.full_like(x, 7.0) for x in (q, k, v))
+        with pytest.raises(fa.FaError) as e:
+            fa.bwd_varlen(q, k, v, o, o, lse, good, cu, max(lens), mx, True, out=(dq, dk, dv))
+        assert e.value.status == 11
+        torch.cuda.synchronize()
+        assert all(bool((x == 7.0).all()) for x in (dq, dk, dv))
+
+
 def check_against_oracle(q, k, v, causal):
     o, lse = fa.fwd(q, k, v, causal)
     torch.cuda.synchronize()

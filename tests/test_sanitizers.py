@@ -57,6 +57,11 @@ def launch_stubs():
             body.append(f"hipError_t {name}({params}) {{ *ptr = (void*)0x200000000000ull; return hipSuccess; }}")
         else:
             body.append(f"hipError_t {name}({params}) {{ ++g_launches; return hipSuccess; }}")
+    # the FA_DEBUG check's runtime calls: the harness passes host arrays there
+    body += ["#include <string.h>",
+             'extern "C" hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }',
+             'extern "C" hipError_t hipMemcpy(void* dst, const void* src, size_t n, hipMemcpyKind) '
+             '{ memcpy(dst, src, n); return hipSuccess; }']
     return "\n".join(body) + "\n"
 
 

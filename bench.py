@@ -379,6 +379,39 @@ def leg_gemm(reps):
             "frac_of_peak": round(flops / t["mean"] / 1e9 / PEAK_BF16_TFLOPS, 4), "timing": timing(t)}
 
 
+def leg_dqaccum(reps):
+    """Cost of the dQ accumulation a fused backward would add (measurement
+    probe `libfa_probe.so`, not part of the path): the dK/dV kernel's grid at
+    B=2, H=16, S=8192, d=128 (2048 workgroups of 128 keys, one per CU at a
+    time) adding a 64 x 128 fp32 partial for each of its 128 query tiles into
+    a 128 MB accumulator -- by device-scope atomics (mode 0), by racy plain
+    read-modify-write (mode 1, a floor for any ordered scheme) and by plain
+    stores (mode 2)."""
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "io_aware_exact_amd")
+    L = ctypes.CDLL(os.path.join(here, "libfa_probe.so"))
+    L.fa_probe_dq_accum.restype = ctypes.c_int
+    L.fa_probe_dq_accum.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    B, H, S, d = 2, 16, 8192, 128
+    acc = torch.zeros((B * H, S, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(mode):
+        rc = L.fa_probe_dq_accum(acc.data_ptr(), B, H, S, d, mode, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"fa_probe_dq_accum returned {rc}")
+    run(0)
+    torch.cuda.synchronize()
+    ok = bool((acc == S // 128).all().item())
+    partial_bytes = B * H * (S // 128) * (S // 64) * 64 * d * 4     # bytes of partials added
+    out = {"workload": "dQ partial adds of a fused backward, B=2 H=16 S=8192 d=128 (2048 workgroups x 128 tiles x 32 KB)",
+           "partial_bytes": partial_bytes, "atomic_result_exact": ok}
+    for mode, name in ((0, "atomic_add"), (1, "plain_rmw"), (2, "plain_store")):
+        t = time_calls(lambda: run(mode), reps)
+        out[name] = {"ms": round(t["mean"], 4), "partial_gbps": round(partial_bytes / t["mean"] / 1e6, 1),
+                     "timing": timing(t)}
+    return out
+
+
 def leg_main(reps, with_bwd):
     """The main workload alone (B=2, H=16, S=8192, d=128, non-causal): fwd, or
     fwd then bwd, reps times -- for profiling."""
@@ -407,7 +440,8 @@ def extra_legs(args, keep_rows=None):
     out = {}
     if args.only in ("fwd", "fwdbwd"):
         return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
-    for name, fn, reps in (("gemm", leg_gemm, 20), ("causal", leg_causal, 20), ("decode", leg_decode, 20),
+    for name, fn, reps in (("gemm", leg_gemm, 20), ("dqaccum", leg_dqaccum, 20), ("causal", leg_causal, 20),
+                           ("decode", leg_decode, 20),
                            ("varlen", leg_varlen, 20), ("kvcache", leg_kvcache, 20),
                            ("fp8", leg_fp8, 20),
                            ("sweep", leg_sweep, 20)):
@@ -427,7 +461,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
     ap.add_argument("--only", choices=["decode", "varlen", "kvcache", "causal", "fp8", "sweep", "fwd",
-                                       "fwdbwd", "gemm"],
+                                       "fwdbwd", "gemm", "dqaccum"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

@@ -1,4 +1,5 @@
-"""Builds libfa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
+"""Builds libfa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and
+libfa_probe.so, a measurement probe the bench uses (not part of the path)."""
 import concurrent.futures
 import os
 import subprocess
@@ -8,6 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
+PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
+PROBE_SOURCES = ["probe_dq_accum.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "fwd.hip", "fwd_pp.hip", "fwd_f32.hip", "bwd.hip", "decode.hip", "fp8.hip",
@@ -36,14 +39,15 @@ def _compile(src, verbose):
 def build(verbose=False):
     """Compile every source for gfx950 and link libfa.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    for lib, o in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + o
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

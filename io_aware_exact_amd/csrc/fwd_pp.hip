@@ -66,9 +66,10 @@ __device__ __forceinline__ void phase_barrier() {
 // (each layout its own instance, which folds away the paths it cannot take)
 template <int D, bool CAUSAL, bool VARLEN, int KVC>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
-  // dense and packed tensors: tiles by LDS DMA; KV caches (whose small pages
-  // need a page per row) through registers
-  constexpr bool DMA = KVC == 0;
+  // dense and packed tensors and KV caches whose 64-key tiles each lie in one
+  // region (no block table, or pages of >= 64 tokens): tiles by LDS DMA;
+  // smaller pages (a page per row) through registers
+  constexpr bool DMA = KVC <= 2;
   using T = PpTile<D, DMA>;
   // one array per stage: the compiler then knows that a DMA into one stage
   // does not write the others, and makes reads of the others wait for it
@@ -231,15 +232,38 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       vdoff[u] = (uint32_t)(row * p.v_ss + col) * 2;
     }
   }
+  // the buffer resource and first-row byte offset of the tile at key j0:
+  // dense, packed and unpaged caches read one region; with pages of >= 64
+  // tokens the tile lies in one page, read through a resource over that
+  // page's rows that hold tokens
+  auto tile_src = [&](int j0, const __amdgpu_buffer_rsrc_t& rd, const __bf16* base, int64_t sp, int64_t ss,
+                      __amdgpu_buffer_rsrc_t& r, uint32_t& off) __attribute__((always_inline)) {
+    if constexpr (KVC == 2) {
+      const int pn = j0 >> shift;
+      win.cover(btrow, pn, pn, last_page_no, lane);
+      const int64_t page = win.uniform(pn);
+      const int first_tok = pn << shift;
+      const int rows = min(Lk - first_tok, 1 << shift);
+      r = make_rsrc(base + page * sp, (uint32_t)(rows * ss * 2));
+      off = (uint32_t)(j0 - first_tok) * (uint32_t)ss * 2;
+    } else {
+      r = rd;
+      off = (uint32_t)j0 * (uint32_t)ss * 2;
+    }
+  };
   auto dma_k = [&](int j0, auto st) __attribute__((always_inline)) {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t off;
+    tile_src(j0, KVC ? rkc : rk, kb, p.kv.k_sp, p.k_ss, r, off);
 #pragma unroll
-    for (int u = 0; u < NLD; ++u)
-      buf_load16_lds(rk, (uint32_t)j0 * (uint32_t)p.k_ss * 2 + kdoff[u], kstage(st) + (8 * wave + RPI * u) * D);
+    for (int u = 0; u < NLD; ++u) buf_load16_lds(r, off + kdoff[u], kstage(st) + (8 * wave + RPI * u) * D);
   };
   auto dma_v = [&](int j0, auto st) __attribute__((always_inline)) {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t off;
+    tile_src(j0, KVC ? rvc : rv, vb, p.kv.v_sp, p.v_ss, r, off);
 #pragma unroll
-    for (int u = 0; u < NLD; ++u)
-      buf_load16_lds(rv, (uint32_t)j0 * (uint32_t)p.v_ss * 2 + vdoff[u], vstage(st) + (8 * wave + RPI * u) * D);
+    for (int u = 0; u < NLD; ++u) buf_load16_lds(r, off + vdoff[u], vstage(st) + (8 * wave + RPI * u) * D);
   };
   // operand addresses in the swizzled stages: per-lane bases plus constants
   // (the chunk permutation depends on the row modulo 16 only)

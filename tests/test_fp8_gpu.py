@@ -208,7 +208,7 @@ def check_fp8_all_rows(o, o_ref, lse_ref, Q, K, V, grp, scale, causal):
 
 @pytest.mark.parametrize("shape", [(1, 256, 256, 2, 2, 64), (2, 300, 300, 4, 2, 128),
                                    (1, 129, 500, 2, 1, 128), (1, 700, 200, 2, 2, 64),
-                                   (1, 1, 130, 4, 4, 128)])
+                                   (1, 1, 130, 4, 4, 128), (1, 600, 650, 2, 1, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_forward(shape, causal):
     B, Sq, Sk, Hq, Hkv, d = shape

@@ -76,7 +76,8 @@ def run_mx(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
 
 @pytest.mark.parametrize("shape", [(1, 256, 256, 2, 2, 64), (2, 300, 300, 4, 2, 128),
                                    (1, 129, 500, 2, 1, 128), (1, 700, 200, 2, 2, 64),
-                                   (1, 1, 130, 4, 4, 128), (1, 100, 37, 2, 2, 128)])
+                                   (1, 1, 130, 4, 4, 128), (1, 100, 37, 2, 2, 128),
+                                   (1, 600, 650, 2, 1, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_mx_forward(shape, causal):
     B, Sq, Sk, Hq, Hkv, d = shape

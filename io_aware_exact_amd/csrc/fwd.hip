@@ -49,14 +49,18 @@ constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NTHREADS = 256;
 
-template <int D>
+// DMA: tiles go from HBM straight into swizzled LDS stages (swz in
+// device_common.h, rows of D elements); otherwise through registers into
+// padded rows.
+template <int D, bool DMA>
 struct FwdTile {
-  // LDS row strides (elements).  K is read in rows of 16 bytes per lane by 16
-  // lanes at once: a stride of 4 banks (mod 64) spreads 16 rows over all 64
-  // banks.  V is read transposed, 4 rows x 64 bytes per 32 lanes: a stride of
-  // 16 banks (mod 64) puts the 4 rows on disjoint banks.
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D + 32;
+  // LDS row strides (elements) of the padded layout.  K is read in rows of
+  // 16 bytes per lane by 16 lanes at once: a stride of 4 banks (mod 64)
+  // spreads 16 rows over all 64 banks.  V is read transposed, 4 rows x 64
+  // bytes per 32 lanes: a stride of 16 banks (mod 64) puts the 4 rows on
+  // disjoint banks.
+  static constexpr int KSTR = DMA ? D : D + 8;
+  static constexpr int VSTR = DMA ? D : D + 32;
   static constexpr int NC = D / 16;     // 16-wide chunks of d (QK^T)
   static constexpr int ND = D / 32;     // 32-row blocks of d (O^T)
   static constexpr int CH = D / 8;      // 16-byte chunks per row
@@ -73,7 +77,10 @@ struct FwdTile {
 // within the registers of three waves per SIMD.
 template <int D, bool CAUSAL, bool VARLEN, int KVC>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdParams p) {
-  using T = FwdTile<D>;
+  // dense and packed tensors and KV caches whose 64-key tiles each lie in one
+  // region: tiles by LDS DMA; smaller pages (a page per row) through registers
+  constexpr bool DMA = KVC <= 2;
+  using T = FwdTile<D, DMA>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
 
   // ---- which (batch, head, query tile).  Dense: consecutive tiles of one
@@ -209,8 +216,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
       load_rows(rk, rv, j0);
     }
   };
-  auto lstore = [&](int st) {
-    __bf16* Ks = smem + st * T::STAGE;
+  auto lstore = [&](__bf16* Ks) {
     __bf16* Vs = Ks + BN * T::KSTR;
 #pragma unroll
     for (int u = 0; u < T::NP; ++u) {
@@ -218,6 +224,56 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
       *(u32x4*)(Vs + (lrow + u * T::RPP) * T::VSTR + lcol) = vreg[u];
     }
   };
+  // LDS DMA: each wave fills rows [16 w, 16 w + 16) of the K and V tiles,
+  // one 1 KB block (RPI rows) per load, every lane fetching the logical
+  // chunk that belongs at its physical place in the swizzled row.
+  constexpr int RPI = 512 / D;
+  constexpr int RPW = BN / 4;
+  constexpr int NLD = RPW / RPI;
+  uint32_t kdoff[NLD], vdoff[NLD];
+  if constexpr (DMA) {
+    const int lrow_in = lane / (64 / RPI), lpc = lane % (64 / RPI);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int row = RPW * wave + RPI * u + lrow_in;
+      const int col = swz<D>(row, 8 * lpc) - row * D;   // logical column of this chunk
+      kdoff[u] = (uint32_t)(row * p.k_ss + col) * 2;
+      vdoff[u] = (uint32_t)(row * p.v_ss + col) * 2;
+    }
+  }
+  // buffer resources and first-row byte offsets of the tile at key j0:
+  // one region, or (pages of >= 64 tokens) the tile's page
+  auto dma = [&](int j0, __bf16* Ks) {
+    __amdgpu_buffer_rsrc_t r_k = KVC ? rkc : rk, r_v = KVC ? rvc : rv;
+    uint32_t ok = (uint32_t)j0 * (uint32_t)p.k_ss * 2, ov = (uint32_t)j0 * (uint32_t)p.v_ss * 2;
+    if constexpr (KVC == 2) {
+      const int pn = j0 >> shift;
+      win.cover(btrow, pn, pn, last_page_no, lane);
+      const int64_t page = win.uniform(pn);
+      const int first_tok = pn << shift;
+      const int rows = min(Lk - first_tok, 1 << shift);
+      r_k = make_rsrc(kb + page * p.kv.k_sp, (uint32_t)(rows * p.k_ss * 2));
+      r_v = make_rsrc(vb + page * p.kv.v_sp, (uint32_t)(rows * p.v_ss * 2));
+      ok = (uint32_t)(j0 - first_tok) * (uint32_t)p.k_ss * 2;
+      ov = (uint32_t)(j0 - first_tok) * (uint32_t)p.v_ss * 2;
+    }
+    __bf16* Vs = Ks + BN * T::KSTR;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      buf_load16_lds(r_k, ok + kdoff[u], Ks + (RPW * wave + RPI * u) * D);
+      buf_load16_lds(r_v, ov + vdoff[u], Vs + (RPW * wave + RPI * u) * D);
+    }
+  };
+  // operand addresses: per-lane bases plus constants (in the swizzled layout
+  // the chunk permutation depends on the row modulo 16 only)
+  int aoff[T::NC], toff[2][T::ND];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) aoff[c] = DMA ? swz<D>(kperm, 16 * c + 8 * hh) : kperm * T::KSTR + 8 * hh + 16 * c;
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db) {
+    toff[0][db] = DMA ? swz<D>(tr_row, 32 * db + tr_col) : tr_row * T::VSTR + tr_col + 32 * db;
+    toff[1][db] = DMA ? swz<D>(tr_row + 4, 32 * db + tr_col) : (tr_row + 4) * T::VSTR + tr_col + 32 * db;
+  }
 
   f32x16 oacc[T::ND];
 #pragma unroll
@@ -228,36 +284,44 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
   const float lazy_margin = 8.f / c2;   // 2^8 growth of the probabilities, in score units
 
   if (ntiles > 0) {
-    gload(0);
-    lstore(0);
+    if constexpr (DMA) {
+      dma(0, smem);
+    } else {
+      gload(0);
+      lstore(smem);
+    }
   }
-  wait_vmem();  // Q fragments have landed on every path into the loop
+  wait_vmem();  // Q fragments (and tile 0) have landed on every path into the loop
   __syncthreads();
 
   const int wave_last_row = q0 + wave * 32 + 31;
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
+  // One tile, with its stage and the other stage as restrict pointers: the
+  // compiler then knows that the DMA filling `nxt` writes nothing this tile
+  // reads, and issues the reads without waiting for it.
+  auto tile = [&](int t, const __bf16* __restrict__ cur, __bf16* __restrict__ nxt) __attribute__((always_inline)) {
     const int j0 = t * BN;
     const bool more = t + 1 < ntiles;
-    if (more) gload(j0 + BN);
+    if (more) {
+      if constexpr (DMA) dma(j0 + BN, nxt);
+      else gload(j0 + BN);
+    }
 
     // Non-causal: always true, but kept opaque to the compiler, which
     // otherwise schedules the loop into more registers than three waves per
     // SIMD allow once the softmax has its two paths.
     const bool wave_active = CAUSAL ? j0 <= wave_last_row + diag : __builtin_amdgcn_readfirstlane(ntiles) > 0;
     if (wave_active) {
-      const __bf16* Ks = smem + st * T::STAGE;
-      const __bf16* Vs = Ks + BN * T::KSTR;
+      const __bf16* Ks = cur;
+      const __bf16* Vs = cur + BN * T::KSTR;
       // ---- S^T = K Q^T for two 32-key blocks
       f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
       // per-lane bases plus compile-time constants (folded into the LDS
       // instructions' offset fields)
-      const __bf16* kbase = Ks + kperm * T::KSTR + 8 * hh;
 #pragma unroll
       for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const bf16x8 kf = *(const bf16x8*)(kbase + 32 * kb2 * T::KSTR + 16 * c);
+          const bf16x8 kf = *(const bf16x8*)(Ks + aoff[c] + 32 * kb2 * T::KSTR);
           sacc[kb2] = mfma32(kf, qf[c], sacc[kb2]);
         }
       }
@@ -325,19 +389,25 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_bf16_kernel(Fwd
       }
       l_run += rs;
       // ---- O^T += V^T P^T
-      const __bf16* vbase = Vs + tr_row * T::VSTR + tr_col;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int db = 0; db < T::ND; ++db) {
-          const __bf16* vp = vbase + 16 * c * T::VSTR + 32 * db;
-          const bf16x8 vf = cat_bf16(lds_read_tr16(vp), lds_read_tr16(vp + 4 * T::VSTR));
+          const bf16x8 vf = cat_bf16(lds_read_tr16(Vs + toff[0][db] + 16 * c * T::VSTR),
+                                     lds_read_tr16(Vs + toff[1][db] + 16 * c * T::VSTR));
           oacc[db] = mfma32(vf, pf[c], oacc[db]);
         }
       }
     }
-    if (more) lstore(st ^ 1);
+    if (more) {
+      if constexpr (DMA) wait_vmem();
+      else lstore(nxt);
+    }
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    __bf16* cur = smem + (t & 1) * T::STAGE;
+    tile(t, cur, smem + ((t & 1) ^ 1) * T::STAGE);
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)

@@ -140,8 +140,10 @@ def test_decode_shape_without_workspace_takes_tiled_path():
     run_kvcache([300, 17], 1, 1, 8, 2, 128, 64, True, True, seed=51, use_workspace=False)
 
 
-def test_dense_cache_prefill():
-    run_kvcache([64, 255], 70, 70, 8, 4, 128, 1, False, True, seed=61)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_cache_prefill(d, causal):
+    run_kvcache([64, 255], 70, 70, 8, 4, d, 1, False, causal, seed=61)
 
 
 def test_tiled_path_equals_dense_forward():

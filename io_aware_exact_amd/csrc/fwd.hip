@@ -28,10 +28,11 @@
 //     O^T += V^T P^T, with no register shuffle and no LDS round trip.
 //   * V^T, the A operand of that product, is read from the row-major V tile
 //     with the LDS transposing load (ds_read_b64_tr_b16).
-//   * K/V tiles of BN = 64 keys are double-buffered in LDS; the next tile's
-//     global loads (16 bytes per lane, whole 256-byte rows per 16 lanes) are
-//     issued before the current tile's MFMAs and written to the other buffer
-//     after them.  One barrier per tile.
+//   * K/V tiles of BN = 64 keys are double-buffered in LDS; the next tile
+//     is issued before the current tile's MFMAs, straight from HBM into the
+//     other (swizzled) buffer by LDS DMA, or for KV caches with pages below
+//     64 tokens through registers (16 bytes per lane) written to it after
+//     them.  One barrier per tile.
 //   * exp2 with the softmax scale and log2(e) folded into one FMA.
 //   * Causal: tiles entirely above the diagonal are skipped (the loop stops at
 //     the last visible key), waves skip tiles none of their rows can see, and

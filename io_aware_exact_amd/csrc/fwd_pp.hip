@@ -15,9 +15,10 @@
 //     t -- while the other runs the softmax of its newest scores, so the two
 //     waves of a SIMD always have different pipes to use;
 //   * group A takes the MFMA role in even phases, B in odd ones; phase f reads
-//     K of tile f/2 and V of tile f/2 - 1, and the loads issued in phase 2t
-//     (K_{t+1}, V_t) are written to the free LDS stages at the end of phase
-//     2t+1.
+//     K of tile f/2 and V of tile f/2 - 1; K_{t+1} and V_t are loaded in
+//     phase 2t into the free LDS stages, straight from HBM by LDS DMA (or,
+//     for KV caches with pages below 64 tokens, through registers written at
+//     the end of phase 2t+1), and are in LDS when phase 2t+1 ends.
 // Operand layouts, the transposed score orientation, lazy rescaling and
 // masking are those of the one-group forward kernel.
 #include <type_traits>

@@ -42,11 +42,17 @@ def fwd_flops(B, Sq, Sk, H, d, causal):
 
 
 def kernel_source_hash(files):
-    """Hash of the kernel sources a counter record was taken on."""
+    """Hash of the kernel sources a counter record was taken on, with
+    comments and whitespace removed (an edit of a comment leaves the kernel,
+    and so the record, unchanged)."""
+    import re
     h = hashlib.sha256()
     for name in files:
-        with open(os.path.join(ROOT, "io_aware_exact_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "io_aware_exact_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

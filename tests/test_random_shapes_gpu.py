@@ -15,7 +15,10 @@ import pytest
 
 from test_bwd_gpu import run_bwd
 from test_bwd_varlen_gpu import run_varlen_bwd
+from test_fp8_gpu import run_fp8
 from test_fwd_gpu import run_dense
+from test_kvcache_gpu import run_kvcache
+from test_mxfp8_gpu import run_mx
 
 pytestmark = pytest.mark.gpu
 
@@ -51,3 +54,26 @@ def test_random_packed(seed):
     lens_q = [int(x) for x in rng.integers(1, 400, size=nseq)]
     lens_k = [int(x) for x in rng.integers(1, 400, size=nseq)] if seed % 2 else list(lens_q)
     run_varlen_bwd(lens_q, lens_k, hkv * group, hkv, d, causal, seed=5000 + seed, scale=scale)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_fp8(seed):
+    """FP8 forward, per-block and MX scales, with the element-wise O bound."""
+    d, hkv, group, sq, sk, _, scale = draw(6000 + seed)
+    causal = seed % 2 == 1
+    run_fp8(1, sq, sk, hkv * group, hkv, d, causal, seed=6100 + seed, scale=scale)
+    run_mx(1, sq, sk, hkv * group, hkv, d, causal, seed=6200 + seed, scale=scale)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_kvcache(seed):
+    """KV-cache attention: cached lengths, appended rows (decode or a chunk),
+    page size (or an unpaged cache) drawn per case."""
+    rng = np.random.default_rng(7000 + seed)
+    d, hkv, group, _, _, _, scale = draw(7100 + seed)
+    nseq = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(0, 900, size=nseq)]
+    snew = int(rng.choice([1, 1, int(rng.integers(2, 300))]))
+    page = int(rng.choice([16, 32, 64, 128, 256, 0]))
+    run_kvcache(lens, snew, snew, hkv * group, hkv, d, page if page else 1, page > 0,
+                seed % 2 == 0, seed=7200 + seed, scale=scale)

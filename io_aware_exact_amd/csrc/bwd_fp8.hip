@@ -75,7 +75,9 @@ __device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
 // Four fp32 values (each within +-448) -> four e4m3 codes in one word, a in
 // the low byte; the hardware rounds to nearest even.
 __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the second conversion overwrites the upper half the first one keeps, so
+  // the kept value can be any dead register (a's bits: no zeroing move)
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 

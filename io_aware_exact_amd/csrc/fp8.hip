@@ -95,7 +95,9 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
 // Four fp32 values -> four e4m3 codes in one word, a in the low byte
 // (hardware rounding to nearest even; inputs here lie in [0, 256]).
 __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the second conversion overwrites the upper half the first one keeps, so
+  // the kept value can be any dead register (a's bits: no zeroing move)
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 

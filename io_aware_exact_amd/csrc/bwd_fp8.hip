@@ -42,7 +42,8 @@
 //     head), each 32-key group split between a P-wave (K resident,
 //     S = Q K^T, P, dV^T += dO^T P) and a dS-wave (V resident, dP = dO V^T,
 //     dS, dK^T += Q^T dS) that runs one query tile behind and receives P in
-//     bf16 through LDS; Q and dO tiles of 64 rows through a 3-stage ring.
+//     fp32 through LDS (the dS-wave has the longer VALU part, so P reaches
+//     it ready to use); Q and dO tiles of 64 rows through a 3-stage ring.
 //   * bwd_dq_fp8: 128 query rows of one (batch, head); Q^T and dO^T
 //     resident, K and V tiles of 64 keys through a 2-stage ring; dQ is a
 //     fixed-order sum over the key tiles (no atomics), at the price of
@@ -119,6 +120,29 @@ __device__ __forceinline__ i32x8 pack_tile(const float (&v)[2][16], float f0, fl
   return out;
 }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+// Four fp32 values divided by s, a power of two, -> four e4m3 codes, with
+// the division done by the scaled conversion itself (v_cvt_scalef32_pk_fp8:
+// it divides by 2^exponent(s); checked with an in-bounds probe against the
+// plain conversion of x / s).  As pack4_fp8, the first conversion's kept
+// upper half is a dead register.
+__device__ __forceinline__ int pack4_fp8_scaled(float a, float b, float c, float d, float s) {
+  const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2, a), a, b, s, false);
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c, d, s, true));
+}
+// pack_tile with the values of block 0 divided by f0, block 1 by f1
+__device__ __forceinline__ i32x8 pack_tile_scaled(const float (&v)[2][16], float f0, float f1) {
+  i32x8 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float f = r < 2 ? f0 : f1;
+    const float* x = &v[r >> 1][8 * (r & 1)];
+    out[2 * r] = pack4_fp8_scaled(x[0], x[1], x[2], x[3], f);
+    out[2 * r + 1] = pack4_fp8_scaled(x[4], x[5], x[6], x[7], f);
+  }
+  return out;
+}
+
 // E4M3 codes of dS for one lane (two 32-token blocks, 16 values each), with
 // one power-of-two scale per block: returns the packed operand and, in
 // `sbyte`, the E8M0 byte this lane passes to the instruction (block 0 from
@@ -134,7 +158,7 @@ __device__ __forceinline__ i32x8 quantise_ds(const float (&v)[2][16], int hh, in
   m1 = fmaxf(m1, wave_xor32(m1));
   const int e0 = fit_exponent(m0), e1 = fit_exponent(m1);
   sbyte = (hh ? e1 : e0) + 127;
-  return pack_tile(v, exp2i(-e0), exp2i(-e1));
+  return pack_tile_scaled(v, exp2i(e0), exp2i(e1));
 }
 
 // ---------------------------------------------------------------------------
@@ -226,7 +250,7 @@ struct DkdvFp8Tile {
   static constexpr int STATS = 2 * BQ * 4 + 16;   // LSE (log2), D * sq, sq, dO scale byte
   static constexpr int STAGE_BYTES = 2 * TILE + STATS;
   static constexpr int NSTAGE = 3;             // P-wave's tile, dS-wave's tile, next tile
-  static constexpr int PEX_SLOT = 4 * 2 * 64 * 16 * 2;   // bf16 P of 4 key groups x 2 blocks
+  static constexpr int PEX_SLOT = 4 * 2 * 64 * 16 * 4;   // fp32 P of 4 key groups x 2 blocks
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES + 2 * PEX_SLOT;
   static constexpr int CH = D / 16;            // 16-byte chunks per row
   static constexpr int LD_THREADS = BQ * CH;   // threads loading one chunk of Q and of dO
@@ -343,9 +367,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
     else if (tid == 2 * T::BQ) stats[2 * T::BQ] = sqv;
     else if (tid == 2 * T::BQ + 1) ((int*)stats)[2 * T::BQ + 1] = edo;
   };
-  // bf16 P of key group kgrp, query block qb, in exchange slot sl
+  // fp32 P of key group kgrp, query block qb, in exchange slot sl: four
+  // 16-byte words per lane, lane-interleaved
   auto pex = [&](int sl, int qb) {
-    return (u32x4*)(smem + T::NSTAGE * T::STAGE_BYTES + sl * T::PEX_SLOT) + ((kgrp * 2 + qb) * 2) * 64 + lane;
+    return (u32x4*)(smem + T::NSTAGE * T::STAGE_BYTES + sl * T::PEX_SLOT) + ((kgrp * 2 + qb) * 4) * 64 + lane;
   };
 
   f32x16 acc[T::ND];
@@ -411,16 +436,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
               if (key >= Lk || (CAUSAL && key > iq + diag)) v[qb][i] = 0.f;
             }
           }
-          // v = 2^8 P: the bf16 exchange carries it exactly scaled
-          bf16x8 ob0, ob1;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ob0[i] = (__bf16)v[qb][i];
-            ob1[i] = (__bf16)v[qb][8 + i];
-          }
+          // v = 2^8 P, passed in fp32
           u32x4* pe = pex(t & 1, qb);
-          pe[0] = __builtin_bit_cast(u32x4, ob0);
-          pe[64] = __builtin_bit_cast(u32x4, ob1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pe[64 * j] = __builtin_bit_cast(u32x4, (f32x4){v[qb][4 * j], v[qb][4 * j + 1], v[qb][4 * j + 2], v[qb][4 * j + 3]});
         }
       } else {
         // dS * sq = 2^8 P (dP sv sq 2^-8 - D sq 2^-8), 2^8 P from the P-wave
@@ -433,13 +453,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
           const float drow_v[16] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3],
                                     dc[0], dc[1], dc[2], dc[3], dd[0], dd[1], dd[2], dd[3]};
           const u32x4* pe = pex(t & 1, qb);
-          const bf16x8 p0 = __builtin_bit_cast(bf16x8, pe[0]);
-          const bf16x8 p1 = __builtin_bit_cast(bf16x8, pe[64]);
+          f32x4 p4[4];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
-            v[qb][i] = pv * __builtin_fmaf(s2[qb][i], f, -drow_v[i]);
-          }
+          for (int j = 0; j < 4; ++j) p4[j] = __builtin_bit_cast(f32x4, pe[64 * j]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[qb][i] = p4[i >> 2][i & 3] * __builtin_fmaf(s2[qb][i], f, -drow_v[i]);
         }
       }
       // ---- B operand of the second product: 2^8 P (P-wave) or dS (dS-wave)

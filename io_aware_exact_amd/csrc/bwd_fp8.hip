@@ -647,15 +647,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(BwdParams p) {
       const float c2t = c2 * sk, f = sv * sk, dsk = dlt * sk;
       const bool need_mask = (j0 + T::BN > Lk) || (CAUSAL && j0 + T::BN - 1 > wrow0 + diag);
       const int lim = CAUSAL ? min(Lk - 1, qrow + diag) : Lk - 1;
+      // Keys past lim get P = 0.  Register i of block kb2 holds key j0 +
+      // 32 kb2 + 16 (i >> 3) + 8 hh + (i & 7), so the test is a constant
+      // against one per-lane threshold, and it runs only on tiles that need
+      // it: need_mask is wave-uniform, and saying so, with the unmasked loop
+      // written out separately, gives a branch instead of selects on every
+      // element of every tile.
       float v[2][16];
+      if (__builtin_amdgcn_readfirstlane((int)need_mask) != 0) {
+        const int thr = lim - j0 - 8 * hh;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(__builtin_fmaf(sacc[kb2][i], c2t, -lse2));
-          if (need_mask && j0 + 32 * kb2 + 16 * (i >> 3) + 8 * hh + (i & 7) > lim) pv = 0.f;
-          v[kb2][i] = pv * __builtin_fmaf(dacc[kb2][i], f, -dsk);
-        }
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(__builtin_fmaf(sacc[kb2][i], c2t, -lse2));
+            if (32 * kb2 + 16 * (i >> 3) + (i & 7) > thr) pv = 0.f;
+            v[kb2][i] = pv * __builtin_fmaf(dacc[kb2][i], f, -dsk);
+          }
+      } else {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            v[kb2][i] = fast_exp2(__builtin_fmaf(sacc[kb2][i], c2t, -lse2)) * __builtin_fmaf(dacc[kb2][i], f, -dsk);
+      }
       int sbyte;
       const i32x8 ds8 = quantise_ds(v, hh, sbyte);
       // ---- dQ^T += K^T dS^T (64 keys per instruction; K^T by transposing reads)

@@ -418,6 +418,47 @@ def leg_dqaccum(reps):
     return out
 
 
+def leg_hbmread(reps):
+    """The box's sustained HBM read rate, measured with a plain streaming
+    kernel (measurement probe `libfa_probe.so`, not part of the path): 8 GiB
+    of random bytes read once per launch in 16-byte loads, ordinary and
+    non-temporal, 4 to 16 loads in flight per thread, over several grid
+    sizes.  The practical ceiling the
+    HBM-bound decode kernel is compared with."""
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "io_aware_exact_amd")
+    L = ctypes.CDLL(os.path.join(here, "libfa_probe.so"))
+    L.fa_probe_hbm_read.restype = ctypes.c_int
+    L.fa_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 8 << 30
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    grids = (2048, 4096, 8192, 16384, 32768)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(grid, mode):
+        rc = L.fa_probe_hbm_read(buf.data_ptr(), nbytes, out.data_ptr(), out.numel(), grid, mode,
+                                 ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"fa_probe_hbm_read returned {rc}")
+    res = {"workload": "HBM read of 8 GiB, 16-byte loads (plain streaming kernel)", "bytes": nbytes, "runs": {}}
+    best = None
+    for mode, name in ((0, "plain_u4"), (1, "nontemporal_u4"), (2, "nontemporal_u8"), (3, "nontemporal_u16")):
+        for grid in grids:
+            t = time_calls(lambda: run(grid, mode), reps)
+            gbps = nbytes / t["median"] / 1e6
+            res["runs"][f"{name}_grid{grid}"] = {"median_ms": round(t["median"], 4), "gbps": round(gbps, 1)}
+            if best is None or gbps > best[0]:
+                best = (gbps, f"{name}_grid{grid}")
+    res["best_gbps"] = round(best[0], 1)
+    res["best_run"] = best[1]
+    res["best_frac_of_hbm"] = round(best[0] / PEAK_HBM_GBPS, 4)
+    del buf
+    return res
+
+
 def leg_main(reps, with_bwd):
     """The main workload alone (B=2, H=16, S=8192, d=128, non-causal): fwd, or
     fwd then bwd, reps times -- for profiling."""
@@ -446,7 +487,8 @@ def extra_legs(args, keep_rows=None):
     out = {}
     if args.only in ("fwd", "fwdbwd"):
         return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
-    for name, fn, reps in (("gemm", leg_gemm, 20), ("dqaccum", leg_dqaccum, 20), ("causal", leg_causal, 20),
+    for name, fn, reps in (("gemm", leg_gemm, 20), ("hbmread", leg_hbmread, 20), ("dqaccum", leg_dqaccum, 20),
+                           ("causal", leg_causal, 20),
                            ("decode", leg_decode, 20),
                            ("varlen", leg_varlen, 20), ("kvcache", leg_kvcache, 20),
                            ("fp8", leg_fp8, 20),
@@ -467,7 +509,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
     ap.add_argument("--only", choices=["decode", "varlen", "kvcache", "causal", "fp8", "sweep", "fwd",
-                                       "fwdbwd", "gemm", "dqaccum"],
+                                       "fwdbwd", "gemm", "dqaccum", "hbmread"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

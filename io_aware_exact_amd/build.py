@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
-PROBE_SOURCES = ["probe_dq_accum.hip"]
+PROBE_SOURCES = ["probe_dq_accum.hip", "probe_hbm_read.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "fwd.hip", "fwd_pp.hip", "fwd_f32.hip", "bwd.hip", "decode.hip", "fp8.hip",

@@ -12,8 +12,9 @@ with every term computed in fp64 from the oracle's inputs:
     its block, 2^e_I the block scale);
   * scores: the FP8 instruction's dot product is within
     eps_ij = 2^-11 scale sum_c |q_ic k_jc| (plus fp32 rounding of the exp2
-    argument), so the kernel's P_ij is within a factor exp(+-eps_ij); the P
-    the dS side uses passes through bf16 (2^-9);
+    argument), so the kernel's P_ij is within a factor exp(+-eps_ij); the dS
+    side receives that P in fp32 and forms dS in fp32 (2^-12 covers that
+    arithmetic with a wide margin);
   * dP = dO V^T and D = rowsum(dO o O) inherit the dO error (the instruction's
     own summation adds 2^-11 of sum |dO||v|; the bf16 O passed in 2^-9);
   * dS = P (dP - D) is then within
@@ -93,7 +94,7 @@ def head_bounds(q, k, v, g, O, lse, scale, causal, chunk=1024):
         dS = P * (dP - D[:, None])
         ddP = delta[r] @ av.T + 2.0 ** -11 * (1 + 2.0 ** -4) * (ag[r] @ av.T)
         dD = (delta[r] * aO[r]).sum(axis=1) + 2.0 ** -9 * (ag[r] * aO[r]).sum(axis=1)
-        E = P * (ddP + dD[:, None]) + np.abs(dS) * (ee + 2.0 ** -8)
+        E = P * (ddP + dD[:, None]) + np.abs(dS) * (ee + 2.0 ** -12)
         M = np.abs(dS) + E
         # dK: dS quantised in blocks of 32 query rows per key
         QK = (1 + 2.0 ** -4) * E + 2.0 ** -4 * np.abs(dS) + 2.0 ** -10 * block_max(M, 0) / 224

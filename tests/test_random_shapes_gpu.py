@@ -2,7 +2,8 @@
 against the fp64 oracle with the usual bars: head dimension, causal flag,
 GQA grouping, unequal and ragged lengths (including a single row or key) and
 the softmax scale drawn per case, so that tile, wave and stage boundaries
-fall at varied places in every kernel.
+fall at varied places in every kernel (bf16 and FP8, forward and backward,
+and the KV-cache paths).
 
 The scale is drawn within [0.5, 1.5] / sqrt(d).  The absolute gradient bar
 holds for scores of about unit spread; the backward forms D = rowsum(dO o O)
@@ -13,6 +14,7 @@ exactly but for D)."""
 import numpy as np
 import pytest
 
+from test_bwd_fp8_gpu import run_fp8_bwd
 from test_bwd_gpu import run_bwd
 from test_bwd_varlen_gpu import run_varlen_bwd
 from test_fp8_gpu import run_fp8
@@ -63,6 +65,15 @@ def test_random_fp8(seed):
     causal = seed % 2 == 1
     run_fp8(1, sq, sk, hkv * group, hkv, d, causal, seed=6100 + seed, scale=scale)
     run_mx(1, sq, sk, hkv * group, hkv, d, causal, seed=6200 + seed, scale=scale)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_fp8_bwd(seed):
+    """FP8 backward with the element-wise gradient bounds (the scale drawn
+    as above, or 1/sqrt(d))."""
+    d, hkv, group, sq, sk, _, scale = draw(6500 + seed)
+    causal = seed % 2 == 0
+    run_fp8_bwd(1 + seed % 2, sq, sk, hkv * group, hkv, d, causal, seed=6600 + seed, scale=scale)
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -387,6 +387,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_fp8_kernel(BwdParams p) {
     gload();
     lstore(0);
   }
+  wait_vmem();
   __syncthreads();
 
   int st_cur = 0, st_prev = 2, st_next = 1;
@@ -590,6 +591,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(BwdParams p) {
                 (uint32_t)((int64_t)Lk * p.v_ss));
   const int lrow = tid / T::CH, lcol = 16 * (tid % T::CH);
   u32x4 kreg[T::NP], vreg[T::NP];
+  // the K and V scales of the tile being loaded travel with it, so their
+  // load latency is hidden like the tile's
+  float sk_n = 1.f, sv_n = 1.f;
   auto gload = [&](int j0) {
 #pragma unroll
     for (int w = 0; w < T::NP; ++w) {
@@ -597,6 +601,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(BwdParams p) {
       kreg[w] = buf_load16(rk, r * (uint32_t)p.k_ss + lcol);
       vreg[w] = buf_load16(rv, r * (uint32_t)p.v_ss + lcol);
     }
+    sk_n = ksc[j0 / QBLK];
+    sv_n = vsc[j0 / QBLK];
   };
   auto lstore = [&](int st) {
     uint8_t* Ks = smem + st * T::STAGE;
@@ -620,6 +626,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(BwdParams p) {
     gload(0);
     lstore(0);
   }
+  float sk_c = sk_n, sv_c = sv_n;   // scales of the tile in LDS
+  wait_vmem();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -630,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(BwdParams p) {
     if (t < nt_w) {
       const uint8_t* Ks = smem + st * T::STAGE;
       const uint8_t* Vs = Ks + T::BN * T::STR;
-      const float sk = ksc[j0 / QBLK], sv = vsc[j0 / QBLK];
+      const float sk = sk_c, sv = sv_c;
       // ---- S^T = K Q^T and dP^T = V dO^T (keys in the rows, queries in the lanes)
       f32x16 sacc[2] = {(f32x16){}, (f32x16){}}, dacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
@@ -688,6 +696,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(BwdParams p) {
       }
     }
     if (more) lstore(st ^ 1);
+    sk_c = sk_n;
+    sv_c = sv_n;
     __syncthreads();
   }
 

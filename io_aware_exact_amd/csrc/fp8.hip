@@ -190,6 +190,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   // half-word for d = 64); V: the key-block-hh scale of d row 32 db + l32.
   // Indices past the sequence end are clamped (their codes read as zero).
   uint32_t ksn[2] = {0u, 0u}, vsn[T::ND];
+  // per-block path: the K and V scales of the next tile, loaded with it so
+  // that their latency is hidden like the tile's (non-causal instances; the
+  // causal ones measured slower this way and load them in the tile)
+  float skn = 1.f, svn = 1.f;
   const int nkb32 = (Lk + 31) / 32;
   auto gload = [&](int j0) {
 #pragma unroll
@@ -197,6 +201,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
       const uint32_t r = (uint32_t)(j0 + lrow + w * T::RPP);
       kreg[w] = buf_load16(rk, r * (uint32_t)p.k_ss + lcol);
       vreg[w] = buf_load16(rv, r * (uint32_t)p.v_ss + lcol);
+    }
+    if constexpr (!MX && !CAUSAL) {
+      skn = ksc[j0 / QBLK];
+      svn = vsc[j0 / QBLK];
     }
     if constexpr (MX) {
 #pragma unroll
@@ -221,7 +229,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
     }
   };
   uint32_t ksc_t[2] = {0u, 0u}, vsc_t[T::ND];   // MX scales of the tile in LDS
+  float sk_t = 1.f, sv_t = 1.f;                  // per-block scales of the tile in LDS
   auto take_scales = [&]() {
+    if constexpr (!MX && !CAUSAL) {
+      sk_t = skn;
+      sv_t = svn;
+    }
     if constexpr (MX) {
       ksc_t[0] = ksn[0];
       ksc_t[1] = ksn[1];
@@ -269,12 +282,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
     if (wave_active) {
       const uint8_t* Ks = smem + st * T::STAGE;
       const uint8_t* Vs = Ks + BN * T::STR;
-      const float c2 = MX ? p.scale_log2 : cq * ksc[j0 / QBLK];
+      const float c2 = MX ? p.scale_log2 : cq * (CAUSAL ? ksc[j0 / QBLK] : sk_t);
       // per-block path: sv_J / sv_ref = 2^kv r, r in [1, 2)
       int pbyte = 127;            // E8M0 scale of the P operand
       float log2r = 0.f, inv_r = 1.f;
       if (!MX) {
-        const uint32_t rb = __builtin_bit_cast(uint32_t, vsc[j0 / QBLK] * inv_sv_ref);
+        const uint32_t rb = __builtin_bit_cast(uint32_t, (CAUSAL ? vsc[j0 / QBLK] : sv_t) * inv_sv_ref);
         const int kv = max(-119, min(0, (int)(rb >> 23) - 127));
         const float r = __builtin_bit_cast(float, (rb & 0x7FFFFFu) | 0x3F800000u);
         pbyte = 127 + kv - (int)P_LOG2_BLK;

@@ -459,6 +459,48 @@ def leg_hbmread(reps):
     return res
 
 
+def leg_fixedcost(reps):
+    """Fixed cost per launch of the three main kernels: each timed at B=2,
+    H=16, d=128, non-causal with the other length 8192 and the swept one at
+    1024..8192 (forward and dQ: key length; dK/dV: query length), and a
+    least-squares line through the medians.  The intercept is the part of a
+    launch that does not scale with the sweep (workgroup start-up, operand
+    loads before the loop, pipeline fill and drain, stores), paid once per
+    round of workgroups."""
+    from io_aware_exact_amd import fa, inputs
+    B, H, d, S = 2, 16, 128, 8192
+    out = {"workload": "B=2 H=16 d=128 non-causal, one length 8192, the other 1024..8192"}
+    for name in ("fwd", "dkdv", "dq"):
+        xs, ys = [], []
+        for L in (1024, 2048, 4096, 8192):
+            Sq, Sk = (S, L) if name in ("fwd", "dq") else (L, S)
+            q, k, v, do = inputs.qkv(B, Sq, Sk, H, H, d, 1234, device="cuda", with_dout=True)
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+            fa.fwd(q, k, v, False, out=o, lse=lse)
+            grads = tuple(torch.empty_like(x) for x in (q, k, v))
+            a = fa.bwd_args(q, k, v, o, do, lse, *grads, False, None)
+            ws = torch.empty(int(fa.lib().fa_bwd_workspace_size(ctypes.byref(a))), dtype=torch.uint8,
+                             device="cuda")
+            fa.bwd(q, k, v, o, do, lse, False, out=grads, workspace=ws)
+            if name == "fwd":
+                fn = lambda: fa.fwd(q, k, v, False, out=o, lse=lse)
+            else:
+                st = fa.FA_BWD_DKDV if name == "dkdv" else fa.FA_BWD_DQ
+                fn = lambda: fa.bwd(q, k, v, o, do, lse, False, out=grads, workspace=ws, stages=st)
+            t = time_calls(fn, reps)["median"]
+            xs.append(L)
+            ys.append(t)
+        n = len(xs)
+        mx, my = sum(xs) / n, sum(ys) / n
+        slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+        out[name] = {"lengths": xs, "median_ms": [round(y, 4) for y in ys],
+                     "intercept_us": round((my - slope * mx) * 1e3, 1), "us_per_1024": round(slope * 1024 * 1e3, 1)}
+        del q, k, v, do, o, grads, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def leg_main(reps, with_bwd):
     """The main workload alone (B=2, H=16, S=8192, d=128, non-causal): fwd, or
     fwd then bwd, reps times -- for profiling."""
@@ -488,6 +530,7 @@ def extra_legs(args, keep_rows=None):
     if args.only in ("fwd", "fwdbwd"):
         return {args.only: leg_main(args.steps, args.only == "fwdbwd")}
     for name, fn, reps in (("gemm", leg_gemm, 20), ("hbmread", leg_hbmread, 20), ("dqaccum", leg_dqaccum, 20),
+                           ("fixedcost", leg_fixedcost, 20),
                            ("causal", leg_causal, 20),
                            ("decode", leg_decode, 20),
                            ("varlen", leg_varlen, 20), ("kvcache", leg_kvcache, 20),
@@ -509,7 +552,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (causal, decode, varlen)")
     ap.add_argument("--only", choices=["decode", "varlen", "kvcache", "causal", "fp8", "sweep", "fwd",
-                                       "fwdbwd", "gemm", "dqaccum", "hbmread"],
+                                       "fwdbwd", "gemm", "dqaccum", "hbmread", "fixedcost"],
                     help="run one secondary workload alone (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference "

@@ -421,11 +421,15 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
 }
 
 // The tiled bf16 forward.  At d = 128 the two-group kernel (one group's
-// softmax runs while the other group's MFMAs run) is faster; at d = 64 the
-// softmax costs about twice the matrix work per tile, so alternating the
-// groups only adds barriers and the one-group kernel is used.
+// softmax runs while the other group's MFMAs run) is faster.  At d = 64 the
+// softmax costs about twice the matrix work per tile; the two-group kernel
+// still wins once each workgroup's sweep is long enough to amortise its
+// start-up over 256 rows (same-box sweep at H = 16: non-causal from 2048
+// keys, causal from 8192), and the one-group kernel (three workgroups of
+// 128 rows per CU) is used below that and for packed sequences.
 hipError_t launch_fwd_tiled(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
   if (d == 128) return launch_fwd_bf16_pp(p, d, causal, varlen, stream);
+  if (d == 64 && !varlen && p.Sk >= (causal ? 8192 : 2048)) return launch_fwd_bf16_pp(p, d, causal, false, stream);
   return launch_fwd_bf16(p, d, causal, varlen, stream);
 }
 

@@ -45,6 +45,18 @@ def test_shapes(shape, causal):
     run_dense(B, Sq, Sk, Hq, Hkv, d, causal, seed=sum(shape))
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 300, 2100, 4, 2, 64), (2, 513, 2048, 2, 1, 64), (1, 700, 8250, 2, 1, 64),
+    (1, 1100, 8192, 1, 1, 64),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes_d64_long_keys(shape, causal):
+    # d = 64 with 2048 keys or more (8192 when causal) runs the two-group
+    # kernel: ragged query and key tails, GQA, Sq < Sk
+    B, Sq, Sk, Hq, Hkv, d = shape
+    run_dense(B, Sq, Sk, Hq, Hkv, d, causal, seed=7 + sum(shape))
+
+
 def test_scale_and_strided_views():
     # q/k/v as views into a packed [B,S,3,H,d] buffer (non-trivial strides)
     B, S, H, d = 2, 190, 4, 128

@@ -380,9 +380,27 @@ def leg_gemm(reps):
     c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
     t = time_calls(lambda: torch.matmul(a, b, out=c), reps)
     flops = 2.0 * n ** 3
-    return {"workload": "bf16 GEMM 8192x8192x8192 (torch.matmul, hipBLASLt)", "ms": round(t["mean"], 4),
-            "tflops": round(flops / t["mean"] / 1e9, 2),
-            "frac_of_peak": round(flops / t["mean"] / 1e9 / PEAK_BF16_TFLOPS, 4), "timing": timing(t)}
+    out = {"workload": "bf16 GEMM 8192x8192x8192 (torch.matmul, hipBLASLt)", "ms": round(t["mean"], 4),
+           "tflops": round(flops / t["mean"] / 1e9, 2),
+           "frac_of_peak": round(flops / t["mean"] / 1e9 / PEAK_BF16_TFLOPS, 4), "timing": timing(t)}
+    # the same product in E4M3 (torch._scaled_mm, per-tensor scales, bf16
+    # out): the sustained fp8 MFMA rate the FP8 kernels are compared with
+    del c
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.to(torch.float8_e4m3fn).t().contiguous().t()     # column-major B
+        one = torch.ones((), dtype=torch.float32, device="cuda")
+        c8 = torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        t8 = time_calls(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16), reps)
+        ref = torch.matmul(a8[:64].float(), b8.float())
+        err = float((c8[:64].float() - ref).abs().max() / ref.abs().max())
+        out["fp8"] = {"workload": "E4M3 GEMM 8192x8192x8192 (torch._scaled_mm, hipBLASLt, bf16 out)",
+                      "ms": round(t8["mean"], 4), "tflops": round(flops / t8["mean"] / 1e9, 2),
+                      "frac_of_peak": round(flops / t8["mean"] / 1e9 / PEAK_FP8_TFLOPS, 4),
+                      "max_rel_err_first_rows": round(err, 5), "timing": timing(t8)}
+    except (RuntimeError, TypeError, AttributeError) as e:
+        out["fp8"] = {"error": str(e).splitlines()[0][:200]}
+    return out
 
 
 def leg_dqaccum(reps):

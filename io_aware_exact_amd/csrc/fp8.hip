@@ -103,13 +103,20 @@ __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
 
 template <int D>
 struct Fp8Tile {
-  static constexpr int STR = D + 16;      // LDS row stride in bytes (K and V)
+  // LDS row strides in bytes.  K rows are read 16 bytes per lane, 16 lanes
+  // at once, rows {0-3, 8-11} and {4-7, 12-15} of a block: a stride of 36
+  // (d = 128) or 20 (d = 64) banks puts them on distinct banks of the 64.
+  // V is read transposed, 8 rows x 32 bytes per 32 lanes: a stride of 40 or
+  // 24 banks (8 times an odd number, mod 64) puts the 8 rows on disjoint
+  // banks, where D + 16 made two of them share 4 banks on every read.
+  static constexpr int STR = D + 16;
+  static constexpr int STR_V = D + 32;
   static constexpr int NC = D / 64;       // 64-wide d chunks of S^T
   static constexpr int ND = D / 32;       // 32-row d blocks of O^T
   static constexpr int CH = D / 16;       // 16-byte chunks per row
   static constexpr int RPP = NTHREADS / CH;
   static constexpr int NP = BN / RPP;
-  static constexpr int STAGE = 2 * BN * STR;
+  static constexpr int STAGE = BN * (STR + STR_V);
 };
 
 template <int D, bool CAUSAL, bool MX>
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
     for (int w = 0; w < T::NP; ++w) {
       *(u32x4*)(Ks + (lrow + w * T::RPP) * T::STR + lcol) = kreg[w];
-      *(u32x4*)(Vs + (lrow + w * T::RPP) * T::STR + lcol) = vreg[w];
+      *(u32x4*)(Vs + (lrow + w * T::RPP) * T::STR_V + lcol) = vreg[w];
     }
   };
   uint32_t ksc_t[2] = {0u, 0u}, vsc_t[T::ND];   // MX scales of the tile in LDS
@@ -358,13 +365,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
       }
       l_run += MX ? rs : rs * inv_r;
       // O_hat^T += V8^T P8^T (64 keys per MFMA)
-      const uint8_t* vbase = Vs + tr_row * T::STR + tr_col;
+      const uint8_t* vbase = Vs + tr_row * T::STR_V + tr_col;
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) {
         i32x8 vf;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const i32x2 x = lds_read_tr8(vbase + 16 * r * T::STR + 32 * db);
+          const i32x2 x = lds_read_tr8(vbase + 16 * r * T::STR_V + 32 * db);
           vf[2 * r] = x[0];
           vf[2 * r + 1] = x[1];
         }

@@ -47,6 +47,19 @@ def test_random_dense(seed):
     run_bwd(B, sq, sk, hkv * group, hkv, d, causal, seed=3000 + seed, scale=scale)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_long_keys(seed):
+    """Dense forward with 2048 to 9000 keys, where d = 64 takes the two-group
+    kernel (causal from 8192 keys) and short query blocks end anywhere."""
+    rng = np.random.default_rng(1500 + seed)
+    d, hkv, group, _, _, _, scale = draw(1600 + seed)
+    d = 64 if seed % 4 else d
+    causal = seed % 2 == 1
+    sk = int(rng.integers(8192, 9001) if causal else rng.integers(2048, 9001))
+    sq = int(rng.integers(1, 900))
+    run_dense(1, sq, sk, hkv * group, hkv, d, causal, seed=1700 + seed, scale=scale)
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_random_packed(seed):
     rng = np.random.default_rng(4000 + seed)

@@ -120,7 +120,7 @@ struct Fp8Tile {
 };
 
 template <int D, bool CAUSAL, bool MX>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
+__global__ __launch_bounds__(NTHREADS, MX ? 2 : 3) void fwd_fp8_kernel(FwdParams p) {
   using T = Fp8Tile<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
 
@@ -256,6 +256,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
   float m_run = -INFINITY;   // running max in log2 units of the scaled scores
   constexpr float PL = MX ? P_LOG2 : P_LOG2_BLK;
   float l_run = 0.f;         // sum of 2^PL p
+  float nbm = PL;            // PL - m_run (PL while m_run is -inf), kept with m_run
   const float cq = p.scale_log2 * sq;
   // per-block path: the head's largest V scale, the reference of O_acc
   float sv_ref = 1.f;
@@ -294,7 +295,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
       int pbyte = 127;            // E8M0 scale of the P operand
       float log2r = 0.f, inv_r = 1.f;
       if (!MX) {
-        const uint32_t rb = __builtin_bit_cast(uint32_t, (CAUSAL ? vsc[j0 / QBLK] : sv_t) * inv_sv_ref);
+        // wave-uniform: the bit manipulation below then runs on the scalar unit
+        const uint32_t rb = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)__builtin_bit_cast(uint32_t, (CAUSAL ? vsc[j0 / QBLK] : sv_t) * inv_sv_ref));
         const int kv = max(-119, min(0, (int)(rb >> 23) - 127));
         const float r = __builtin_bit_cast(float, (rb & 0x7FFFFFu) | 0x3F800000u);
         pbyte = 127 + kv - (int)P_LOG2_BLK;
@@ -338,18 +341,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(FwdParams p) {
       // the maximum, so that the largest stored value, 2^PL r exp2(mx - m),
       // is exactly 2^PL: a row dominated by one key then carries no e4m3
       // rounding on that key's probability.
-      const float m_new = mx + log2r;
       const bool grow = mx > m_run + LAZY;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-      if (grow) m_run = m_new;
-      l_run *= alpha;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare after the first tiles
+        const float m_new = mx + log2r;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+        if (grow) m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < T::ND; ++i) oacc[i] *= alpha;
+        nbm = (m_run == -INFINITY ? 0.f : -m_run) + PL;
       }
       // stored value 2^PL r exp2(s c2 - m): the prescale and log2 r ride in
       // the FMA constant
-      const float nb = (m_run == -INFINITY ? 0.f : -m_run) + PL + log2r;
+      const float nb = nbm + log2r;
       float rs = 0.f;
       i32x8 pf;
 #pragma unroll

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from io_aware_exact_amd import fa
+from io_aware_exact_amd import fa, inputs
 from parity import Guarded, check_lse, check_o
 
 pytestmark = pytest.mark.gpu
@@ -211,3 +211,46 @@ def test_full_size_paged_decode():
         o_r, lse_r = oracle.attention_fwd(q[b:b + 1].cpu(), kk[None].cpu(), vv[None].cpu(), True)
         check_o(f"O seq {b}", o[b:b + 1].float().cpu().numpy(), o_r)
         check_lse(f"LSE seq {b}", lse[b:b + 1].cpu().numpy(), lse_r)
+
+
+def test_full_size_paged_prefill():
+    """A prefill chunk against a paged cache at the benchmark's size: B=4,
+    Hq=32, Hkv=8, d=128, 15360 cached tokens and 1024 appended per sequence,
+    causal, 256-token pages in a shuffled order (the tiled path, pages read
+    by DMA).  Sampled query rows of every sequence and head against the
+    oracle, the cache's new rows checked bitwise."""
+    B, Hq, Hkv, d, ps, L0, sn = 4, 32, 8, 128, 256, 15360, 1024
+    L = L0 + sn
+    grp = Hq // Hkv
+    print(f"kvcache full size prefill B={B} cached={L0} new={sn} page={ps}", flush=True)
+    per = (L + ps - 1) // ps
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3300)
+    kc = torch.randn((B * per, ps, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((B * per, ps, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, sn, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn((B, sn, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((B, sn, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    gc = torch.Generator(device="cpu")
+    gc.manual_seed(3301)
+    bt = torch.randperm(B * per, generator=gc).to(torch.int32).view(B, per).cuda()
+    lens = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    o, lse = fa.fwd_kvcache(q, kc, vc, lens, bt, kn, vn, True)
+    torch.cuda.synchronize()
+    j = torch.arange(L, device="cuda")
+    for b in range(B):
+        pages = bt[b].long()[j // ps]
+        kk = kc[pages, j % ps]
+        vv = vc[pages, j % ps]
+        assert torch.equal(kk[L0:], kn[b]) and torch.equal(vv[L0:], vn[b])
+        pos = np.asarray(inputs.sample_indices(sn, 12, 3302 + b, always=(0, 1, sn - 1)), np.int64)
+        for kvh in range(Hkv):
+            hs = list(range(kvh * grp, (kvh + 1) * grp))
+            qr = q[b, pos][:, hs, :].transpose(0, 1).reshape(-1, d).cpu()
+            o_r, l_r = oracle.head_fwd(qr, np.tile(pos, grp), kk[:, kvh].cpu(), vv[:, kvh].cpu(),
+                                       L - sn, True, 1.0 / np.sqrt(d))
+            got_o = o[b, pos][:, hs, :].transpose(0, 1).reshape(-1, d).float().cpu().numpy()
+            got_l = lse[b, hs][:, pos].reshape(-1).cpu().numpy()
+            check_o(f"O seq {b} kv head {kvh}", got_o, o_r)
+            check_lse(f"LSE seq {b} kv head {kvh}", got_l, l_r)
+

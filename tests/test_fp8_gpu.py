@@ -170,11 +170,13 @@ def all_rows(B, Hq, Sq):
     return bi, hi, ii
 
 
-def run_fp8(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
+def run_fp8(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None, xs=None):
+    """xs: the fp32 q, k, v to quantise (default: the outlier distribution)."""
     print(f"fp8 B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}",
           flush=True)
-    xs = [inputs.outlier_normal(s, seed + i) for i, s in
-          enumerate([(B, Sq, Hq, d), (B, Sk, Hkv, d), (B, Sk, Hkv, d)])]
+    if xs is None:
+        xs = [inputs.outlier_normal(s, seed + i) for i, s in
+              enumerate([(B, Sq, Hq, d), (B, Sk, Hkv, d), (B, Sk, Hkv, d)])]
     qc, qs = fa.quantize_fp8(xs[0].cuda())
     kc, ks = fa.quantize_fp8(xs[1].cuda())
     vc, vs = fa.quantize_fp8(xs[2].cuda())
@@ -213,6 +215,22 @@ def check_fp8_all_rows(o, o_ref, lse_ref, Q, K, V, grp, scale, causal):
 def test_fp8_forward(shape, causal):
     B, Sq, Sk, Hq, Hkv, d = shape
     run_fp8(B, Sq, Sk, Hq, Hkv, d, causal, seed=500 + sum(shape))
+
+
+
+def growing_keys(Sq, Sk, Hq, Hkv, d, seed):
+    """Outlier-distributed q, k, v with the keys' norm growing along the
+    sequence (x1 to x4): later key tiles hold much larger scores, so each
+    row's reference has to move (and O, l be rescaled) on many tiles."""
+    q, k, v = (inputs.outlier_normal(s, seed + i) for i, s in
+               enumerate([(1, Sq, Hq, d), (1, Sk, Hkv, d), (1, Sk, Hkv, d)]))
+    return [q, k * torch.linspace(1.0, 4.0, Sk).view(1, Sk, 1, 1), v]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_growing_scores(d, causal):
+    run_fp8(1, 700, 900, 4, 2, d, causal, seed=91 + d, xs=growing_keys(700, 900, 4, 2, d, 91 + d))
 
 
 def test_fp8_forward_scale():

@@ -16,7 +16,8 @@ import oracle
 from oracle import fp8 as ofp8
 from io_aware_exact_amd import fa, inputs
 from parity import Guarded
-from test_fp8_gpu import abs_dot_max, check_fp8_all_rows, check_lse_fp8, check_o_fp8, o_bound_rows
+from test_fp8_gpu import (abs_dot_max, check_fp8_all_rows, check_lse_fp8, check_o_fp8, growing_keys,
+                          o_bound_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,11 +51,13 @@ def test_mx_quantiser_strided_and_special_values():
         assert np.array_equal(codes.cpu().numpy(), c_ref)
 
 
-def run_mx(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
+def run_mx(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None, xs=None):
+    """xs: the fp32 q, k, v to quantise (default: the outlier distribution)."""
     print(f"mxfp8 B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}",
           flush=True)
-    xs = [inputs.outlier_normal(s, seed + i) for i, s in
-          enumerate([(B, Sq, Hq, d), (B, Sk, Hkv, d), (B, Sk, Hkv, d)])]
+    if xs is None:
+        xs = [inputs.outlier_normal(s, seed + i) for i, s in
+              enumerate([(B, Sq, Hq, d), (B, Sk, Hkv, d), (B, Sk, Hkv, d)])]
     qc, qs = fa.quantize_mxfp8(xs[0].cuda(), 0)
     kc, ks = fa.quantize_mxfp8(xs[1].cuda(), 0)
     vc, vs = fa.quantize_mxfp8(xs[2].cuda(), 1)
@@ -82,6 +85,12 @@ def run_mx(B, Sq, Sk, Hq, Hkv, d, causal, seed, scale=None):
 def test_mx_forward(shape, causal):
     B, Sq, Sk, Hq, Hkv, d = shape
     run_mx(B, Sq, Sk, Hq, Hkv, d, causal, seed=700 + sum(shape))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mx_growing_scores(d, causal):
+    run_mx(1, 700, 900, 4, 2, d, causal, seed=93 + d, xs=growing_keys(700, 900, 4, 2, d, 93 + d))
 
 
 def test_mx_forward_scale():

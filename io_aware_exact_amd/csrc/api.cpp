@@ -424,12 +424,15 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
 // softmax runs while the other group's MFMAs run) is faster.  At d = 64 the
 // softmax costs about twice the matrix work per tile; the two-group kernel
 // still wins once each workgroup's sweep is long enough to amortise its
-// start-up over 256 rows (same-box sweep at H = 16: non-causal from 2048
-// keys, causal from 8192), and the one-group kernel (three workgroups of
-// 128 rows per CU) is used below that and for packed sequences.
+// start-up over 256 rows (same-box sweeps at H = 16: non-causal from 2048
+// keys, causal from 8192) and the query block fills most of those rows (at
+// 64 query rows against 8192 keys it ran 20% slower; from 256 rows it was
+// between 4% slower and 9% faster).  The one-group kernel (three workgroups
+// of 128 rows per CU) is used otherwise and for packed sequences.
 hipError_t launch_fwd_tiled(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
   if (d == 128) return launch_fwd_bf16_pp(p, d, causal, varlen, stream);
-  if (d == 64 && !varlen && p.Sk >= (causal ? 8192 : 2048)) return launch_fwd_bf16_pp(p, d, causal, false, stream);
+  if (d == 64 && !varlen && p.Sq >= 256 && p.Sk >= (causal ? 8192 : 2048))
+    return launch_fwd_bf16_pp(p, d, causal, false, stream);
   return launch_fwd_bf16(p, d, causal, varlen, stream);
 }
 

@@ -57,6 +57,19 @@ def test_shapes_d64_long_keys(shape, causal):
     run_dense(B, Sq, Sk, Hq, Hkv, d, causal, seed=7 + sum(shape))
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 33, 40, 2, 1, 128), (2, 64, 3000, 4, 2, 128), (1, 128, 8192, 2, 2, 128),
+    (1, 100, 517, 8, 1, 128), (3, 127, 127, 2, 2, 128), (1, 128, 64, 2, 2, 128),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes_d128_few_rows(shape, causal):
+    # d = 128 with at most 128 query rows (and more than 32 rows per kv head,
+    # so not the split-KV path) runs the one-group kernel: GQA, Sq > Sk with
+    # fully masked causal rows, long and ragged key sweeps
+    B, Sq, Sk, Hq, Hkv, d = shape
+    run_dense(B, Sq, Sk, Hq, Hkv, d, causal, seed=11 + sum(shape))
+
+
 def test_scale_and_strided_views():
     # q/k/v as views into a packed [B,S,3,H,d] buffer (non-trivial strides)
     B, S, H, d = 2, 190, 4, 128

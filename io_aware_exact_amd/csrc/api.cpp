@@ -973,8 +973,9 @@ fa_status fa_fwd_kvcache(const fa_fwd_kvcache_args* a, hipStream_t stream) {
   p.scale_log2 = scale_log2;
   p.kv = kv;
   const bool causal = a->causal != 0;
-  return hip_status(a->d == 128 ? launch_fwd_bf16_pp_kvcache(p, a->d, causal, stream)
-                                : launch_fwd_bf16_kvcache(p, a->d, causal, stream));
+  // at most 128 query rows: the one-group kernel, as for the dense forward
+  return hip_status(a->d == 128 && a->Sq > 128 ? launch_fwd_bf16_pp_kvcache(p, a->d, causal, stream)
+                                               : launch_fwd_bf16_kvcache(p, a->d, causal, stream));
 }
 
 }  // extern "C"

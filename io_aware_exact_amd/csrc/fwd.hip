@@ -442,6 +442,15 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// KV-cache instances, one per cache layout (no block table, pages of at
+// least 64 tokens, smaller pages)
+template <int D>
+hipError_t launch_kvcache(const FwdParams& p, bool causal, hipStream_t stream) {
+  if (!p.kv.block_table) return causal ? launch<D, true, false, 1>(p, stream) : launch<D, false, false, 1>(p, stream);
+  if (p.kv.page_shift >= 6) return causal ? launch<D, true, false, 2>(p, stream) : launch<D, false, false, 2>(p, stream);
+  return causal ? launch<D, true, false, 3>(p, stream) : launch<D, false, false, 3>(p, stream);
+}
+
 }  // namespace
 
 // d = 64, and dense d = 128 with at most 128 query rows (otherwise d = 128
@@ -453,11 +462,10 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, 
   return varlen ? launch<64, false, true>(p, stream) : launch<64, false, false>(p, stream);
 }
 
-// KV-cache attention with the one-group kernel (d = 64; d = 128 uses the
-// ping-pong kernel).
+// KV-cache attention with the one-group kernel (d = 64, and d = 128 with at
+// most 128 query rows; other d = 128 inputs use the ping-pong kernel).
 hipError_t launch_fwd_bf16_kvcache(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-  if (d != 64) return hipErrorInvalidValue;
-  if (!p.kv.block_table) return causal ? launch<64, true, false, 1>(p, stream) : launch<64, false, false, 1>(p, stream);
-  if (p.kv.page_shift >= 6) return causal ? launch<64, true, false, 2>(p, stream) : launch<64, false, false, 2>(p, stream);
-  return causal ? launch<64, true, false, 3>(p, stream) : launch<64, false, false, 3>(p, stream);
+  if (d == 64) return launch_kvcache<64>(p, causal, stream);
+  if (d == 128) return launch_kvcache<128>(p, causal, stream);
+  return hipErrorInvalidValue;
 }

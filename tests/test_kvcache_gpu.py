@@ -136,6 +136,14 @@ def test_chunked_prefill_growing_scores(d, causal):
     run_kvcache([0, 100, 513], 200, 200, 4, 1, d, 64, True, causal, seed=43, ramp=True)
 
 
+@pytest.mark.parametrize("page_size", [16, 32, 64, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_short_chunk_d128(page_size, causal):
+    # at most 128 new rows at d = 128 (the one-group kernel's cache paths):
+    # small pages read row by row, larger ones tile by tile
+    run_kvcache([0, 100, 513], 96, 96, 8, 2, 128, page_size, True, causal, seed=47 + page_size)
+
+
 def test_decode_shape_without_workspace_takes_tiled_path():
     run_kvcache([300, 17], 1, 1, 8, 2, 128, 64, True, True, seed=51, use_workspace=False)
 

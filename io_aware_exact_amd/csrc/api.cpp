@@ -430,13 +430,13 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
 // between 4% slower and 9% faster).  The one-group kernel (three workgroups
 // of 128 rows per CU) is used otherwise and for packed sequences.
 //
-// At d = 128 and at most 128 query rows the two-group kernel's 256-row
-// workgroups are at least half padding, and the one-group kernel (two
-// 128-row workgroups per CU at d = 128) ran 17% faster at 64 and 128 rows
-// against 8192 keys (B=16, H=16, both masks); at 192-255 rows it ran 18%
-// slower.
+// At d = 128 and at most 128 query rows (per sequence, for packed inputs)
+// the two-group kernel's 256-row workgroups are at least half padding, and
+// the one-group kernel (two 128-row workgroups per CU at d = 128) ran 17%
+// faster at 64 and 128 rows against 8192 keys (B=16, H=16, both masks); at
+// 192-255 rows it ran 18% slower.
 hipError_t launch_fwd_tiled(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
-  if (d == 128 && !varlen && p.Sq <= 128) return launch_fwd_bf16(p, d, causal, false, stream);
+  if (d == 128 && p.Sq <= 128) return launch_fwd_bf16(p, d, causal, varlen, stream);   // packed: Sq is the longest
   if (d == 128) return launch_fwd_bf16_pp(p, d, causal, varlen, stream);
   if (d == 64 && !varlen && p.Sq >= 256 && p.Sk >= (causal ? 8192 : 2048))
     return launch_fwd_bf16_pp(p, d, causal, false, stream);

@@ -2,8 +2,8 @@
 // accumulate, bf16 out, fp32 LSE), one group of four waves per workgroup.
 // Serves d = 64, where the softmax outweighs the matrix work per tile, for
 // packed sequences, KV caches and dense inputs with short key sweeps, and
-// dense d = 128 inputs of at most 128 query rows; other d = 128 inputs and
-// long dense d = 64 sweeps run the two-group kernel of fwd_pp.hip.
+// d = 128 inputs of at most 128 query rows per sequence; other d = 128
+// inputs and long dense d = 64 sweeps run the two-group kernel of fwd_pp.hip.
 //
 // Method (pages on IO-aware exact attention): blocks of Q, K and V are moved
 // from HBM into on-chip memory and partial outputs are computed there
@@ -453,10 +453,13 @@ hipError_t launch_kvcache(const FwdParams& p, bool causal, hipStream_t stream) {
 
 }  // namespace
 
-// d = 64, and dense d = 128 with at most 128 query rows (otherwise d = 128
-// and long dense d = 64 sweeps run the ping-pong kernel)
+// d = 64, and d = 128 with at most 128 query rows per sequence (otherwise
+// d = 128 and long dense d = 64 sweeps run the ping-pong kernel)
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
-  if (d == 128 && !varlen) return causal ? launch<128, true, false>(p, stream) : launch<128, false, false>(p, stream);
+  if (d == 128) {
+    if (causal) return varlen ? launch<128, true, true>(p, stream) : launch<128, true, false>(p, stream);
+    return varlen ? launch<128, false, true>(p, stream) : launch<128, false, false>(p, stream);
+  }
   if (d != 64) return hipErrorInvalidValue;
   if (causal) return varlen ? launch<64, true, true>(p, stream) : launch<64, true, false>(p, stream);
   return varlen ? launch<64, false, true>(p, stream) : launch<64, false, false>(p, stream);

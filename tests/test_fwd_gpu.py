@@ -98,8 +98,10 @@ def test_gqa_equals_repeated_heads():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen(d, causal):
-    lens = [1, 0, 17, 128, 129, 300, 64, 255]
+@pytest.mark.parametrize("lens", [[1, 0, 17, 128, 129, 300, 64, 255], [1, 0, 17, 128, 64, 100, 33]])
+def test_varlen(d, causal, lens):
+    # the second list has no sequence over 128 rows: at d = 128 it runs the
+    # one-group kernel, the first the two-group kernel
     Hq, Hkv = 4, 2
     print(f"varlen lens={lens} d={d} causal={causal}", flush=True)
     q, k, v = inputs.packed_qkv(lens, lens, Hq, Hkv, d, 21, device="cuda")
@@ -114,6 +116,22 @@ def test_varlen(d, causal):
     o_ref, lse_ref = oracle.attention_fwd_varlen(q, k, v, cu.cpu(), cu.cpu(), causal)
     check_o("O", go.t.float().cpu().numpy(), o_ref)
     check_lse("LSE", gl.t.cpu().numpy(), lse_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_short_queries_long_keys(causal):
+    # packed d = 128 queries of at most 128 rows (the one-group kernel) over
+    # key sequences of other lengths, up to 1000 keys and down to none
+    lq, lk = [1, 64, 128, 33, 90], [500, 64, 1000, 10, 0]
+    Hq, Hkv, d = 8, 2, 128
+    print(f"varlen short queries lq={lq} lk={lk} causal={causal}", flush=True)
+    q, k, v = inputs.packed_qkv(lq, lk, Hq, Hkv, d, 23, device="cuda")
+    cq, ck = inputs.cu_seqlens(lq, device="cuda"), inputs.cu_seqlens(lk, device="cuda")
+    o, lse = fa.fwd_varlen(q, k, v, cq, ck, max(lq), max(lk), causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_varlen(q, k, v, cq.cpu(), ck.cpu(), causal)
+    check_o("O", o.float().cpu().numpy(), o_ref)
+    check_lse("LSE", lse.cpu().numpy(), lse_ref)
 
 
 def test_varlen_equals_dense_per_sequence():

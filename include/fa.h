@@ -105,10 +105,11 @@ typedef struct {
  * softmax_scale must be finite and > 0 (1/sqrt(d) is the usual choice).
  *
  * Split-KV decode path (KV-cache inference: the repository overview's
- * flash_attn_with_kvcache entry point, here over a dense cache).  When all
- * query rows of one kv head fit one 32-wide tile, Sq * (Hq / Hkv) <= 32
- * (e.g. one new token per sequence), fa_fwd_workspace_size returns a nonzero
- * size; given a workspace of at least that many bytes (256-byte aligned, not
+ * flash_attn_with_kvcache entry point, here over a dense cache).  When the
+ * M = Sq * (Hq / Hkv) query rows of one kv head fit one 32-wide tile (M <= 32,
+ * e.g. one new token per sequence), or up to four such tiles that number
+ * fewer than the group's query heads (ceil(M / 32) < Hq / Hkv, M <= 128),
+ * fa_fwd_workspace_size returns a nonzero size; given a workspace of at least that many bytes (256-byte aligned, not
  * overlapping any tensor), fa_fwd cuts the keys into chunks that run in
  * parallel, each producing a partial (O_p, LSE_p), and merges them exactly:
  * LSE = ln sum_p exp(LSE_p), O = sum_p exp(LSE_p - LSE) O_p.  Without a
@@ -257,8 +258,9 @@ typedef struct {
  *
  * max_seqlen_k bounds every L_b (0: the capacity, max_pages_per_seq *
  * page_size, or page_size for a dense cache); it sizes the grid and the
- * split plan.  When Sq * (Hq / Hkv) <= 32, fa_fwd_kvcache_workspace_size is
- * nonzero and with that workspace (256-byte aligned) the keys are cut into
+ * split plan.  For the decode shapes of fa_fwd (Sq * (Hq / Hkv) <= 32, or up
+ * to 128 in fewer 32-row tiles than Hq / Hkv), fa_fwd_kvcache_workspace_size
+ * is nonzero and with that workspace (256-byte aligned) the keys are cut into
  * chunks that run in parallel and are merged exactly, as in fa_fwd's decode
  * path; otherwise (or without a workspace) the tiled forward kernels read
  * the cache pages directly (chunked prefill against a cache).

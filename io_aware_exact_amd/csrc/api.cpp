@@ -104,30 +104,43 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// ---- split-KV decode plan: taken when all query rows of one kv head fit in
-// the 32 columns of one MFMA tile.
-constexpr int kDecodeMaxRows = 32;
+// ---- split-KV decode plan: taken when the query rows of one kv head fit in
+// a few 32-column MFMA tiles (row blocks), each a workgroup that reads the
+// kv head's keys of its split.  With more than one row block it is taken
+// only when the blocks are fewer than the group's query heads, i.e. when it
+// streams each kv head's keys fewer times than the tiled kernels (one pass
+// per query head).  Same box, d = 128, against the tiled path: B=8, 64 query
+// heads on one kv head, one row each, 32768 keys: 855 -> 61 us; B=8, group
+// 4, 16 rows per head, 8192 keys: 160 -> 110 us; the same with 32 rows per
+// head (four blocks): 160 -> 153 us; B=4, group 1, 64 rows (two blocks):
+// 166 -> 196 us.
+constexpr int kDecodeTileRows = 32;
+constexpr int kDecodeMaxRowBlocks = 4;
+constexpr int kDecodeMaxRows = kDecodeTileRows * kDecodeMaxRowBlocks;
 constexpr int64_t kDecodeTargetWaves = 4096;  // one wave per (batch, kv head, split)
 constexpr int64_t kDecodeMinKeysPerSplit = 256;
 constexpr int64_t kDecodeMaxSplits = 64;
 
 struct DecodePlan {
   bool eligible;
-  int nsplit, chunk;
+  int nsplit, chunk, nrblk;
   size_t o_part_bytes, lse_part_bytes;
 };
 
 DecodePlan split_plan(fa_dtype dtype, int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
                       int64_t d) {
-  DecodePlan pl = {false, 1, 32, 0, 0};
+  DecodePlan pl = {false, 1, 32, 1, 0, 0};
   if (dtype != FA_BF16 || B <= 0 || Sq <= 0 || Sk < 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 ||
       (d != 64 && d != 128))
     return pl;
   const int64_t group = Hq / Hkv;
   if (Sq * group > kDecodeMaxRows) return pl;
+  const int64_t nrblk = (Sq * group + kDecodeTileRows - 1) / kDecodeTileRows;
+  if (nrblk > 1 && nrblk >= group) return pl;
   pl.eligible = true;
+  pl.nrblk = (int)nrblk;
   if (Sk > 0) {
-    const int64_t pairs = B * Hkv;
+    const int64_t pairs = B * Hkv * pl.nrblk;
     int64_t ns = (kDecodeTargetWaves + pairs - 1) / pairs;
     const int64_t by_len = (Sk + kDecodeMinKeysPerSplit - 1) / kDecodeMinKeysPerSplit;
     if (ns > by_len) ns = by_len;
@@ -619,6 +632,7 @@ fa_status fa_fwd(const fa_fwd_args* a, hipStream_t stream) {
     d.B = p.B; d.Sq = p.Sq; d.Sk = p.Sk; d.Hq = p.Hq; d.Hkv = p.Hkv; d.group = p.group;
     d.causal = a->causal != 0;
     d.nsplit = pl.nsplit;
+    d.nrblk = pl.nrblk;
     d.chunk = pl.chunk;
     d.scale = p.scale;
     d.scale_log2 = p.scale_log2;
@@ -952,6 +966,7 @@ fa_status fa_fwd_kvcache(const fa_fwd_kvcache_args* a, hipStream_t stream) {
     d.B = a->B; d.Sq = a->Sq; d.Sk = (int)maxlen; d.Hq = a->Hq; d.Hkv = a->Hkv; d.group = a->Hq / a->Hkv;
     d.causal = a->causal != 0;
     d.nsplit = pl.nsplit;
+    d.nrblk = pl.nrblk;
     d.chunk = pl.chunk;
     d.scale = a->softmax_scale;
     d.scale_log2 = scale_log2;

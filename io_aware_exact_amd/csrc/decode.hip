@@ -1,5 +1,6 @@
 // Split-KV decode forward of IO-aware exact attention for gfx950 (bf16 in,
-// fp32 accumulate), for few query rows per kv head: Sq * (Hq / Hkv) <= 32.
+// fp32 accumulate), for few query rows per kv head (Sq * (Hq / Hkv) up to a
+// few 32-row tiles).
 //
 // Method.  The same tiled exact attention as the dense forward (blocks of K
 // and V are streamed through on-chip memory with an online softmax: "Flash
@@ -16,10 +17,11 @@
 // gfx950 mapping.  One decode step reads every K and V byte once and does
 // ~4 flop per byte, so the kernel is bound by HBM bandwidth; MFMA is still
 // the cheapest way to do the dot products.
-//   * A workgroup is ONE wave that owns (batch, kv head, key chunk).  The
-//     M = Sq * group query rows of the kv head (all query heads of the group,
-//     all query positions) form the 32 columns of S^T = K Q^T, so K and V are
-//     read once for the whole group; unused columns are zero.
+//   * A workgroup is ONE wave that owns (batch, kv head, row block, key
+//     chunk).  The M = Sq * group query rows of the kv head (all query heads
+//     of the group, all query positions) form the columns of S^T = K Q^T, 32
+//     per row block, so K and V are read once per 32 rows of the group;
+//     unused columns are zero.
 //   * K and V tiles of 32 keys go from HBM straight into a 2-stage,
 //     wave-private LDS ring by DMA (buffer_load ... lds), stored swizzled so
 //     that the K A-operand reads (16 consecutive rows per 16 lanes, in the
@@ -95,8 +97,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   // compiler takes as per-lane would put every load in a waterfall loop
   const int split = __builtin_amdgcn_readfirstlane(blockIdx.x % p.nsplit);
   const int rest = __builtin_amdgcn_readfirstlane(blockIdx.x / p.nsplit);
-  const int g = __builtin_amdgcn_readfirstlane(rest % p.Hkv);
-  const int b = __builtin_amdgcn_readfirstlane(rest / p.Hkv);
+  const int rblk = __builtin_amdgcn_readfirstlane(rest % p.nrblk);
+  const int rest2 = __builtin_amdgcn_readfirstlane(rest / p.nrblk);
+  const int g = __builtin_amdgcn_readfirstlane(rest2 % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(rest2 / p.Hkv);
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -108,8 +112,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int kend = min(Lk, kbeg + p.chunk);
   const int nblk = kend > kbeg ? (kend - kbeg + BNK - 1) / BNK : 0;
 
-  // ---- Q^T fragments: column n is query row (head-in-group n / Sq, position n % Sq)
-  const int n = l32;
+  // ---- Q^T fragments: column l32 of row block rblk is query row n (head in
+  // the group n / Sq, position n % Sq)
+  const int n = 32 * rblk + l32;
   const int hi = n / p.Sq, qi = n % p.Sq;
   const int h = g * p.group + hi;
   bf16x8 qf[T::NC];
@@ -327,7 +332,7 @@ constexpr int kDecodeStages = 2;   // DMA stages per wave (3 measured slower)
 
 template <int D, int KVC>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
-  const long nblk = (long)p.B * p.Hkv * p.nsplit;
+  const long nblk = (long)p.B * p.Hkv * p.nrblk * p.nsplit;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_split_kernel<D, KVC, kDecodeStages>), dim3((unsigned)nblk), dim3(64), 0, stream, p);

@@ -105,6 +105,7 @@ struct DecodeParams {
   int B, Sq, Sk, Hq, Hkv, group;
   int causal;
   int nsplit, chunk;          // keys [s*chunk, (s+1)*chunk) form split s
+  int nrblk;                  // blocks of 32 of the Sq * group query rows of a kv head
   float scale;
   float scale_log2;
   KvCacheParams kv;           // KV-cache kernels only (then Sk bounds every length)

@@ -320,7 +320,8 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None):
 
 def fwd_decode(q, k, v, causal=False, scale=None, out=None, lse=None):
     """Forward that allocates the split-KV workspace when the decode path
-    applies (Sq * Hq / Hkv <= 32), else the plain dense forward."""
+    applies (M = Sq * Hq / Hkv <= 32, or M <= 128 in fewer 32-row blocks than
+    Hq / Hkv), else the plain dense forward."""
     n = fwd_workspace_bytes(q, k, v, causal, scale)
     ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
     return fwd(q, k, v, causal, scale, out, lse, ws)

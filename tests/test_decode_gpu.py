@@ -41,6 +41,20 @@ def test_shapes(shape, causal):
     run_decode(B, Sq, Sk, Hq, Hkv, d, causal, seed=300 + sum(shape))
 
 
+@pytest.mark.parametrize("shape", [
+    (2, 1, 3000, 64, 1, 128), (1, 16, 1000, 32, 8, 128), (2, 24, 777, 32, 8, 64),
+    (1, 5, 4000, 20, 1, 128), (1, 3, 2, 40, 1, 64), (1, 3, 300, 16, 1, 128),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes_several_row_blocks(shape, causal):
+    # 33 to 128 query rows per kv head, fewer 32-row blocks than query heads
+    # in the group: each block is its own workgroup over the same keys; block
+    # boundaries inside a head's rows (Sq = 3, 5), causal rows that see no
+    # key (Sq > Sk)
+    B, Sq, Sk, Hq, Hkv, d = shape
+    run_decode(B, Sq, Sk, Hq, Hkv, d, causal, seed=350 + sum(shape))
+
+
 def test_scale():
     run_decode(2, 1, 900, 8, 2, 128, False, seed=31, scale=0.3)
 

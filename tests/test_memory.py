@@ -91,6 +91,27 @@ def test_decode_workspace_bounded_in_sk(Sq, Hq, Hkv):
         assert 0 < nk <= cap, (Sk, nk)
 
 
+@pytest.mark.parametrize("Sq,Hq,Hkv,split", [
+    (1, 32, 8, True),      # 4 rows: one block
+    (8, 16, 4, True),      # 32 rows: one block
+    (1, 64, 1, True),      # 64 rows in 2 blocks, 64 query heads per kv head
+    (16, 32, 8, True),     # 64 rows in 2 blocks, group 4
+    (24, 32, 8, True),     # 96 rows in 3 blocks, group 4
+    (32, 32, 8, False),    # 128 rows in 4 blocks: as many as the group's heads
+    (64, 32, 32, False),   # 64 rows, group 1
+    (33, 1, 1, False),     # 33 rows, group 1
+    (1, 160, 1, False),    # 160 rows: over four blocks
+])
+def test_decode_row_block_rule(Sq, Hq, Hkv, split):
+    """The split-KV path takes up to four 32-row blocks of a kv head's query
+    rows, when the blocks are fewer than the group's query heads (each block
+    reads the kv head's keys; the tiled kernels read them once per query
+    head): its workspace is non-zero exactly then, for the dense and the
+    KV-cache entry points alike."""
+    assert (fwd_ws(2, Sq, 4096, Hq, Hkv, 128) > 0) == split
+    assert (kvcache_ws(2, Sq, 4096, Hq, Hkv, 128) > 0) == split
+
+
 def test_tiled_shapes_need_no_workspace():
     for S in LENGTHS:
         assert fwd_ws(2, max(S, 64), S, 16, 16, 128) == 0

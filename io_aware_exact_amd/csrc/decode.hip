@@ -332,6 +332,7 @@ constexpr int kDecodeStages = 2;   // DMA stages per wave (3 measured slower)
 
 template <int D, int KVC>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
+  if (p.nrblk < 1 || p.nsplit < 1) return hipErrorInvalidValue;
   const long nblk = (long)p.B * p.Hkv * p.nrblk * p.nsplit;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffL) return hipErrorInvalidValue;

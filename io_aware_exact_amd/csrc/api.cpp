@@ -451,8 +451,12 @@ fa_status check_bwd_varlen(const fa_bwd_varlen_args* a) {
 hipError_t launch_fwd_tiled(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
   if (d == 128 && p.Sq <= 128) return launch_fwd_bf16(p, d, causal, varlen, stream);   // packed: Sq is the longest
   if (d == 128) return launch_fwd_bf16_pp(p, d, causal, varlen, stream);
-  if (d == 64 && !varlen && p.Sq >= 256 && p.Sk >= (causal ? 8192 : 2048))
-    return launch_fwd_bf16_pp(p, d, causal, false, stream);
+  // packed d = 64 (longest sequences at least 256 queries and 2048 keys):
+  // 16 lengths on [128, 32768], Hq = 32, Hkv = 8, same box: non-causal
+  // 921-926 -> 962-967 TFLOP/s with the two-group kernel, causal 985-993 ->
+  // 943-948, so packed causal inputs keep the one-group kernel
+  const bool pp64 = varlen ? !causal && p.Sk >= 2048 : p.Sk >= (causal ? 8192 : 2048);
+  if (d == 64 && p.Sq >= 256 && pp64) return launch_fwd_bf16_pp(p, d, causal, varlen, stream);
   return launch_fwd_bf16(p, d, causal, varlen, stream);
 }
 

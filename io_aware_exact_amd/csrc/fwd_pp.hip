@@ -543,10 +543,12 @@ hipError_t launch(FwdParams p, hipStream_t stream) {
 
 }  // namespace
 
-// d = 128, dense or packed; d = 64 dense only (packed d = 64 inputs run the
-// one-group kernel, whose varlen dispatch this kernel's d = 64 is not built for).
+// d = 128 and d = 64, dense or packed.
 hipError_t launch_fwd_bf16_pp(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t stream) {
-  if (d == 64 && !varlen) return causal ? launch<64, true, false>(p, stream) : launch<64, false, false>(p, stream);
+  if (d == 64) {
+    if (causal) return varlen ? launch<64, true, true>(p, stream) : launch<64, true, false>(p, stream);
+    return varlen ? launch<64, false, true>(p, stream) : launch<64, false, false>(p, stream);
+  }
   if (d != 128) return hipErrorInvalidValue;
   if (causal) return varlen ? launch<128, true, true>(p, stream) : launch<128, true, false>(p, stream);
   return varlen ? launch<128, false, true>(p, stream) : launch<128, false, false>(p, stream);

@@ -134,6 +134,21 @@ def test_varlen_short_queries_long_keys(causal):
     check_lse("LSE", lse.cpu().numpy(), lse_ref)
 
 
+def test_varlen_d64_long_sequences():
+    # packed d = 64, non-causal, longest sequence over 2048 keys: the
+    # two-group kernel over every sequence of the pack, short ones included
+    lens = [2100, 300, 2500, 17, 256, 1]
+    Hq, Hkv, d = 4, 2, 64
+    print(f"varlen d64 long lens={lens}", flush=True)
+    q, k, v = inputs.packed_qkv(lens, lens, Hq, Hkv, d, 25, device="cuda")
+    cu = inputs.cu_seqlens(lens, device="cuda")
+    o, lse = fa.fwd_varlen(q, k, v, cu, cu, max(lens), max(lens), False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_varlen(q, k, v, cu.cpu(), cu.cpu(), False)
+    check_o("O", o.float().cpu().numpy(), o_ref)
+    check_lse("LSE", lse.cpu().numpy(), lse_ref)
+
+
 def test_varlen_equals_dense_per_sequence():
     lens_q = [100, 37, 256]
     lens_k = [150, 37, 300]
